@@ -1,0 +1,178 @@
+/*
+ * addnormq.h -- C ABI of the fused local tail of a transformer layer on
+ * AMD Instinct MI355X (gfx950):
+ *
+ *   residual <- x + residual            (in place, rounded to the activation type)
+ *   n        <- RMSNorm(residual) * gamma   (binary32)
+ *   q        <- FP8 E4M3 (per-tensor scale) or NVFP4 (E2M1 + per-16 E4M3 scales)
+ *   norm_out <- n rounded to the activation type   (optional)
+ *
+ * and of the Q/K per-head RMSNorm + NeoX RoPE + uniform FP8 store.
+ *
+ * Sources of the operations (the pages these ops are built from):
+ *  - TensorRT-LLM issue #17900, "[Performance]: Fuse local NVFP4 tail after
+ *    NCCL fallback", Proposal: residual + RMSNorm + NVFP4 in one launch, with or
+ *    without a returned high-precision norm output; contiguous FP16/BF16 with
+ *    matching dtypes; per-tensor scale a contiguous FP32 scalar; no bias;
+ *    hidden divisible by 16; unsupported cases keep a separated path.
+ *  - TensorRT-LLM PR #17288, "Add NanoJet backend for AutoDeploy prefill-only
+ *    FP8 inference", Description: RMSNorm with FP8 quantisation in the kernel
+ *    epilogue; FP8 projection with an in-place residual add; Q/K RMSNorm and
+ *    RoPE.  Test Coverage: head-layout and RoPE-width guards.
+ *  - TensorRT-LLM PR #14361, "[perf] Add AutoDeploy NVFP4 RMSNorm quant
+ *    fusion", Changes table: fused add + RMSNorm + NVFP4 ops (with and without
+ *    the norm output) over a 2-D [tokens, hidden] view; review thread: one
+ *    shared helper for the packed-FP4 / scale-factor shapes.
+ *  - SGLang PR #32975, "perf: add fused norm + RoPE + uniform fp8 store for
+ *    TRT-LLM DSv4 sparse attention": norm + RoPE + FP8 store into a uniform
+ *    FP8 buffer.
+ *
+ * Numerics (every step is one IEEE binary32 operation, rounded to nearest
+ * even, never fused):
+ *   h_i   = RNE_T(x_i + res_i)                      written back to residual
+ *   ss    = sum_i h_i^2, exact, rounded once to binary32
+ *   r     = 1 / sqrt(ss / H + eps)                  four correctly rounded ops
+ *   n_i   = (h_i * r) * gamma_i
+ *   FP8   : q_i = E4M3(n_i / s)                     s = *scale (dequant scale)
+ *   NVFP4 : per 16 consecutive elements of a row:
+ *           sf = E4M3(G * (max|n_i| / 6)), S = value of sf,
+ *           c_i = E2M1(n_i * (G / S))   (c_i = +-0 when S == 0), G = *global_scale
+ * E4M3 is OCP E4M3FN (max 448, no infinities); E2M1 values {0,.5,1,1.5,2,3,4,6}
+ * with the sign in bit 3. Both encoders round to nearest, ties to even, and
+ * saturate; the sign of a code is the sign bit of its binary32 input.
+ *
+ * Layouts (all row-major, contiguous, no padding):
+ *   x, residual, norm_out : [tokens, hidden] of T (T = fp16 or bf16, one dtype per call)
+ *   gamma                 : [hidden] of T
+ *   FP8 q                 : [tokens, hidden] bytes, one E4M3 code per element
+ *   NVFP4 q               : [tokens, hidden/2] bytes; byte j of a row holds element 2j
+ *                           in bits 0-3 and element 2j+1 in bits 4-7
+ *   NVFP4 sf              : [tokens, hidden/16] bytes, E4M3 code of block b at column b
+ *   qkv, out (Q/K op)     : [tokens, (nq+nk+nv)*head_dim]: Q heads, then K, then V
+ *   cos_sin               : [max_pos, head_dim] binary32; columns k < head_dim/2 hold
+ *                           cos(angle_k), columns head_dim/2 + k hold sin(angle_k)
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are device pointers unless stated; the caller owns every buffer.
+ *    The library allocates nothing, keeps no state between calls and never
+ *    synchronises the host.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *    runs asynchronously. Scales are read on the device when the kernel runs,
+ *    so a producer kernel on the same stream may write them.
+ *  - Arguments are validated on the host before any HIP call. A rejected call
+ *    returns a nonzero status and enqueues nothing. tokens == 0 returns ANQ_OK
+ *    and enqueues nothing.
+ *  - residual is the only in/out buffer. Every output must be disjoint from
+ *    every other buffer of the call; x must be disjoint from residual; the
+ *    read-only inputs may overlap each other. Violations return ANQ_ERR_ALIAS.
+ *  - 16-byte alignment is required for x, residual, gamma, norm_out, q and
+ *    qkv/out/cos_sin; 4 bytes for scalars; 8 for positions; sf has none.
+ *  - Left to the caller (not checked): finite inputs, a finite nonzero scale,
+ *    0 <= positions[t] < max_pos. Breaking them gives unspecified codes, never
+ *    an out-of-bounds access except for positions outside [0, max_pos).
+ *  - Calls that share output buffers and overlap in time on different streams
+ *    race; calls on one stream are ordered.
+ */
+#ifndef ADDNORMQ_H
+#define ADDNORMQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Activation type T of a call. */
+typedef enum { ANQ_F16 = 0, ANQ_BF16 = 1 } anq_dtype;
+
+/* Status codes. ANQ_ERR_UNSUPPORTED is the "keep your separated path" answer
+ * for valid arguments outside what the fused kernels cover. */
+enum {
+  ANQ_OK = 0,
+  ANQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  ANQ_ERR_SHAPE = 2,       /* tokens < 0, hidden <= 0, hidden % 16 != 0, size overflow */
+  ANQ_ERR_DTYPE = 3,       /* dtype is not ANQ_F16 / ANQ_BF16 */
+  ANQ_ERR_ALIGN = 4,       /* a pointer breaks the alignment rule above */
+  ANQ_ERR_ALIAS = 5,       /* buffers overlap where they must not */
+  ANQ_ERR_UNSUPPORTED = 6, /* hidden > ANQ_MAX_HIDDEN, head_dim not supported, rotary_dim != head_dim */
+  ANQ_ERR_LAUNCH = 7,      /* the HIP launch failed (message via anq_status_string) */
+  ANQ_ERR_VALUE = 8        /* eps negative or not finite, max_pos < 1, negative head counts */
+};
+
+/* Largest hidden size the fused row kernels take (a row is held in registers). */
+#define ANQ_MAX_HIDDEN 65536
+
+/*
+ * Residual add + RMSNorm + per-tensor FP8 E4M3 quantisation.
+ * (NanoJet "RMSNorm with FP8 quantization in the kernel epilogue" and the
+ * in-place residual add, TensorRT-LLM PR #17288, Description.)
+ *
+ *   x        [tokens, hidden] T, read only
+ *   residual [tokens, hidden] T, in/out: receives h = RNE_T(x + residual)
+ *   gamma    [hidden] T
+ *   scale    device pointer to one binary32 s; q = E4M3(n / s)
+ *   eps      added to the mean square inside the square root (>= 0, finite)
+ *   q        [tokens, hidden] uint8 E4M3 codes (output)
+ *   norm_out [tokens, hidden] T (output) or NULL to skip it
+ */
+int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* gamma, const float* scale,
+                          float eps, int64_t tokens, int64_t hidden, int dtype, uint8_t* q,
+                          void* norm_out, void* stream);
+
+/*
+ * Residual add + RMSNorm + NVFP4 quantisation, with or without the
+ * high-precision norm output (residualRmsNormFp4Quant-style local tail,
+ * TensorRT-LLM issue #17900, Proposal).
+ *
+ *   global_scale  device pointer to one binary32 G (encode direction: the
+ *                 block scale is E4M3(G * amax / 6), codes are E2M1(n * G / S))
+ *   q             [tokens, hidden/2] uint8 packed E2M1 (output)
+ *   sf            [tokens, hidden/16] uint8 E4M3 block scales (output)
+ *   other arguments as for add_rmsnorm_quant_fp8.
+ */
+int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
+                            const float* global_scale, float eps, int64_t tokens, int64_t hidden,
+                            int dtype, uint8_t* q, uint8_t* sf, void* norm_out, void* stream);
+
+/*
+ * Q/K per-head RMSNorm + NeoX RoPE + uniform FP8 E4M3 store of a fused QKV
+ * buffer (SGLang PR #32975; Q/K RMSNorm and RoPE of TensorRT-LLM PR #17288).
+ *
+ * For token t and each of its nq Q heads and nk K heads (head_dim D each):
+ *   n = RMSNorm over D with gamma_q (Q) or gamma_k (K), binary32;
+ *   o_k       = n_k * cos_k - n_{k+D/2} * sin_k,
+ *   o_{k+D/2} = n_{k+D/2} * cos_k + n_k * sin_k   (k < D/2; each product and sum rounded),
+ *   with cos_k = cos_sin[positions[t], k], sin_k = cos_sin[positions[t], D/2 + k];
+ *   out = E4M3(o / s).  V heads: out = E4M3(v / s).
+ *
+ *   qkv        [tokens, (nq+nk+nv)*D] T, read only
+ *   gamma_q,gamma_k [D] T
+ *   positions  [tokens] int64 (device)
+ *   cos_sin    [max_pos, D] binary32
+ *   scale      device pointer to one binary32 s
+ *   rotary_dim must equal head_dim (partial rotation is not fused: ANQ_ERR_UNSUPPORTED)
+ *   head_dim   one of 32, 64, 128, 256, 512
+ *   out        [tokens, (nq+nk+nv)*D] uint8 E4M3 codes (output)
+ */
+int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
+                     const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                     const float* scale, float eps, int64_t tokens, int32_t nq, int32_t nk,
+                     int32_t nv, int32_t head_dim, int32_t rotary_dim, int dtype, uint8_t* out,
+                     void* stream);
+
+/*
+ * The one place that states the NVFP4 output shapes (the review thread of
+ * TensorRT-LLM PR #14361 asks for a single shared shape helper):
+ *   q_cols = hidden / 2, sf_cols = hidden / 16, for tokens rows each.
+ * Host only, no HIP call. Returns ANQ_OK, or ANQ_ERR_NULL / ANQ_ERR_SHAPE.
+ */
+int anq_nvfp4_shape(int64_t tokens, int64_t hidden, int64_t* q_cols, int64_t* sf_cols);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* anq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADDNORMQ_H */

@@ -1,0 +1,194 @@
+"""Python binding of libaddnormq.so, the MI355X (gfx950) fused local tail:
+residual add + RMSNorm + FP8 E4M3 / NVFP4 quantisation, and the Q/K per-head
+RMSNorm + NeoX RoPE + FP8 store.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/addnormq.h). PyTorch provides device memory
+and the current stream. There is no CPU path: without the built library, or
+without a GPU, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library binds to
+
+__all__ = ["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4", "qk_norm_rope_fp8",
+           "nvfp4_shape", "status_string", "lib", "AnqError", "LIB_PATH",
+           "ANQ_F16", "ANQ_BF16", "STATUS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddnormq.so")
+
+ANQ_F16, ANQ_BF16 = 0, 1
+STATUS = {0: "ANQ_OK", 1: "ANQ_ERR_NULL", 2: "ANQ_ERR_SHAPE", 3: "ANQ_ERR_DTYPE",
+          4: "ANQ_ERR_ALIGN", 5: "ANQ_ERR_ALIAS", 6: "ANQ_ERR_UNSUPPORTED", 7: "ANQ_ERR_LAUNCH",
+          8: "ANQ_ERR_VALUE"}
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_F = ctypes.c_float
+_SIGS = {
+    "add_rmsnorm_quant_fp8": [_P, _P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P, _P],
+    "add_rmsnorm_quant_nvfp4": [_P, _P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P, _P, _P],
+    "qk_norm_rope_fp8": [_P, _P, _P, _P, _P, _I64, _P, _F, _I64, _I32, _I32, _I32, _I32, _I32,
+                         ctypes.c_int, _P, _P],
+    "anq_nvfp4_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
+    "anq_status_string": [ctypes.c_int],
+}
+
+_lib = None
+
+
+class AnqError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn}: {STATUS.get(code, code)} ({status_string(code)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m nvfp4_quantization_place_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "anq_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().anq_status_string(code).decode()
+
+
+def nvfp4_shape(tokens: int, hidden: int) -> tuple[int, int]:
+    """(q_cols, sf_cols) of the NVFP4 outputs: hidden/2 packed bytes and hidden/16 scales per row."""
+    q, s = _I64(), _I64()
+    st = lib().anq_nvfp4_shape(tokens, hidden, ctypes.byref(q), ctypes.byref(s))
+    if st:
+        raise AnqError("anq_nvfp4_shape", st)
+    return q.value, s.value
+
+
+_DT = {torch.float16: ANQ_F16, torch.bfloat16: ANQ_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _check_gpu(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU (there is no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream(dev, stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _rows(x: torch.Tensor) -> tuple[int, int]:
+    hidden = x.shape[-1]
+    return (x.numel() // hidden if hidden else 0), hidden
+
+
+def _scalar(s: torch.Tensor, name: str):
+    if s.dtype != torch.float32 or s.numel() != 1:
+        raise ValueError(f"{name} must be a one-element float32 device tensor")
+
+
+def add_rmsnorm_quant_fp8(x, residual, gamma, scale, eps: float, norm_out: bool = False,
+                          q=None, norm=None, stream=None):
+    """residual += x (in place, rounded to T); n = RMSNorm(residual) * gamma;
+    returns (q, norm_out): q uint8 E4M3 codes of n / scale, norm_out n in T or None."""
+    dev = _check_gpu(x, residual, gamma, scale, q, norm)
+    _scalar(scale, "scale")
+    tokens, hidden = _rows(x)
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    if norm_out and norm is None:
+        norm = torch.empty_like(x)
+    if residual.dtype != x.dtype or gamma.dtype != x.dtype or residual.shape != x.shape:
+        raise ValueError("x, residual and gamma must share the dtype; x and residual the shape")
+    st = lib().add_rmsnorm_quant_fp8(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(scale), eps,
+                                     tokens, hidden, _dtype_code(x), _ptr(q), _ptr(norm),
+                                     _stream(dev, stream))
+    if st:
+        raise AnqError("add_rmsnorm_quant_fp8", st)
+    return q, norm
+
+
+def add_rmsnorm_quant_nvfp4(x, residual, gamma, global_scale, eps: float, norm_out: bool = False,
+                            q=None, sf=None, norm=None, stream=None):
+    """residual += x; n = RMSNorm(residual) * gamma; returns (q, sf, norm_out):
+    q [.., hidden/2] packed E2M1, sf [.., hidden/16] E4M3 block scales under
+    the global scale G, norm_out n in T or None."""
+    dev = _check_gpu(x, residual, gamma, global_scale, q, sf, norm)
+    _scalar(global_scale, "global_scale")
+    tokens, hidden = _rows(x)
+    if hidden % 16 == 0 and hidden > 0:
+        qc, sc = nvfp4_shape(tokens, hidden)
+    else:
+        qc, sc = max(hidden // 2, 1), max(hidden // 16, 1)
+    if q is None:
+        q = torch.empty(*x.shape[:-1], qc, dtype=torch.uint8, device=dev)
+    if sf is None:
+        sf = torch.empty(*x.shape[:-1], sc, dtype=torch.uint8, device=dev)
+    if norm_out and norm is None:
+        norm = torch.empty_like(x)
+    if residual.dtype != x.dtype or gamma.dtype != x.dtype or residual.shape != x.shape:
+        raise ValueError("x, residual and gamma must share the dtype; x and residual the shape")
+    st = lib().add_rmsnorm_quant_nvfp4(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(global_scale),
+                                       eps, tokens, hidden, _dtype_code(x), _ptr(q), _ptr(sf),
+                                       _ptr(norm), _stream(dev, stream))
+    if st:
+        raise AnqError("add_rmsnorm_quant_nvfp4", st)
+    return q, sf, norm
+
+
+def qk_norm_rope_fp8(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: float, nq: int,
+                     nk: int, nv: int, head_dim: int, rotary_dim: int | None = None, out=None,
+                     stream=None):
+    """Q/K per-head RMSNorm + NeoX RoPE + FP8 E4M3 of o / scale; V heads E4M3 of v / scale.
+    Returns out (uint8, the shape of qkv)."""
+    dev = _check_gpu(qkv, gamma_q, gamma_k, positions, cos_sin, scale, out)
+    _scalar(scale, "scale")
+    if positions.dtype != torch.int64 or cos_sin.dtype != torch.float32:
+        raise ValueError("positions must be int64 and cos_sin float32")
+    cols = (nq + nk + nv) * head_dim
+    if qkv.shape[-1] != cols:
+        raise ValueError(f"qkv last dim {qkv.shape[-1]} != (nq+nk+nv)*head_dim = {cols}")
+    tokens = qkv.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty(qkv.shape, dtype=torch.uint8, device=dev)
+    max_pos = cos_sin.shape[0]
+    st = lib().qk_norm_rope_fp8(_ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), _ptr(positions),
+                                _ptr(cos_sin), max_pos, _ptr(scale), eps, tokens, nq, nk, nv,
+                                head_dim, head_dim if rotary_dim is None else rotary_dim,
+                                _dtype_code(qkv), _ptr(out), _stream(dev, stream))
+    if st:
+        raise AnqError("qk_norm_rope_fp8", st)
+    return out

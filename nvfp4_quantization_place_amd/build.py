@@ -1,0 +1,65 @@
+"""Build libaddnormq.so in-tree with hipcc for gfx950.
+
+    python -m nvfp4_quantization_place_amd.build
+
+Flags that are part of correctness, not tuning:
+  -ffp-contract=off                           no a*b+c contraction: every step of the op
+                                              is a separately rounded binary32 operation
+  -fhip-fp32-correctly-rounded-divide-sqrt    IEEE division and square root (the default,
+                                              stated explicitly)
+  no -ffast-math / -ffinite-math-only
+  -Xclang -target-feature -Xclang -packed-fp32-ops   no packed-FP32 instructions
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libaddnormq.so")
+SOURCES = ["anq_api.hip", "anq_tail.hip", "anq_qk.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+            "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link the shared library; returns its path."""
+    objs = []
+    cc = hipcc()
+    tmp = os.path.join(PKG, "_build")
+    os.makedirs(tmp, exist_ok=True)
+    for src in SOURCES:
+        obj = os.path.join(tmp, src + ".o")
+        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    out_tmp = LIB + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(out_tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,190 @@
+// C-ABI front end: argument validation (host only, before any HIP call),
+// tiling choice and launch. The contract of every entry point is stated in
+// include/addnormq.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/addnormq.h"
+#include "anq_internal.h"
+
+namespace {
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi), empty when lo == hi
+};
+
+Span span(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(const Span& a, const Span& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// outputs[i] must not overlap any other buffer; inputs may overlap each other
+bool any_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+  }
+  return false;
+}
+
+bool valid_dtype(int d) { return d == ANQ_F16 || d == ANQ_BF16; }
+
+bool valid_eps(float eps) { return isfinite(eps) && eps >= 0.0f; }
+
+// Common checks of the two row ops; fills the byte sizes on success.
+int check_tail(const void* x, const void* residual, const void* gamma, const float* scale,
+               float eps, int64_t tokens, int64_t hidden, int dtype, const void* q,
+               const void* norm_out, int64_t* act_bytes) {
+  if (!x || !residual || !gamma || !scale || !q) return ANQ_ERR_NULL;
+  if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
+  if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
+  if (hidden > ANQ_MAX_HIDDEN) return ANQ_ERR_UNSUPPORTED;
+  if (tokens > INT64_MAX / (2 * hidden)) return ANQ_ERR_SHAPE;
+  if (!valid_eps(eps)) return ANQ_ERR_VALUE;
+  if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(gamma, 16) || !aligned(q, 16) ||
+      (norm_out && !aligned(norm_out, 16)) || !aligned(scale, 4))
+    return ANQ_ERR_ALIGN;
+  *act_bytes = tokens * hidden * 2;
+  return ANQ_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? ANQ_OK : ANQ_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* gamma,
+                                     const float* scale, float eps, int64_t tokens, int64_t hidden,
+                                     int dtype, uint8_t* q, void* norm_out, void* stream) {
+  int64_t act = 0;
+  int st = check_tail(x, residual, gamma, scale, eps, tokens, hidden, dtype, q, norm_out, &act);
+  if (st != ANQ_OK) return st;
+  const Span outs[3] = {span(residual, act), span(q, tokens * hidden), span(norm_out, norm_out ? act : 0)};
+  const Span ins[3] = {span(x, act), span(gamma, hidden * 2), span(scale, 4)};
+  if (any_alias(outs, 3, ins, 3)) return ANQ_ERR_ALIAS;
+  if (tokens == 0) return ANQ_OK;
+
+  anq::TailParams p{};
+  p.x = x;
+  p.residual = residual;
+  p.gamma = gamma;
+  p.scale = scale;
+  p.norm_out = norm_out;
+  p.q = q;
+  p.sf = nullptr;
+  p.eps = eps;
+  p.tokens = tokens;
+  p.hidden = (int32_t)hidden;
+  p.vec = (int32_t)(hidden / 8);
+  const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
+  return launch_status(anq::launch_tail(dtype, anq::kEpiFp8, norm_out != nullptr, p, t,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
+                                       const float* global_scale, float eps, int64_t tokens,
+                                       int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
+                                       void* norm_out, void* stream) {
+  if (!sf) return ANQ_ERR_NULL;
+  int64_t act = 0;
+  int st = check_tail(x, residual, gamma, global_scale, eps, tokens, hidden, dtype, q, norm_out,
+                      &act);
+  if (st != ANQ_OK) return st;
+  const Span outs[4] = {span(residual, act), span(q, tokens * (hidden / 2)),
+                        span(sf, tokens * (hidden / 16)), span(norm_out, norm_out ? act : 0)};
+  const Span ins[3] = {span(x, act), span(gamma, hidden * 2), span(global_scale, 4)};
+  if (any_alias(outs, 4, ins, 3)) return ANQ_ERR_ALIAS;
+  if (tokens == 0) return ANQ_OK;
+
+  anq::TailParams p{};
+  p.x = x;
+  p.residual = residual;
+  p.gamma = gamma;
+  p.scale = global_scale;
+  p.norm_out = norm_out;
+  p.q = q;
+  p.sf = sf;
+  p.eps = eps;
+  p.tokens = tokens;
+  p.hidden = (int32_t)hidden;
+  p.vec = (int32_t)(hidden / 8);
+  const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
+  return launch_status(anq::launch_tail(dtype, anq::kEpiNvfp4, norm_out != nullptr, p, t,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
+                                const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                const float* scale, float eps, int64_t tokens, int32_t nq,
+                                int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
+                                int dtype, uint8_t* out, void* stream) {
+  if (!qkv || !positions || !cos_sin || !scale || !out) return ANQ_ERR_NULL;
+  if (nq > 0 && !gamma_q) return ANQ_ERR_NULL;
+  if (nk > 0 && !gamma_k) return ANQ_ERR_NULL;
+  if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
+  if (nq < 0 || nk < 0 || nv < 0 || max_pos < 1) return ANQ_ERR_VALUE;
+  if (tokens < 0 || head_dim <= 0 || nq + nk + nv == 0) return ANQ_ERR_SHAPE;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return ANQ_ERR_UNSUPPORTED;
+  if (rotary_dim != head_dim) return ANQ_ERR_UNSUPPORTED;
+  if (!valid_eps(eps)) return ANQ_ERR_VALUE;
+  const int64_t cols = (int64_t)(nq + nk + nv) * head_dim;
+  if (tokens > INT64_MAX / (2 * cols) || max_pos > INT64_MAX / (4 * (int64_t)head_dim))
+    return ANQ_ERR_SHAPE;
+  if (!aligned(qkv, 16) || !aligned(out, 16) || !aligned(cos_sin, 16) || !aligned(positions, 8) ||
+      !aligned(scale, 4) || (nq > 0 && !aligned(gamma_q, 16)) || (nk > 0 && !aligned(gamma_k, 16)))
+    return ANQ_ERR_ALIGN;
+  const Span outs[1] = {span(out, tokens * cols)};
+  const Span ins[6] = {span(qkv, tokens * cols * 2), span(nq ? gamma_q : nullptr, nq ? head_dim * 2 : 0),
+                       span(nk ? gamma_k : nullptr, nk ? head_dim * 2 : 0), span(positions, tokens * 8),
+                       span(cos_sin, max_pos * head_dim * 4), span(scale, 4)};
+  if (any_alias(outs, 1, ins, 6)) return ANQ_ERR_ALIAS;
+  if (tokens == 0) return ANQ_OK;
+
+  anq::QKParams p{};
+  p.qkv = qkv;
+  p.gamma_q = gamma_q;
+  p.gamma_k = gamma_k;
+  p.positions = positions;
+  p.cos_sin = cos_sin;
+  p.scale = scale;
+  p.out = out;
+  p.eps = eps;
+  p.tokens = tokens;
+  p.pairs = tokens * (int64_t)(nq + nk + nv);
+  p.nq = nq;
+  p.nk = nk;
+  p.nv = nv;
+  p.head_dim = head_dim;
+  return launch_status(anq::launch_qk(dtype, p, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int anq_nvfp4_shape(int64_t tokens, int64_t hidden, int64_t* q_cols, int64_t* sf_cols) {
+  if (!q_cols || !sf_cols) return ANQ_ERR_NULL;
+  if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
+  *q_cols = hidden / 2;
+  *sf_cols = hidden / 16;
+  return ANQ_OK;
+}
+
+extern "C" const char* anq_status_string(int status) {
+  switch (status) {
+    case ANQ_OK: return "ok";
+    case ANQ_ERR_NULL: return "a required pointer is NULL";
+    case ANQ_ERR_SHAPE: return "bad shape: tokens < 0, hidden <= 0, hidden % 16 != 0 or size overflow";
+    case ANQ_ERR_DTYPE: return "dtype must be ANQ_F16 or ANQ_BF16";
+    case ANQ_ERR_ALIGN: return "misaligned pointer (16 bytes for tensors, 4 for scalars, 8 for positions)";
+    case ANQ_ERR_ALIAS: return "output buffers overlap another buffer";
+    case ANQ_ERR_UNSUPPORTED: return "unsupported case (hidden > 65536, head_dim not in {32..512}, rotary_dim != head_dim): use a separated path";
+    case ANQ_ERR_LAUNCH: return "HIP kernel launch failed";
+    case ANQ_ERR_VALUE: return "bad scalar argument (eps < 0 or not finite, max_pos < 1, negative head count)";
+    default: return "unknown status";
+  }
+}

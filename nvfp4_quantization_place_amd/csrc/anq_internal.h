@@ -1,0 +1,57 @@
+// Launch interface between the C-ABI front end (anq_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace anq {
+
+enum Epilogue { kEpiFp8 = 0, kEpiNvfp4 = 1 };
+
+struct TailParams {
+  const void* x;
+  void* residual;
+  const void* gamma;
+  const float* scale;  // FP8: s; NVFP4: G
+  void* norm_out;      // may be null
+  uint8_t* q;
+  uint8_t* sf;         // NVFP4 only
+  float eps;
+  int64_t tokens;
+  int32_t hidden;
+  int32_t vec;         // hidden / 8: 16-byte vectors per row
+};
+
+// How a row is spread over lanes: `group` lanes of one wavefront per row
+// (16, 32 or 64; the workgroup holds 256 / group rows), or group == 0 for one
+// row per workgroup of `block` lanes. Each lane owns vectors lane + k*lanes,
+// k < vec_per_lane.
+struct Tiling {
+  int group;
+  int vec_per_lane;
+  int block;
+  int64_t grid;
+};
+
+Tiling pick_tail_tiling(int32_t vec, int64_t tokens);
+
+hipError_t launch_tail(int dtype, int epi, bool norm_out, const TailParams& p, const Tiling& t,
+                       hipStream_t stream);
+
+struct QKParams {
+  const void* qkv;
+  const void* gamma_q;
+  const void* gamma_k;
+  const int64_t* positions;
+  const float* cos_sin;
+  const float* scale;
+  uint8_t* out;
+  float eps;
+  int64_t tokens;
+  int64_t pairs;  // tokens * (nq + nk + nv)
+  int32_t nq, nk, nv, head_dim;
+};
+
+hipError_t launch_qk(int dtype, const QKParams& p, hipStream_t stream);
+
+}  // namespace anq

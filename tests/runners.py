@@ -1,0 +1,69 @@
+"""Run one workload through the HIP library (via the Python binding) and
+through the CPU oracle, on the same seeded inputs, and hand back numpy arrays
+of raw bits for the comparators."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import workloads as W
+
+
+def _np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def oracle_global_scale(inp: W.TailInputs) -> np.float32:
+    n = O.rmsnorm_f32(W.bits(inp.x), W.bits(inp.residual), W.bits(inp.gamma), inp.dtype, inp.eps)
+    return O.nvfp4_global_scale(n)
+
+
+def gpu_tail(inp: W.TailInputs, scale: float, dev="cuda", stream=None) -> dict:
+    import nvfp4_quantization_place_amd as A
+    x = inp.x.to(dev)
+    res = inp.residual.to(dev)
+    g = inp.gamma.to(dev)
+    s = torch.tensor([scale], dtype=torch.float32, device=dev)
+    if inp.op == "fp8":
+        q, norm = A.add_rmsnorm_quant_fp8(x, res, g, s, inp.eps, norm_out=inp.norm_out, stream=stream)
+        out = dict(q=q)
+    else:
+        q, sf, norm = A.add_rmsnorm_quant_nvfp4(x, res, g, s, inp.eps, norm_out=inp.norm_out,
+                                                stream=stream)
+        out = dict(q=q, sf=sf)
+    torch.cuda.synchronize()
+    out["residual"] = res
+    if norm is not None:
+        out["norm_out"] = norm
+    return {k: _np(v) for k, v in out.items()}
+
+
+def oracle_tail(inp: W.TailInputs, scale: float, rows=None) -> dict:
+    sel = slice(None) if rows is None else rows
+    xb = W.bits(inp.x)[sel]
+    rb = W.bits(inp.residual)[sel]
+    gb = W.bits(inp.gamma)
+    if inp.op == "fp8":
+        return O.add_rmsnorm_quant_fp8(xb, rb, gb, inp.dtype, scale, inp.eps, inp.norm_out)
+    return O.add_rmsnorm_quant_nvfp4(xb, rb, gb, inp.dtype, scale, inp.eps, inp.norm_out)
+
+
+def gpu_qk(inp: W.QKInputs, dev="cuda", stream=None) -> np.ndarray:
+    import nvfp4_quantization_place_amd as A
+    out = A.qk_norm_rope_fp8(inp.qkv.to(dev), inp.gamma_q.to(dev), inp.gamma_k.to(dev),
+                             inp.positions.to(dev), torch.from_numpy(inp.cos_sin).to(dev),
+                             torch.tensor([inp.scale], dtype=torch.float32, device=dev), inp.eps,
+                             inp.nq, inp.nk, inp.nv, inp.head_dim, stream=stream)
+    torch.cuda.synchronize()
+    return _np(out)
+
+
+def oracle_qk(inp: W.QKInputs, tokens=None) -> np.ndarray:
+    sel = slice(None) if tokens is None else tokens
+    return O.qk_norm_rope_fp8(W.bits(inp.qkv)[sel], W.bits(inp.gamma_q), W.bits(inp.gamma_k),
+                              inp.positions.numpy()[sel], inp.cos_sin, inp.scale, inp.eps, inp.nq,
+                              inp.nk, inp.nv, inp.head_dim, inp.dtype)["out"]

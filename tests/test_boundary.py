@@ -1,0 +1,158 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every entry
+point that include/addnormq.h declares, and its host-side validation rejects
+bad arguments with the documented status before any HIP call (tokens == 0 is
+a no-op). No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_quantization_place_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "addnormq.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, LAUNCH, VALUE = range(9)
+
+# fake, well-aligned, disjoint device addresses: validation never dereferences them
+BASE = 1 << 40
+MB = 1 << 20
+
+
+def addr(i, off=0):
+    return BASE + i * 64 * MB + off
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(A.LIB_PATH):
+        from nvfp4_quantization_place_amd import build
+        build.build()
+    return A.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4",
+                                           "qk_norm_rope_fp8", "anq_nvfp4_shape",
+                                           "anq_status_string"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    # exported as plain C symbols (no C++ mangling)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_status_strings(L):
+    for code in range(9):
+        s = A.status_string(code)
+        assert s and s != "unknown status"
+    assert A.status_string(99) == "unknown status"
+
+
+def test_nvfp4_shape_helper(L):
+    assert A.nvfp4_shape(64, 8192) == (4096, 512)
+    assert A.nvfp4_shape(8192, 7168) == (3584, 448)
+    assert A.nvfp4_shape(0, 16) == (8, 1)
+    q, s = ctypes.c_int64(), ctypes.c_int64()
+    assert L.anq_nvfp4_shape(4, 24, ctypes.byref(q), ctypes.byref(s)) == SHAPE
+    assert L.anq_nvfp4_shape(4, 0, ctypes.byref(q), ctypes.byref(s)) == SHAPE
+    assert L.anq_nvfp4_shape(-1, 16, ctypes.byref(q), ctypes.byref(s)) == SHAPE
+    assert L.anq_nvfp4_shape(4, 16, None, ctypes.byref(s)) == NULL
+
+
+def fp8(L, **kw):
+    a = dict(x=addr(0), res=addr(1), gamma=addr(2), scale=addr(3), eps=1e-6, tokens=0,
+             hidden=128, dtype=0, q=addr(4), norm=addr(5), stream=None)
+    a.update(kw)
+    return L.add_rmsnorm_quant_fp8(a["x"], a["res"], a["gamma"], a["scale"], a["eps"], a["tokens"],
+                                   a["hidden"], a["dtype"], a["q"], a["norm"], a["stream"])
+
+
+def nvfp4(L, **kw):
+    a = dict(x=addr(0), res=addr(1), gamma=addr(2), scale=addr(3), eps=1e-6, tokens=0,
+             hidden=128, dtype=1, q=addr(4), sf=addr(6), norm=addr(5), stream=None)
+    a.update(kw)
+    return L.add_rmsnorm_quant_nvfp4(a["x"], a["res"], a["gamma"], a["scale"], a["eps"],
+                                     a["tokens"], a["hidden"], a["dtype"], a["q"], a["sf"],
+                                     a["norm"], a["stream"])
+
+
+def qk(L, **kw):
+    a = dict(qkv=addr(0), gq=addr(1), gk=addr(2), pos=addr(3), cs=addr(4), max_pos=4096,
+             scale=addr(5), eps=1e-6, tokens=0, nq=16, nk=8, nv=8, D=128, rot=128, dtype=1,
+             out=addr(6), stream=None)
+    a.update(kw)
+    return L.qk_norm_rope_fp8(a["qkv"], a["gq"], a["gk"], a["pos"], a["cs"], a["max_pos"],
+                              a["scale"], a["eps"], a["tokens"], a["nq"], a["nk"], a["nv"], a["D"],
+                              a["rot"], a["dtype"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("op", [fp8, nvfp4])
+def test_row_ops_validation(L, op):
+    assert op(L) == OK                                   # tokens == 0: no-op, no HIP call
+    assert op(L, norm=None) == OK                        # norm_out is optional
+    for k in ("x", "res", "gamma", "scale", "q"):
+        assert op(L, **{k: None}) == NULL, k
+    assert op(L, dtype=2) == DTYPE
+    assert op(L, dtype=-1) == DTYPE
+    for h in (0, -16, 24, 100, 8):
+        assert op(L, hidden=h) == SHAPE, h
+    assert op(L, tokens=-1) == SHAPE
+    assert op(L, hidden=65536 + 16) == UNSUP
+    assert op(L, tokens=1 << 60, hidden=1024) == SHAPE   # size overflow
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert op(L, eps=eps) == VALUE
+    for k in ("x", "res", "gamma", "q", "norm"):
+        assert op(L, **{k: addr(7, 8)}) == ALIGN, k
+    assert op(L, scale=addr(3, 2)) == ALIGN
+    assert op(L, scale=addr(3, 4)) == OK                 # 4-byte aligned scalar is fine
+
+
+def test_row_ops_alias_rules(L):
+    t, h = 16, 128
+    act = t * h * 2
+    # every case below with tokens > 0 is rejected before any HIP call
+    assert fp8(L, tokens=t, hidden=h, res=addr(0)) == ALIAS   # x is read while residual is written
+    assert fp8(L, tokens=0, hidden=h, res=addr(0)) == OK      # empty buffers overlap nothing
+    assert fp8(L, tokens=t, hidden=h, q=addr(1, act - 16)) == ALIAS  # q overlaps residual's tail
+    assert fp8(L, tokens=t, hidden=h, norm=addr(4, 16)) == ALIAS     # norm_out overlaps q
+    assert fp8(L, tokens=t, hidden=h, scale=addr(4, 4)) == ALIAS     # scale inside q
+    assert fp8(L, tokens=0, hidden=h, gamma=addr(0)) == OK           # read-only inputs may overlap
+    assert nvfp4(L, tokens=t, hidden=h, sf=addr(4, 16)) == ALIAS     # sf inside q
+    assert nvfp4(L, sf=None) == NULL
+
+
+def test_qk_validation(L):
+    assert qk(L) == OK
+    for k in ("qkv", "pos", "cs", "scale", "out"):
+        assert qk(L, **{k: None}) == NULL, k
+    assert qk(L, gq=None) == NULL
+    assert qk(L, gq=None, nq=0) == OK                   # gamma_q unused without Q heads
+    assert qk(L, gk=None, nk=0) == OK
+    assert qk(L, dtype=5) == DTYPE
+    assert qk(L, rot=64) == UNSUP                        # partial rotary width is not fused
+    for d in (48, 96, 1024, 16):
+        assert qk(L, D=d, rot=d) == UNSUP, d
+    assert qk(L, nq=-1) == VALUE
+    assert qk(L, max_pos=0) == VALUE
+    assert qk(L, nq=0, nk=0, nv=0) == SHAPE
+    assert qk(L, tokens=-2) == SHAPE
+    assert qk(L, eps=-1.0) == VALUE
+    assert qk(L, qkv=addr(0, 8)) == ALIGN
+    assert qk(L, pos=addr(3, 4)) == ALIGN
+    assert qk(L, tokens=4, out=addr(0)) == ALIAS        # rejected before any HIP call
+    assert qk(L, tokens=4, cs=addr(6)) == ALIAS
+    assert qk(L, tokens=4, pos=addr(6, 8)) == ALIAS
