@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused add + RMSNorm + FP8/NVFP4 tail (and the Q/K norm +
+RoPE + FP8 store) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-sweep] [--no-cpu]
+
+A step is one call of the fused op on one batch of the workload's seeded
+synthetic inputs, already resident in HBM. Inputs and outputs rotate over
+enough buffer sets (>= 1 GiB in total) that every call streams from HBM rather
+than from the 256 MB last-level cache. The timed region replays a HIP graph
+holding K calls, bracketed by device synchronisation; kernel time comes from
+HIP events on the launch stream. Eager (host-launched) time per call is
+reported beside it.
+
+Prints ONE JSON line. `value` is achieved algorithmic HBM throughput in GB/s
+on the headline workload (fp16 [64, 8192] add + RMSNorm + NVFP4, the shape the
+pages measure: 0.039 ms on an RTX 5060 Ti, TensorRT-LLM issue #17900,
+Performance result). `all_workloads` holds the same figures for every shape.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused add+RMSNorm+FP8/NVFP4 quant: µs/call and achieved HBM GB/s (% peak)"
+PEAK_GBS = 8000.0                      # MI355X HBM3E
+PAGES_US = {2: 39.0}                   # the pages' fused-tail latency for this exact workload
+ROTATE_BYTES = 1 << 30
+SCALARS = os.path.join(ROOT, "tests", "golden", "workload_scalars.json")
+TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "nvfp4_quantization_place_amd", "csrc")
+
+
+def algorithmic_bytes(inp) -> int:
+    """Bytes the method must move per call (gamma and scales counted once)."""
+    import workloads as W
+    if isinstance(inp, W.QKInputs):
+        D = inp.head_dim
+        C = (inp.nq + inp.nk + inp.nv) * D
+        return inp.tokens * C * 3 + inp.tokens * (4 * D + 8) + 4 * D + 4
+    M, H = inp.tokens, inp.hidden
+    per = 2 + 2 + 2 + (1 if inp.op == "fp8" else 0.5 + 1 / 16) + (2 if inp.norm_out else 0)
+    return int(round(M * H * per)) + 2 * H + 4
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    """Device-resident inputs and outputs of one workload, in R rotating sets."""
+
+    def __init__(self, k: int, scalars: dict, steps: int):
+        import torch
+
+        import workloads as W
+        self.k = k
+        self.inp = W.make_config(k)
+        self.bytes = algorithmic_bytes(self.inp)
+        # a graph of `steps` calls only ever touches `steps` sets
+        self.sets = max(2, min(math.ceil(ROTATE_BYTES / self.bytes), steps))
+        dev = "cuda"
+        inp = self.inp
+        if isinstance(inp, W.QKInputs):
+            self.kind = "qk"
+            qkv = inp.qkv.to(dev)
+            self.qkv = [qkv] + [qkv.clone() for _ in range(self.sets - 1)]
+            self.out = [torch.empty(qkv.shape, dtype=torch.uint8, device=dev) for _ in range(self.sets)]
+            self.gq, self.gk = inp.gamma_q.to(dev), inp.gamma_k.to(dev)
+            self.pos = inp.positions.to(dev)
+            self.cs = torch.from_numpy(inp.cos_sin).to(dev)
+            self.scale = torch.tensor([inp.scale], dtype=torch.float32, device=dev)
+            self.dtype = inp.dtype
+            self.name = inp.name
+            return
+        self.kind = inp.op
+        self.name = inp.name
+        self.dtype = inp.dtype
+        x, r = inp.x.to(dev), inp.residual.to(dev)
+        self.x = [x] + [x.clone() for _ in range(self.sets - 1)]
+        self.res = [r] + [r.clone() for _ in range(self.sets - 1)]
+        self.g = inp.gamma.to(dev)
+        if inp.op == "fp8":
+            s = inp.scale
+        else:
+            s = scalars[str(k)]["global_scale"]
+        self.scale = torch.tensor([s], dtype=torch.float32, device=dev)
+        M, H = inp.tokens, inp.hidden
+        qcols = H if inp.op == "fp8" else H // 2
+        self.q = [torch.empty(M, qcols, dtype=torch.uint8, device=dev) for _ in range(self.sets)]
+        self.sf = ([torch.empty(M, H // 16, dtype=torch.uint8, device=dev) for _ in range(self.sets)]
+                   if inp.op == "nvfp4" else None)
+        self.norm = ([torch.empty_like(x) for _ in range(self.sets)] if inp.norm_out else None)
+
+    def call(self, i: int):
+        import nvfp4_quantization_place_amd as A
+        j = i % self.sets
+        inp = self.inp
+        if self.kind == "qk":
+            A.qk_norm_rope_fp8(self.qkv[j], self.gq, self.gk, self.pos, self.cs, self.scale, inp.eps,
+                               inp.nq, inp.nk, inp.nv, inp.head_dim, out=self.out[j])
+        elif self.kind == "fp8":
+            A.add_rmsnorm_quant_fp8(self.x[j], self.res[j], self.g, self.scale, inp.eps,
+                                    q=self.q[j], norm=self.norm[j] if self.norm else None)
+        else:
+            A.add_rmsnorm_quant_nvfp4(self.x[j], self.res[j], self.g, self.scale, inp.eps,
+                                      q=self.q[j], sf=self.sf[j],
+                                      norm=self.norm[j] if self.norm else None)
+
+
+def time_workload(w: Workload, steps: int, warmup: int) -> dict:
+    import torch
+    for i in range(warmup):
+        w.call(i)
+    torch.cuda.synchronize()
+    # eager: host-launched calls, wall clock
+    t0 = time.perf_counter()
+    for i in range(steps):
+        w.call(i)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) / steps * 1e6
+    # graph of `steps` calls, replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(2):
+            w.call(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            w.call(i)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    dev_us = ev0.elapsed_time(ev1) * 1e3 / steps
+    gbs = w.bytes / (dev_us * 1e-6) / 1e9
+    return dict(workload=w.name, io_dtype=w.dtype, bytes_per_call=w.bytes, rotating_sets=w.sets,
+                us_per_call=round(dev_us, 3), eager_us_per_call=round(eager_us, 3),
+                wall_ms_timed=round(wall_s * 1e3, 3), gbs=round(gbs, 1),
+                frac_of_peak=round(gbs / PEAK_GBS, 4))
+
+
+def cpu_baseline(k: int, scalars: dict, budget_s: float = 10.0) -> dict:
+    """The oracle as it stands, single process, on a bounded sample of the
+    same workload: whole calls for small workloads, a fixed slice of rows
+    (tokens) for large ones, repeated until about budget_s of CPU time."""
+    import oracle as O
+    import workloads as W
+    inp = W.make_config(k)
+    if isinstance(inp, W.QKInputs):
+        rows = min(inp.tokens, 64)
+        sub = W.QKInputs(**{**inp.__dict__, "tokens": rows, "qkv": inp.qkv[:rows],
+                            "positions": inp.positions[:rows]})
+        args = (W.bits(sub.qkv), W.bits(sub.gamma_q), W.bits(sub.gamma_k), sub.positions.numpy(),
+                sub.cos_sin, sub.scale, sub.eps, sub.nq, sub.nk, sub.nv, sub.head_dim, sub.dtype)
+        fn = lambda: O.qk_norm_rope_fp8(*args)  # noqa: E731
+        nbytes = algorithmic_bytes(sub)
+        sample = f"{rows} of {inp.tokens} tokens per pass"
+    else:
+        rows = min(inp.tokens, max(1, (64 * 8192) // inp.hidden))
+        xb, rb, gb = W.bits(inp.x)[:rows], W.bits(inp.residual)[:rows], W.bits(inp.gamma)
+        if inp.op == "fp8":
+            fn = lambda: O.add_rmsnorm_quant_fp8(xb, rb, gb, inp.dtype, inp.scale, inp.eps,  # noqa
+                                                 inp.norm_out)
+        else:
+            G = scalars[str(k)]["global_scale"]
+            fn = lambda: O.add_rmsnorm_quant_nvfp4(xb, rb, gb, inp.dtype, G, inp.eps,  # noqa
+                                                   inp.norm_out)
+        sub = W.TailInputs(**{**inp.__dict__, "tokens": rows})
+        nbytes = algorithmic_bytes(sub)
+        sample = f"{rows} of {inp.tokens} rows per pass"
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(nbytes * passes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": f"{sample}, {passes} passes in {el:.1f} s",
+            "us_per_call_equiv": round(el / passes * (inp.tokens / rows) * 1e6, 1)}
+
+
+def load_traffic(k: int, bytes_per_call: int):
+    """HBM bytes per call measured by rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE), if they were taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get(str(k))
+    if not e or t.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_call")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-sweep", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the fused tail is row-parallel and this build runs "
+              "on a single MI355X; rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_quantization_place_amd as A
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    A.lib()
+    with open(SCALARS) as fh:
+        scalars = json.load(fh)
+
+    todo = [args.workload] + ([] if args.no_sweep else [k for k in (1, 2, 3, 4, 5) if k != args.workload])
+    results = {}
+    for k in todo:
+        w = Workload(k, scalars, args.steps)
+        r = time_workload(w, args.steps, args.warmup)
+        r["traffic_bytes_per_call"] = load_traffic(k, w.bytes)
+        results[k] = r
+        print(f"# workload {k} {r['workload']}: {r['us_per_call']} us/call (graph), "
+              f"{r['eager_us_per_call']} us/call (eager), {r['gbs']} GB/s", file=sys.stderr, flush=True)
+        del w
+        torch.cuda.empty_cache()
+
+    head = results[args.workload]
+    inp_dtype = head["io_dtype"]
+    traffic = head["traffic_bytes_per_call"]
+    line = {
+        "metric": METRIC,
+        "value": head["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_call"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(head["gbs"] / (head["bytes_per_call"] / PAGES_US[args.workload] / 1e3), 2)
+                        if args.workload in PAGES_US else None),
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "io_dtype": inp_dtype,
+                   "us_per_call": head["us_per_call"], "eager_us_per_call": head["eager_us_per_call"],
+                   "bytes_per_call": head["bytes_per_call"], "timing": "HIP graph of steps calls, "
+                   "HIP events on the launch stream; inputs rotate over >= 1 GiB of buffers"},
+        "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": head["frac_of_peak"],
+                     "traffic": (round(traffic / (head["us_per_call"] * 1e-6) / 1e9, 1)
+                                 if traffic else None)},
+        "all_workloads": {str(k): v for k, v in results.items()},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.workload, scalars)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

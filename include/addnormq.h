@@ -61,7 +61,8 @@
  *    so a producer kernel on the same stream may write them.
  *  - Arguments are validated on the host before any HIP call. A rejected call
  *    returns a nonzero status and enqueues nothing. tokens == 0 returns ANQ_OK
- *    and enqueues nothing.
+ *    and enqueues nothing; the token-sized buffers (x, residual, q, sf,
+ *    norm_out, qkv, positions, out) may then be NULL, as empty tensors are.
  *  - residual is the only in/out buffer. Every output must be disjoint from
  *    every other buffer of the call; x must be disjoint from residual; the
  *    read-only inputs may overlap each other. Violations return ANQ_ERR_ALIAS.

@@ -43,7 +43,8 @@ bool valid_eps(float eps) { return isfinite(eps) && eps >= 0.0f; }
 int check_tail(const void* x, const void* residual, const void* gamma, const float* scale,
                float eps, int64_t tokens, int64_t hidden, int dtype, const void* q,
                const void* norm_out, int64_t* act_bytes) {
-  if (!x || !residual || !gamma || !scale || !q) return ANQ_ERR_NULL;
+  // token-sized buffers may be NULL when there are no tokens (empty tensors)
+  if (!gamma || !scale || (tokens != 0 && (!x || !residual || !q))) return ANQ_ERR_NULL;
   if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
   if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
   if (hidden > ANQ_MAX_HIDDEN) return ANQ_ERR_UNSUPPORTED;
@@ -92,7 +93,7 @@ extern "C" int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void
                                        const float* global_scale, float eps, int64_t tokens,
                                        int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
                                        void* norm_out, void* stream) {
-  if (!sf) return ANQ_ERR_NULL;
+  if (!sf && tokens != 0) return ANQ_ERR_NULL;
   int64_t act = 0;
   int st = check_tail(x, residual, gamma, global_scale, eps, tokens, hidden, dtype, q, norm_out,
                       &act);
@@ -125,7 +126,7 @@ extern "C" int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void
                                 const float* scale, float eps, int64_t tokens, int32_t nq,
                                 int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
                                 int dtype, uint8_t* out, void* stream) {
-  if (!qkv || !positions || !cos_sin || !scale || !out) return ANQ_ERR_NULL;
+  if (!cos_sin || !scale || (tokens != 0 && (!qkv || !positions || !out))) return ANQ_ERR_NULL;
   if (nq > 0 && !gamma_q) return ANQ_ERR_NULL;
   if (nk > 0 && !gamma_k) return ANQ_ERR_NULL;
   if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;

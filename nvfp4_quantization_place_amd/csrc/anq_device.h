@@ -76,42 +76,46 @@ __device__ __forceinline__ U4 pack8(const float (&f)[8]) {
 
 // ------------------------------------------------------------ E4M3 / E2M1
 
-// binary32 -> OCP E4M3FN code, nearest even, saturating to +-448, sign copied.
-// Subnormals (|v| < 2^-6) are multiples of 2^-9: v * 512 is exact and rintf
-// rounds half to even; a result of 8 is the smallest normal 0x08, as it should
-// be. Normals round the binary32 significand to 3 bits with the usual
-// add-half-minus-one-plus-lsb trick and re-bias the exponent (127 -> 7).
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = __builtin_fabsf(v);
-  uint32_t mag;
-  if (a >= 448.0f) {
-    mag = 0x7Eu;
-  } else if (a < 0.015625f) {
-    mag = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);
-    mag = (b >> 20) - (120u << 3);
-  }
-  return sign | mag;
+// gfx950 conversion instructions, used exactly where their semantics match the
+// definition of the op (checked against definition-based encoders over every
+// rounding interval, exact ties included, on the target):
+//  * v_cvt_pk_fp8_f32 converts to OCP E4M3FN, nearest even, signed zeros kept,
+//    subnormals kept; it returns NaN beyond +-448, so inputs are first clamped
+//    with v_med3_f32 (saturation to +-448 is the nearest-even result there).
+//  * v_cvt_scalef32_pk_fp4_f32 with scale 1.0 converts to E2M1, nearest even,
+//    saturating at +-6, sign copied; the first operand goes to the low nibble.
+
+// Four binary32 values -> four E4M3FN codes, element i in byte i.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, 448.0f, -448.0f);
+  b = __builtin_amdgcn_fmed3f(b, 448.0f, -448.0f);
+  c = __builtin_amdgcn_fmed3f(c, 448.0f, -448.0f);
+  d = __builtin_amdgcn_fmed3f(d, 448.0f, -448.0f);
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
 
-// Value of a non-negative E4M3FN code (the NVFP4 block scale), exact.
+// One non-negative binary32 value -> its E4M3FN code.
+__device__ __forceinline__ uint32_t e4m3_pos(float a) {
+  a = __builtin_amdgcn_fmed3f(a, 448.0f, -448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, 0.0f, 0, false) & 0xFFu;
+}
+
+// Value of a non-negative E4M3FN code (the NVFP4 block scale), exact:
+// E >= 1: 2^(E-7) (1 + M/8); E = 0: M 2^-9.
 __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
   const uint32_t e = c >> 3, m = c & 7u;
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
-// binary32 -> E2M1 code: count the rounding thresholds of |v| (the midpoints
-// 0.25 .. 5 of the value set), strict where the tie goes down to an even code,
-// inclusive where it goes up to one; 6 and beyond saturate to code 7.
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-  const float a = __builtin_fabsf(v);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-               (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
+// Eight binary32 values -> eight E2M1 codes, element i in bits 4i..4i+3.
+__device__ __forceinline__ uint32_t e2m1x8(const float (&v)[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
 }
 
 // ---------------------------------------------------------------- division

@@ -98,15 +98,16 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
         ob[i] = b[i];
       }
     }
-    uint2 qa, qb;
-    qa.x = qa.y = qb.x = qb.y = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qa.x |= e4m3_encode(div_rn(oa[i], sc, inv_sc)) << (8 * i);
-      qa.y |= e4m3_encode(div_rn(oa[4 + i], sc, inv_sc)) << (8 * i);
-      qb.x |= e4m3_encode(div_rn(ob[i], sc, inv_sc)) << (8 * i);
-      qb.y |= e4m3_encode(div_rn(ob[4 + i], sc, inv_sc)) << (8 * i);
+    for (int i = 0; i < 8; ++i) {
+      oa[i] = div_rn(oa[i], sc, inv_sc);
+      ob[i] = div_rn(ob[i], sc, inv_sc);
     }
+    uint2 qa, qb;
+    qa.x = e4m3x4(oa[0], oa[1], oa[2], oa[3]);
+    qa.y = e4m3x4(oa[4], oa[5], oa[6], oa[7]);
+    qb.x = e4m3x4(ob[0], ob[1], ob[2], ob[3]);
+    qb.y = e4m3x4(ob[4], ob[5], ob[6], ob[7]);
     *reinterpret_cast<uint2*>(p.out + ea) = qa;
     *reinterpret_cast<uint2*>(p.out + eb) = qb;
   }

@@ -193,15 +193,12 @@ __global__ void __launch_bounds__(1024) tail_kernel(TailParams p) {
       for (int i = 0; i < 8; ++i) n[i] = (h[k][i] * r) * g[k][i];
       if constexpr (NORM) st16(nout + rbase + (size_t)v * 16, pack8<DT>(n));
       if constexpr (EPI == kEpiFp8) {
-        uint32_t w0 = 0, w1 = 0;
+        float t[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w0 |= e4m3_encode(div_rn(n[i], sc, inv_sc)) << (8 * i);
-          w1 |= e4m3_encode(div_rn(n[4 + i], sc, inv_sc)) << (8 * i);
-        }
+        for (int i = 0; i < 8; ++i) t[i] = div_rn(n[i], sc, inv_sc);
         uint2 o;
-        o.x = w0;
-        o.y = w1;
+        o.x = e4m3x4(t[0], t[1], t[2], t[3]);
+        o.y = e4m3x4(t[4], t[5], t[6], t[7]);
         *reinterpret_cast<uint2*>(p.q + (size_t)row * p.hidden + (size_t)v * 8) = o;
       } else {
         float am = 0.0f;
@@ -209,12 +206,13 @@ __global__ void __launch_bounds__(1024) tail_kernel(TailParams p) {
         for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(n[i]));
         am = fmaxf(am, __shfl_xor(am, 1, 64));  // the other half of the 16-element block
         const float s_b = sc * div_rn(am, 6.0f, kInv6);
-        const uint32_t sfc = e4m3_encode(s_b);
+        const uint32_t sfc = e4m3_pos(s_b);
         const float S = e4m3_value_pos(sfc);
         const float mult = S > 0.0f ? sc / S : 0.0f;
-        uint32_t w = 0;
+        float t[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w |= e2m1_encode(n[i] * mult) << (4 * i);
+        for (int i = 0; i < 8; ++i) t[i] = n[i] * mult;
+        const uint32_t w = e2m1x8(t);
         *reinterpret_cast<uint32_t*>(p.q + (size_t)row * (p.hidden / 2) + (size_t)v * 4) = w;
         if ((lane & 1) == 0) p.sf[(size_t)row * (p.hidden / 16) + (v >> 1)] = (uint8_t)sfc;
       }

@@ -105,7 +105,11 @@ def test_row_ops_validation(L, op):
     assert op(L) == OK                                   # tokens == 0: no-op, no HIP call
     assert op(L, norm=None) == OK                        # norm_out is optional
     for k in ("x", "res", "gamma", "scale", "q"):
-        assert op(L, **{k: None}) == NULL, k
+        assert op(L, tokens=4, **{k: None}) == NULL, k
+    for k in ("x", "res", "q", "norm"):                  # empty tensors carry NULL pointers
+        assert op(L, tokens=0, **{k: None}) == OK, k
+    for k in ("gamma", "scale"):
+        assert op(L, tokens=0, **{k: None}) == NULL, k
     assert op(L, dtype=2) == DTYPE
     assert op(L, dtype=-1) == DTYPE
     for h in (0, -16, 24, 100, 8):
@@ -132,13 +136,16 @@ def test_row_ops_alias_rules(L):
     assert fp8(L, tokens=t, hidden=h, scale=addr(4, 4)) == ALIAS     # scale inside q
     assert fp8(L, tokens=0, hidden=h, gamma=addr(0)) == OK           # read-only inputs may overlap
     assert nvfp4(L, tokens=t, hidden=h, sf=addr(4, 16)) == ALIAS     # sf inside q
-    assert nvfp4(L, sf=None) == NULL
+    assert nvfp4(L, tokens=4, sf=None) == NULL
+    assert nvfp4(L, tokens=0, sf=None) == OK
 
 
 def test_qk_validation(L):
     assert qk(L) == OK
     for k in ("qkv", "pos", "cs", "scale", "out"):
-        assert qk(L, **{k: None}) == NULL, k
+        assert qk(L, tokens=4, **{k: None}) == NULL, k
+    for k in ("qkv", "pos", "out"):
+        assert qk(L, tokens=0, **{k: None}) == OK, k
     assert qk(L, gq=None) == NULL
     assert qk(L, gq=None, nq=0) == OK                   # gamma_q unused without Q heads
     assert qk(L, gk=None, nk=0) == OK
