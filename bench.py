@@ -202,6 +202,27 @@ def cpu_baseline(k: int, scalars: dict, budget_s: float = 10.0) -> dict:
             "us_per_call_equiv": round(el / passes * (inp.tokens / rows) * 1e6, 1)}
 
 
+def copy_calibration(steps: int, warmup: int, nbytes: int = 1 << 30) -> dict:
+    """A plain 1 GiB device-to-device copy (HIP's copy kernel), read + write
+    bytes over event time: the streaming rate this GPU reaches in practice."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    return {"copy_bytes": nbytes, "us_per_copy": round(us, 2),
+            "gbs_read_plus_write": round(2 * nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(2 * nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, 4)}
+
+
 def load_traffic(k: int, bytes_per_call: int):
     """HBM bytes per call measured by rocprofv3 counters (FETCH_SIZE +
     WRITE_SIZE), if they were taken on the current kernel sources."""
@@ -224,6 +245,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-sweep", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain device-to-device copy of 1 GiB instead (practical "
+                    "streaming ceiling; the same copy calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused tail is row-parallel and this build runs "
@@ -237,6 +261,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     A.lib()
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(args.steps, args.warmup)), flush=True)
+        return
     with open(SCALARS) as fh:
         scalars = json.load(fh)
 

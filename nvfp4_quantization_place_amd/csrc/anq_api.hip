@@ -85,6 +85,7 @@ extern "C" int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* 
   p.hidden = (int32_t)hidden;
   p.vec = (int32_t)(hidden / 8);
   const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
+  p.rows_per_group = t.rows;
   return launch_status(anq::launch_tail(dtype, anq::kEpiFp8, norm_out != nullptr, p, t,
                                         static_cast<hipStream_t>(stream)));
 }
@@ -117,6 +118,7 @@ extern "C" int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void
   p.hidden = (int32_t)hidden;
   p.vec = (int32_t)(hidden / 8);
   const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
+  p.rows_per_group = t.rows;
   return launch_status(anq::launch_tail(dtype, anq::kEpiNvfp4, norm_out != nullptr, p, t,
                                         static_cast<hipStream_t>(stream)));
 }

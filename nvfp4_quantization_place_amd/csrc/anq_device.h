@@ -27,6 +27,16 @@ __device__ __forceinline__ void st16(void* p, const U4& v) {
   *reinterpret_cast<U4*>(p) = v;
 }
 
+// A pointer known to be the same in every lane, moved to scalar registers so
+// that loads and stores address it as SGPR base + 32-bit lane offset.
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------- T <-> f32
 
 template <int DT>

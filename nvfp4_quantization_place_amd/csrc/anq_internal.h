@@ -20,16 +20,19 @@ struct TailParams {
   int64_t tokens;
   int32_t hidden;
   int32_t vec;         // hidden / 8: 16-byte vectors per row
+  int32_t rows_per_group;  // consecutive rows each lane group processes
 };
 
 // How a row is spread over lanes: `group` lanes of one wavefront per row
-// (16, 32 or 64; the workgroup holds 256 / group rows), or group == 0 for one
-// row per workgroup of `block` lanes. Each lane owns vectors lane + k*lanes,
-// k < vec_per_lane.
+// (16, 32 or 64; the workgroup holds 256 / group lane groups), or group == 0
+// for one row at a time per workgroup of `block` lanes. Each lane owns vectors
+// lane + k*lanes, k < vec_per_lane. Each lane group walks `rows` consecutive
+// rows, loading the next while it finishes the current one.
 struct Tiling {
   int group;
   int vec_per_lane;
   int block;
+  int rows;
   int64_t grid;
 };
 

@@ -22,6 +22,9 @@
 //    again as a double-double, which settles the rounding of the exact sum.
 //  * NVFP4: a 16-element block is two adjacent vectors held by lanes 2j and
 //    2j+1; their amax meet through one lane swap.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "anq_device.h"
@@ -36,7 +39,7 @@ namespace anq {
 // partial sums in every lane).
 template <int G>
 struct GroupReduce {
-  __device__ __forceinline__ double sum(double v) const {
+  __device__ __forceinline__ double sum(double v, int) const {
 #pragma unroll
     for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
     return v;
@@ -51,147 +54,207 @@ struct GroupReduce {
   }
 };
 
-// One row per workgroup: wavefront butterflies, then every lane adds the
-// wavefront partials from LDS in wavefront order.
+// One row per workgroup: a butterfly inside each wavefront, wavefront partials
+// through LDS, then every 16-lane group of every wavefront reads the partials
+// one per lane (zeros past the last wavefront) and runs the same butterfly over
+// them. All groups add the same values in the same order, so all lanes of the
+// workgroup hold identical bits. Partials of consecutive rows go to
+// alternating LDS slots, so one barrier per row suffices: the slot a row reads
+// is next written two rows later, after the following row's barrier.
 struct BlockReduce {
-  double* lds;  // >= 2 * 16 doubles
-  __device__ __forceinline__ double sum(double v) const {
-    v = GroupReduce<64>().sum(v);
-    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    if ((threadIdx.x & 63) == 0) lds[w] = v;
+  double* lds;  // 2 x 16 float64 partials, then 16 double-double partials
+  __device__ __forceinline__ double sum(double v, int parity) const {
+    v = GroupReduce<64>().sum(v, 0);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    double* slot = lds + 16 * parity;
+    if (lane == 0) slot[w] = v;
     __syncthreads();
-    double s = 0.0;
-    for (int i = 0; i < nw; ++i) s += lds[i];
-    __syncthreads();
-    return s;
+    const int i = lane & 15;
+    return GroupReduce<16>().sum(i < nw ? slot[i] : 0.0, 0);
   }
   __device__ __forceinline__ void sum_dd(double& hi, double& lo) const {
     GroupReduce<64>().sum_dd(hi, lo);
-    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-      lds[2 * w] = hi;
-      lds[2 * w + 1] = lo;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    double* slot = lds + 32;
+    __syncthreads();  // a previous double-double reduction may still be reading
+    if (lane == 0) {
+      slot[2 * w] = hi;
+      slot[2 * w + 1] = lo;
     }
     __syncthreads();
-    double h = 0.0, l = 0.0;
-    for (int i = 0; i < nw; ++i) dd_add(h, l, lds[2 * i], lds[2 * i + 1]);
-    __syncthreads();
-    hi = h;
-    lo = l;
+    const int i = lane & 15;
+    hi = i < nw ? slot[2 * i] : 0.0;
+    lo = i < nw ? slot[2 * i + 1] : 0.0;
+    GroupReduce<16>().sum_dd(hi, lo);
   }
 };
 
 // ---------------------------------------------------------------- the kernel
 
-// Rounded-once binary32 sum of squares of the row's h values (see above).
-template <int K, class Red>
-__device__ __forceinline__ float row_sum_squares(const float (&h)[K][8], double acc,
-                                                 int32_t width, const Red& red) {
-  const double S = red.sum(acc);
-  float ss = (float)S;
-  // float64 error of a sum of `width` non-negative terms is below width * 2^-53 * S
-  if (near_f32_midpoint(S, ss, S * (double)width * 0x1p-52)) {  // uniform over the row
-    double hi = 0.0, lo = 0.0;
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double d = (double)h[k][i];
-        dd_add(hi, lo, d * d, 0.0);
-      }
-    red.sum_dd(hi, lo);
-    ss = dd_to_f32(hi, lo);
+// Start of a row in a tensor. With one row per workgroup the row is the same in
+// every lane, and the pointer goes to scalar registers (SGPR base + 32-bit lane
+// offsets instead of a 64-bit address per lane).
+template <int G, class T>
+__device__ __forceinline__ T* row_ptr(T* base, size_t off) {
+  if constexpr (G == 0) return uniform_ptr(base + off);
+  return base + off;
+}
+
+// Rounded-once binary32 sum of squares of a row (see above). The rare
+// double-double pass re-reads the lane's own h values from the residual row it
+// has just stored (a thread always observes its own earlier stores), one
+// element at a time, so it adds no registers to the common path.
+template <int DT, int K, class Red>
+__device__ __forceinline__ float row_sum_squares_dd(const uint8_t* res_row, const uint32_t* voff,
+                                                 const bool* vok, const Red& red) {
+  double hi = 0.0, lo = 0.0;
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    if (!vok[k]) continue;
+#pragma unroll 1
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t b = *reinterpret_cast<const volatile uint16_t*>(res_row + voff[k] + 2 * i);
+      float f, unused;
+      unpack2<DT>((uint32_t)b, f, unused);
+      const double d = (double)f;
+      dd_add(hi, lo, d * d, 0.0);
+    }
   }
+  red.sum_dd(hi, lo);
+  return dd_to_f32(hi, lo);
+}
+
+template <int DT, int K, class Red>
+__device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int parity,
+                                                 const uint8_t* res_row, const uint32_t* voff,
+                                                 const bool* vok, const Red& red) {
+  const double S = red.sum(acc, parity);
+  const float ss = (float)S;
+  // float64 error of a sum of `width` non-negative terms is below width * 2^-53 * S
+  if (near_f32_midpoint(S, ss, S * (double)width * 0x1p-52))  // uniform over the row
+    return row_sum_squares_dd<DT, K>(res_row, voff, vok, red);
   return ss;
 }
 
+// Each lane group (G lanes, or the whole workgroup when G == 0) walks
+// rows_per_group consecutive rows and loads the next row's x and residual
+// before it reduces and stores the current one, so load latency overlaps the
+// previous row's work while the rows in flight across the GPU stay a compact
+// window of the tensor. Loads use clamped indices and are never predicated,
+// so every load of a row is in flight at once; only the stores of vectors past
+// the row end (hidden not a multiple of 8 * lanes) are skipped.
+//
+// Register budget: 7 wavefronts per SIMD (<= 72 VGPRs) for one vector per
+// lane, which then needs no spills; 4 (<= 128) for rows wider than 8192.
 template <int DT, int EPI, bool NORM, int K, int G>
-__global__ void __launch_bounds__(1024) tail_kernel(TailParams p) {
-  __shared__ double lds[32];
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 ? 256 : 1024),
+                               amdgpu_waves_per_eu(K == 1 ? 7 : 4)))
+tail_kernel(TailParams p) {
+  __shared__ double lds[64];
+  __shared__ float mult_tab[128];  // NVFP4: G / value(sf) for every block-scale code
   const int32_t V = p.vec;
   int lane, L;
-  int64_t row, step;
+  int64_t group;
   if constexpr (G > 0) {
     lane = threadIdx.x & (G - 1);
     L = G;
-    const int rpb = blockDim.x / G;
-    row = (int64_t)blockIdx.x * rpb + threadIdx.x / G;
-    step = (int64_t)gridDim.x * rpb;
+    group = (int64_t)blockIdx.x * (blockDim.x / G) + threadIdx.x / G;
   } else {
     lane = threadIdx.x;
     L = blockDim.x;
-    row = blockIdx.x;
-    step = gridDim.x;
+    group = blockIdx.x;
   }
+  int64_t row = group * p.rows_per_group;
+  const int64_t row_end = row + p.rows_per_group < p.tokens ? row + p.rows_per_group : p.tokens;
+  const int64_t last = p.tokens - 1;
 
   const uint8_t* x = static_cast<const uint8_t*>(p.x);
   uint8_t* res = static_cast<uint8_t*>(p.residual);
   const uint8_t* gam = static_cast<const uint8_t*>(p.gamma);
   uint8_t* nout = static_cast<uint8_t*>(p.norm_out);
+  const size_t row_bytes = (size_t)p.hidden * 2;
 
-  float g[K][8];
+  uint32_t voff[K];  // byte offset of each owned vector within a row (clamped)
+  bool vok[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int v = lane + k * L;
-    if (v < V) {
-      unpack8<DT>(ld16(gam + (size_t)v * 16), g[k]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) g[k][i] = 0.0f;
-    }
+    vok[k] = v < V;
+    voff[k] = (uint32_t)(vok[k] ? v : V - 1) * 16u;
   }
 
-  const float sc = *p.scale;   // FP8: s, NVFP4: G
+  U4 gv[K], xv[K], rv[K];
+  {
+    const size_t rb = (size_t)(row < last ? row : last) * row_bytes;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      gv[k] = ld16(gam + voff[k]);
+      xv[k] = ld16(x + rb + voff[k]);
+      rv[k] = ld16(res + rb + voff[k]);
+    }
+  }
+  const float sc = *p.scale;       // FP8: s, NVFP4: G
   const float inv_sc = 1.0f / sc;  // RN(1/s), correctly rounded division
   constexpr float kInv6 = 0x1.555556p-3f;  // RN(1/6)
+  if constexpr (EPI == kEpiNvfp4) {
+    for (int c = threadIdx.x; c < 128; c += blockDim.x) {
+      const float S = c < 127 ? e4m3_value_pos((uint32_t)c) : 0.0f;
+      mult_tab[c] = S > 0.0f ? sc / S : 0.0f;
+    }
+    __syncthreads();
+  }
+  // gamma stays packed in registers (4 per vector) and is unpacked per row:
+  // one extra conversion per element buys the registers that keep the
+  // two-vector variants at 6 wavefronts per SIMD without spilling.
 
   typename std::conditional<(G > 0), GroupReduce<(G > 0 ? G : 64)>, BlockReduce>::type red;
   if constexpr (G == 0) red.lds = lds;
 
-  for (; row < p.tokens; row += step) {
-    const size_t rbase = (size_t)row * (size_t)p.hidden * 2;  // byte offset of the row in T
-    U4 xv[K], rv[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int v = lane + k * L;
-      if (v < V) {
-        xv[k] = ld16(x + rbase + (size_t)v * 16);
-        rv[k] = ld16(res + rbase + (size_t)v * 16);
-      }
-    }
+  int parity = 0;
+  for (; row < row_end; ++row, parity ^= 1) {
+    uint8_t* rrow = row_ptr<G>(res, (size_t)row * row_bytes);
     float h[K][8];
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int v = lane + k * L;
-      if (v < V) {
-        float xf[8], rf[8], s[8];
-        unpack8<DT>(xv[k], xf);
-        unpack8<DT>(rv[k], rf);
+      float xf[8], rf[8], s[8];
+      unpack8<DT>(xv[k], xf);
+      unpack8<DT>(rv[k], rf);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s[i] = xf[i] + rf[i];
-        const U4 hv = pack8<DT>(s);
-        st16(res + rbase + (size_t)v * 16, hv);
-        unpack8<DT>(hv, h[k]);
+      for (int i = 0; i < 8; ++i) s[i] = xf[i] + rf[i];
+      const U4 hv = pack8<DT>(s);
+      if (vok[k]) st16(rrow + voff[k], hv);
+      unpack8<DT>(hv, h[k]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc = __builtin_fma((double)h[k][i], (double)h[k][i], acc);
-      } else {
+      for (int i = 0; i < 8; ++i) {
+        h[k][i] = vok[k] ? h[k][i] : 0.0f;
+        acc = __builtin_fma((double)h[k][i], (double)h[k][i], acc);
+      }
+    }
+    // Prefetch this group's next row into the registers just freed; it lands
+    // while this row is reduced, normalised and stored.
+    if (row + 1 < row_end) {
+      const uint8_t* xn = row_ptr<G>(x, (size_t)(row + 1) * row_bytes);
+      const uint8_t* rn = row_ptr<G>(res, (size_t)(row + 1) * row_bytes);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[k][i] = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        xv[k] = ld16(xn + voff[k]);
+        rv[k] = ld16(rn + voff[k]);
       }
     }
 
-    const float ss = row_sum_squares<K>(h, acc, p.hidden, red);
+    const float ss = row_sum_squares<DT, K>(acc, p.hidden, parity, rrow, voff, vok, red);
     const float r = 1.0f / sqrtf(ss / (float)p.hidden + p.eps);
 
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int v = lane + k * L;
-      if (v >= V) continue;
-      float n[8];
+      float g[8], n[8];
+      unpack8<DT>(gv[k], g);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) n[i] = (h[k][i] * r) * g[k][i];
-      if constexpr (NORM) st16(nout + rbase + (size_t)v * 16, pack8<DT>(n));
+      for (int i = 0; i < 8; ++i) n[i] = (h[k][i] * r) * g[i];
+      if constexpr (NORM) {
+        if (vok[k]) st16(row_ptr<G>(nout, (size_t)row * row_bytes) + voff[k], pack8<DT>(n));
+      }
       if constexpr (EPI == kEpiFp8) {
         float t[8];
 #pragma unroll
@@ -199,7 +262,8 @@ __global__ void __launch_bounds__(1024) tail_kernel(TailParams p) {
         uint2 o;
         o.x = e4m3x4(t[0], t[1], t[2], t[3]);
         o.y = e4m3x4(t[4], t[5], t[6], t[7]);
-        *reinterpret_cast<uint2*>(p.q + (size_t)row * p.hidden + (size_t)v * 8) = o;
+        if (vok[k])
+          *reinterpret_cast<uint2*>(row_ptr<G>(p.q, (size_t)row * p.hidden) + voff[k] / 2) = o;
       } else {
         float am = 0.0f;
 #pragma unroll
@@ -207,14 +271,16 @@ __global__ void __launch_bounds__(1024) tail_kernel(TailParams p) {
         am = fmaxf(am, __shfl_xor(am, 1, 64));  // the other half of the 16-element block
         const float s_b = sc * div_rn(am, 6.0f, kInv6);
         const uint32_t sfc = e4m3_pos(s_b);
-        const float S = e4m3_value_pos(sfc);
-        const float mult = S > 0.0f ? sc / S : 0.0f;
+        const float mult = mult_tab[sfc];
         float t[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) t[i] = n[i] * mult;
         const uint32_t w = e2m1x8(t);
-        *reinterpret_cast<uint32_t*>(p.q + (size_t)row * (p.hidden / 2) + (size_t)v * 4) = w;
-        if ((lane & 1) == 0) p.sf[(size_t)row * (p.hidden / 16) + (v >> 1)] = (uint8_t)sfc;
+        if (vok[k]) {
+          *reinterpret_cast<uint32_t*>(row_ptr<G>(p.q, (size_t)row * (p.hidden / 2)) + voff[k] / 4) = w;
+          if ((lane & 1) == 0)
+            row_ptr<G>(p.sf, (size_t)row * (p.hidden / 16))[voff[k] / 32] = (uint8_t)sfc;
+        }
       }
     }
   }
@@ -222,23 +288,58 @@ __global__ void __launch_bounds__(1024) tail_kernel(TailParams p) {
 
 // ---------------------------------------------------------------- dispatch
 
+namespace {
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+}  // namespace
+
+// Tiling by row width (vec = hidden / 8 vectors of 16 bytes), one vector per
+// lane wherever a row fits in a workgroup:
+//   vec <= 16, 32, 64 : 16, 32, 64 lanes of a wavefront per row
+//   vec <= 1024       : a workgroup of vec lanes (rounded up to 64) per row
+//   larger            : a workgroup of up to 1024 lanes, 2, 4 or 8 vectors each
+// and rows per lane group chosen so that a small grid still fills the GPU.
+// ANQ_TAIL_TILING="G:K" (G in {0,16,32,64}) and ANQ_ROWS_PER_GROUP override
+// the choice, for sweeps; every choice gives identical results.
 Tiling pick_tail_tiling(int32_t vec, int64_t tokens) {
   Tiling t{};
-  const int64_t kMaxGrid = 1 << 22;
-  if (vec <= 128) {
+  if (vec <= 64) {
     t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
-    t.vec_per_lane = vec <= 64 ? 1 : 2;
-    t.block = 256;
-    const int64_t rpb = 256 / t.group;
-    t.grid = (tokens + rpb - 1) / rpb;
+    t.vec_per_lane = 1;
   } else {
     t.group = 0;
-    t.vec_per_lane = vec <= 2048 ? 2 : (vec <= 4096 ? 4 : 8);
+    t.vec_per_lane = vec <= 1024 ? 1 : (vec <= 2048 ? 2 : (vec <= 4096 ? 4 : 8));
+  }
+  if (const char* o = getenv("ANQ_TAIL_TILING")) {
+    int g = -1, k = -1;
+    if (sscanf(o, "%d:%d", &g, &k) == 2 && (g == 0 || g == 16 || g == 32 || g == 64) &&
+        (k == 1 || k == 2 || k == 4 || k == 8) && (g == 0 ? (vec + k - 1) / k <= 1024 : g * k >= vec) &&
+        (g == 0 || k <= 2)) {
+      t.group = g;
+      t.vec_per_lane = k;
+    }
+  }
+  int64_t groups_per_block;
+  if (t.group > 0) {
+    t.block = 256;
+    groups_per_block = 256 / t.group;
+  } else {
     const int lanes = (vec + t.vec_per_lane - 1) / t.vec_per_lane;
     t.block = (lanes + 63) / 64 * 64;
-    t.grid = tokens;
+    groups_per_block = 1;
   }
-  if (t.grid > kMaxGrid) t.grid = kMaxGrid;
+  // wide rows: two rows per workgroup once there are rows enough to spare, so
+  // the second row's loads overlap the first row's reduction and stores
+  t.rows = (t.group == 0 && t.block >= 512 && tokens >= 4096) ? 2 : 1;
+  const int env_rows = env_int("ANQ_ROWS_PER_GROUP", 0);
+  if (env_rows > 0) t.rows = env_rows;
+  const int64_t kMaxGrid = 0x7FFFFFFF;
+  while ((tokens + groups_per_block * t.rows - 1) / (groups_per_block * t.rows) > kMaxGrid) t.rows *= 2;
+  t.grid = (tokens + groups_per_block * t.rows - 1) / (groups_per_block * t.rows);
   return t;
 }
 

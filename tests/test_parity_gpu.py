@@ -208,3 +208,28 @@ def test_qk_grid(head_dim, heads, dtype):
     cs = code_stats(got, ref, e4m3_rank)
     check_codes(cs, "qk")
     assert cs["bit_exact"], cs
+
+
+# ----------------------------------------------------- every tiling agrees --
+
+@pytest.mark.parametrize("hidden,tilings", [
+    (128, ["16:1", "32:1", "64:1", "0:1", "0:2"]),
+    (1024, ["64:2", "0:1", "0:2", "0:4", "0:8"]),
+    (512, ["64:1", "0:1", "0:2"]),
+    (1040, ["0:1", "0:2", "0:4"]),
+    (7168, ["0:1", "0:2", "0:4", "0:8"]),
+])
+@pytest.mark.parametrize("op", ["fp8", "nvfp4"])
+def test_every_tiling_matches_the_oracle(hidden, tilings, op, monkeypatch):
+    """The lane mapping (lanes per row, vectors per lane, rows per lane group)
+    changes only the order of float64 partial sums, never a result bit."""
+    inp = W.make_tail(900 + hidden, op, "bf16", 67, hidden, norm_out=True,
+                      scale=0.03 if op == "fp8" else None, outliers=0.002)
+    scale = _scale(inp)
+    ref = oracle_tail(inp, scale)
+    for t in tilings:
+        for rows in ("", "1", "3", "64"):
+            monkeypatch.setenv("ANQ_TAIL_TILING", t)
+            monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
+            got = gpu_tail(inp, scale)
+            compare_tail(inp, scale, got, ref)
