@@ -120,17 +120,19 @@ class Workload:
                                       norm=self.norm[j] if self.norm else None)
 
 
-def time_workload(w: Workload, steps: int, warmup: int) -> dict:
+def time_workload(w: Workload, steps: int, warmup: int, eager: bool = True) -> dict:
     import torch
     for i in range(warmup):
         w.call(i)
     torch.cuda.synchronize()
     # eager: host-launched calls, wall clock
-    t0 = time.perf_counter()
-    for i in range(steps):
-        w.call(i)
-    torch.cuda.synchronize()
-    eager_us = (time.perf_counter() - t0) / steps * 1e6
+    eager_us = None
+    if eager:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            w.call(i)
+        torch.cuda.synchronize()
+        eager_us = round((time.perf_counter() - t0) / steps * 1e6, 3)
     # graph of `steps` calls, replayed
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -156,7 +158,7 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     dev_us = ev0.elapsed_time(ev1) * 1e3 / steps
     gbs = w.bytes / (dev_us * 1e-6) / 1e9
     return dict(workload=w.name, io_dtype=w.dtype, bytes_per_call=w.bytes, rotating_sets=w.sets,
-                us_per_call=round(dev_us, 3), eager_us_per_call=round(eager_us, 3),
+                us_per_call=round(dev_us, 3), eager_us_per_call=eager_us,
                 wall_ms_timed=round(wall_s * 1e3, 3), gbs=round(gbs, 1),
                 frac_of_peak=round(gbs / PEAK_GBS, 4))
 
@@ -245,6 +247,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-sweep", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-eager", action="store_true",
+                    help="skip the eager timing (so a kernel trace holds graph launches only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 1 GiB instead (practical "
                     "streaming ceiling; the same copy calibrates the HBM byte counters)")
@@ -271,7 +275,7 @@ def main():
     results = {}
     for k in todo:
         w = Workload(k, scalars, args.steps)
-        r = time_workload(w, args.steps, args.warmup)
+        r = time_workload(w, args.steps, args.warmup, eager=not args.no_eager)
         r["traffic_bytes_per_call"] = load_traffic(k, w.bytes)
         results[k] = r
         print(f"# workload {k} {r['workload']}: {r['us_per_call']} us/call (graph), "

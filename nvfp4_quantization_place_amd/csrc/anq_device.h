@@ -27,14 +27,62 @@ __device__ __forceinline__ void st16(void* p, const U4& v) {
   *reinterpret_cast<U4*>(p) = v;
 }
 
-// A pointer known to be the same in every lane, moved to scalar registers so
-// that loads and stores address it as SGPR base + 32-bit lane offset.
-template <class T>
-__device__ __forceinline__ T* uniform_ptr(T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
+// Row streams of a call much larger than the last-level cache are read once and
+// written once: with NT they carry the non-temporal hint (the `nt` bit of
+// gfx950 global loads and stores), which keeps them from displacing each other
+// in the L2 and the Infinity Cache. Measured on MI355X at 8192 x 7168 and
+// 65536 x 1024, the 16-byte row loads and stores hinted together cut the
+// kernel time by ~10%; either hint alone does little.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ U4 ld16s(const void* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    U4 r;
+    r.w[0] = v.x;
+    r.w[1] = v.y;
+    r.w[2] = v.z;
+    r.w[3] = v.w;
+    return r;
+  }
+  return ld16(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st16s(void* p, const U4& v) {
+  if constexpr (NT) {
+    const u32x4 x = {v.w[0], v.w[1], v.w[2], v.w[3]};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+  } else {
+    st16(p, v);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void st8s(void* p, uint32_t lo, uint32_t hi) {
+  const u32x2 x = {lo, hi};
+  if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(p));
+  else *reinterpret_cast<u32x2*>(p) = x;
+}
+template <bool NT>
+__device__ __forceinline__ void st4s(void* p, uint32_t v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+  else *reinterpret_cast<uint32_t*>(p) = v;
+}
+template <bool NT>
+__device__ __forceinline__ void st1s(void* p, uint8_t v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<uint8_t*>(p));
+  else *reinterpret_cast<uint8_t*>(p) = v;
+}
+
+// A 64-bit value known to be the same in every lane, moved to scalar
+// registers. Used for row offsets so that a global pointer plus the offset
+// stays a global pointer (no flat addressing) and is addressed as SGPR base +
+// 32-bit lane offset.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // ---------------------------------------------------------------- T <-> f32
@@ -141,6 +189,48 @@ __device__ __forceinline__ float div_rn(float a, float b, float y) {
   return __builtin_copysignf(q1, q0);
 }
 
+// ------------------------------------------------------ cross-lane sums
+
+// DPP lane moves inside a 16-lane row (VALU, no LDS round trip):
+//   0xB1 quad_perm [1,0,3,2] (lane ^ 1), 0x4E quad_perm [2,3,0,1] (lane ^ 2),
+//   0x141 row_half_mirror (lane i <-> 7 - i within 8), 0x140 row_mirror (i <-> 15 - i).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+// Sum over aligned groups of W lanes (W a power of two, 2..64). Every lane of a
+// group ends with the same bits: each step adds a value and its partner's, and
+// IEEE addition commutes; groups of 32 and 64 combine their 16-lane rows read
+// with readlane in one fixed order. A group's lanes must all be active.
+template <int W>
+__device__ __forceinline__ double lanes_sum(double v) {
+  if constexpr (W >= 2) v += dpp_f64<0xB1>(v);
+  if constexpr (W >= 4) v += dpp_f64<0x4E>(v);
+  if constexpr (W >= 8) v += dpp_f64<0x141>(v);
+  if constexpr (W >= 16) v += dpp_f64<0x140>(v);
+  if constexpr (W == 32) {
+    const double lo = readlane_f64(v, 0) + readlane_f64(v, 16);
+    const double hi = readlane_f64(v, 32) + readlane_f64(v, 48);
+    v = (__lane_id() < 32) ? lo : hi;
+  } else if constexpr (W == 64) {
+    v = (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+  }
+  return v;
+}
+
 // ------------------------------------------------- exact sum of squares
 
 // a + b = s + e exactly (Knuth's TwoSum; no contraction allowed).
@@ -156,6 +246,40 @@ __device__ __forceinline__ void dd_add(double& hi, double& lo, double bh, double
   e += lo + bl;
   hi = s + e;
   lo = e - (hi - s);
+}
+
+// Double-double sum over aligned groups of W lanes, same pattern as lanes_sum.
+template <int CTRL>
+__device__ __forceinline__ void dd_step(double& hi, double& lo) {
+  const double oh = dpp_f64<CTRL>(hi), ol = dpp_f64<CTRL>(lo);
+  dd_add(hi, lo, oh, ol);
+}
+template <int W>
+__device__ __forceinline__ void lanes_sum_dd(double& hi, double& lo) {
+  if constexpr (W >= 2) dd_step<0xB1>(hi, lo);
+  if constexpr (W >= 4) dd_step<0x4E>(hi, lo);
+  if constexpr (W >= 8) dd_step<0x141>(hi, lo);
+  if constexpr (W >= 16) dd_step<0x140>(hi, lo);
+  if constexpr (W >= 32) {
+    double r[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      r[q][0] = readlane_f64(hi, 16 * q);
+      r[q][1] = readlane_f64(lo, 16 * q);
+    }
+    double h0 = r[0][0], l0 = r[0][1], h1 = r[2][0], l1 = r[2][1];
+    dd_add(h0, l0, r[1][0], r[1][1]);
+    dd_add(h1, l1, r[3][0], r[3][1]);
+    if constexpr (W == 64) {
+      dd_add(h0, l0, h1, l1);
+      hi = h0;
+      lo = l0;
+    } else {
+      const bool low = __lane_id() < 32;
+      hi = low ? h0 : h1;
+      lo = low ? l0 : l1;
+    }
+  }
 }
 
 __device__ __forceinline__ float f32_next_up(float f) {

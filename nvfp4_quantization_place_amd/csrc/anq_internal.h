@@ -33,6 +33,7 @@ struct Tiling {
   int vec_per_lane;
   int block;
   int rows;
+  bool stream;  // non-temporal loads and stores of the row streams
   int64_t grid;
 };
 

@@ -6,32 +6,17 @@
 // wavefront. Lane j holds elements [8j, 8j+8) of the first half of the head and
 // [D/2 + 8j, D/2 + 8j + 8) of the second half, so every NeoX rotation pair
 // (k, k + D/2) lives in one lane and each lane issues two 16-byte loads and
-// two 8-byte stores. The head's sum of squares meets through a xor butterfly
+// two 8-byte stores. The head's sum of squares meets through a DPP butterfly
 // over the D/16 lanes. cos|sin rows are read per (token, head) and come from
 // cache after the first head of a token.
+#include <stdlib.h>
+
 #include "anq_device.h"
 #include "anq_internal.h"
 
 namespace anq {
 
-template <int LPH>
-__device__ __forceinline__ double head_sum(double v) {
-#pragma unroll
-  for (int m = 1; m < LPH; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-template <int LPH>
-__device__ __forceinline__ void head_sum_dd(double& hi, double& lo) {
-#pragma unroll
-  for (int m = 1; m < LPH; m <<= 1) {
-    const double oh = __shfl_xor(hi, m, 64);
-    const double ol = __shfl_xor(lo, m, 64);
-    dd_add(hi, lo, oh, ol);
-  }
-}
-
-template <int DT, int LPH>
+template <int DT, int LPH, bool NT>
 __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
   constexpr int D = LPH * 16;
   constexpr int HALF = D / 2;
@@ -50,8 +35,8 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
     const size_t e0 = (size_t)t * heads * D + (size_t)hd * D;  // first element of the head
     const size_t ea = e0 + 8 * lane, eb = e0 + HALF + 8 * lane;
     float a[8], b[8], oa[8], ob[8];
-    unpack8<DT>(ld16(qkv + ea * 2), a);
-    unpack8<DT>(ld16(qkv + eb * 2), b);
+    unpack8<DT>(ld16s<NT>(qkv + ea * 2), a);
+    unpack8<DT>(ld16s<NT>(qkv + eb * 2), b);
     if (hd < qk_heads) {  // uniform over the head's lanes
       const uint8_t* gp = static_cast<const uint8_t*>(hd < p.nq ? p.gamma_q : p.gamma_k);
       float ga[8], gb[8];
@@ -63,7 +48,7 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
         acc = __builtin_fma((double)a[i], (double)a[i], acc);
         acc = __builtin_fma((double)b[i], (double)b[i], acc);
       }
-      const double S = head_sum<LPH>(acc);
+      const double S = lanes_sum<LPH>(acc);
       float ss = (float)S;
       if (near_f32_midpoint(S, ss, S * (double)D * 0x1p-52)) {
         double hi = 0.0, lo = 0.0;
@@ -72,7 +57,7 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
           dd_add(hi, lo, (double)a[i] * (double)a[i], 0.0);
           dd_add(hi, lo, (double)b[i] * (double)b[i], 0.0);
         }
-        head_sum_dd<LPH>(hi, lo);
+        lanes_sum_dd<LPH>(hi, lo);
         ss = dd_to_f32(hi, lo);
       }
       const float r = 1.0f / sqrtf(ss / (float)D + p.eps);
@@ -103,27 +88,22 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
       oa[i] = div_rn(oa[i], sc, inv_sc);
       ob[i] = div_rn(ob[i], sc, inv_sc);
     }
-    uint2 qa, qb;
-    qa.x = e4m3x4(oa[0], oa[1], oa[2], oa[3]);
-    qa.y = e4m3x4(oa[4], oa[5], oa[6], oa[7]);
-    qb.x = e4m3x4(ob[0], ob[1], ob[2], ob[3]);
-    qb.y = e4m3x4(ob[4], ob[5], ob[6], ob[7]);
-    *reinterpret_cast<uint2*>(p.out + ea) = qa;
-    *reinterpret_cast<uint2*>(p.out + eb) = qb;
+    st8s<NT>(p.out + ea, e4m3x4(oa[0], oa[1], oa[2], oa[3]), e4m3x4(oa[4], oa[5], oa[6], oa[7]));
+    st8s<NT>(p.out + eb, e4m3x4(ob[0], ob[1], ob[2], ob[3]), e4m3x4(ob[4], ob[5], ob[6], ob[7]));
   }
 }
 
-template <int DT>
-static hipError_t launch_qk_dt(const QKParams& p, hipStream_t s) {
+template <int DT, bool NT>
+static hipError_t launch_qk_nt(const QKParams& p, hipStream_t s) {
   void* args[] = {const_cast<QKParams*>(&p)};
   const void* fn = nullptr;
-  int lph = p.head_dim / 16;
+  const int lph = p.head_dim / 16;
   switch (lph) {
-    case 2: fn = (const void*)&qk_kernel<DT, 2>; break;
-    case 4: fn = (const void*)&qk_kernel<DT, 4>; break;
-    case 8: fn = (const void*)&qk_kernel<DT, 8>; break;
-    case 16: fn = (const void*)&qk_kernel<DT, 16>; break;
-    case 32: fn = (const void*)&qk_kernel<DT, 32>; break;
+    case 2: fn = (const void*)&qk_kernel<DT, 2, NT>; break;
+    case 4: fn = (const void*)&qk_kernel<DT, 4, NT>; break;
+    case 8: fn = (const void*)&qk_kernel<DT, 8, NT>; break;
+    case 16: fn = (const void*)&qk_kernel<DT, 16, NT>; break;
+    case 32: fn = (const void*)&qk_kernel<DT, 32, NT>; break;
     default: return hipErrorInvalidConfiguration;
   }
   const int block = 256;
@@ -131,6 +111,16 @@ static hipError_t launch_qk_dt(const QKParams& p, hipStream_t s) {
   int64_t grid = (p.pairs + gpb - 1) / gpb;
   if (grid > (1 << 22)) grid = 1 << 22;
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(block), args, 0, s);
+}
+
+// Streaming hints (see ld16s) once qkv alone is >= 32 MiB; ANQ_STREAM=0/1 overrides.
+template <int DT>
+static hipError_t launch_qk_dt(const QKParams& p, hipStream_t s) {
+  bool stream = p.pairs * (int64_t)p.head_dim * 2 >= ((int64_t)32 << 20);
+  if (const char* e = getenv("ANQ_STREAM")) {
+    if (*e) stream = atoi(e) != 0;
+  }
+  return stream ? launch_qk_nt<DT, true>(p, s) : launch_qk_nt<DT, false>(p, s);
 }
 
 hipError_t launch_qk(int dtype, const QKParams& p, hipStream_t s) {

@@ -34,24 +34,11 @@ namespace anq {
 
 // ---------------------------------------------------------------- reducers
 
-// G lanes of one wavefront, G in {16, 32, 64}: xor butterfly. Every lane ends
-// with the same bits (IEEE addition commutes, and each step pairs the same
-// partial sums in every lane).
+// G lanes of one wavefront, G in {16, 32, 64}: DPP butterfly (lanes_sum).
 template <int G>
 struct GroupReduce {
-  __device__ __forceinline__ double sum(double v, int) const {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
-    return v;
-  }
-  __device__ __forceinline__ void sum_dd(double& hi, double& lo) const {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) {
-      const double oh = __shfl_xor(hi, m, 64);
-      const double ol = __shfl_xor(lo, m, 64);
-      dd_add(hi, lo, oh, ol);
-    }
-  }
+  __device__ __forceinline__ double sum(double v, int) const { return lanes_sum<G>(v); }
+  __device__ __forceinline__ void sum_dd(double& hi, double& lo) const { lanes_sum_dd<G>(hi, lo); }
 };
 
 // One row per workgroup: a butterfly inside each wavefront, wavefront partials
@@ -92,11 +79,11 @@ struct BlockReduce {
 // ---------------------------------------------------------------- the kernel
 
 // Start of a row in a tensor. With one row per workgroup the row is the same in
-// every lane, and the pointer goes to scalar registers (SGPR base + 32-bit lane
+// every lane, and its offset goes to scalar registers (SGPR base + 32-bit lane
 // offsets instead of a 64-bit address per lane).
 template <int G, class T>
 __device__ __forceinline__ T* row_ptr(T* base, size_t off) {
-  if constexpr (G == 0) return uniform_ptr(base + off);
+  if constexpr (G == 0) return base + uniform_u64(off);
   return base + off;
 }
 
@@ -146,7 +133,7 @@ __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int 
 //
 // Register budget: 7 wavefronts per SIMD (<= 72 VGPRs) for one vector per
 // lane, which then needs no spills; 4 (<= 128) for rows wider than 8192.
-template <int DT, int EPI, bool NORM, int K, int G>
+template <int DT, int EPI, bool NORM, int K, int G, bool NT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 ? 256 : 1024),
                                amdgpu_waves_per_eu(K == 1 ? 7 : 4)))
 tail_kernel(TailParams p) {
@@ -189,8 +176,8 @@ tail_kernel(TailParams p) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       gv[k] = ld16(gam + voff[k]);
-      xv[k] = ld16(x + rb + voff[k]);
-      rv[k] = ld16(res + rb + voff[k]);
+      xv[k] = ld16s<NT>(x + rb + voff[k]);
+      rv[k] = ld16s<NT>(res + rb + voff[k]);
     }
   }
   const float sc = *p.scale;       // FP8: s, NVFP4: G
@@ -223,13 +210,12 @@ tail_kernel(TailParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) s[i] = xf[i] + rf[i];
       const U4 hv = pack8<DT>(s);
-      if (vok[k]) st16(rrow + voff[k], hv);
+      if (vok[k]) st16s<NT>(rrow + voff[k], hv);
       unpack8<DT>(hv, h[k]);
+      double a = 0.0;  // vectors past the row end hold a clamped copy: not counted
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        h[k][i] = vok[k] ? h[k][i] : 0.0f;
-        acc = __builtin_fma((double)h[k][i], (double)h[k][i], acc);
-      }
+      for (int i = 0; i < 8; ++i) a = __builtin_fma((double)h[k][i], (double)h[k][i], a);
+      acc += vok[k] ? a : 0.0;
     }
     // Prefetch this group's next row into the registers just freed; it lands
     // while this row is reduced, normalised and stored.
@@ -238,14 +224,17 @@ tail_kernel(TailParams p) {
       const uint8_t* rn = row_ptr<G>(res, (size_t)(row + 1) * row_bytes);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        xv[k] = ld16(xn + voff[k]);
-        rv[k] = ld16(rn + voff[k]);
+        xv[k] = ld16s<NT>(xn + voff[k]);
+        rv[k] = ld16s<NT>(rn + voff[k]);
       }
     }
 
     const float ss = row_sum_squares<DT, K>(acc, p.hidden, parity, rrow, voff, vok, red);
     const float r = 1.0f / sqrtf(ss / (float)p.hidden + p.eps);
 
+    // Codes and block scales are stored without the streaming hint: their 8-,
+    // 4- and 1-byte stores only fill whole lines once merged in the L2, and
+    // hinting them measured ~5% slower on MI355X.
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       float g[8], n[8];
@@ -253,22 +242,20 @@ tail_kernel(TailParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) n[i] = (h[k][i] * r) * g[i];
       if constexpr (NORM) {
-        if (vok[k]) st16(row_ptr<G>(nout, (size_t)row * row_bytes) + voff[k], pack8<DT>(n));
+        if (vok[k]) st16s<NT>(row_ptr<G>(nout, (size_t)row * row_bytes) + voff[k], pack8<DT>(n));
       }
       if constexpr (EPI == kEpiFp8) {
         float t[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) t[i] = div_rn(n[i], sc, inv_sc);
-        uint2 o;
-        o.x = e4m3x4(t[0], t[1], t[2], t[3]);
-        o.y = e4m3x4(t[4], t[5], t[6], t[7]);
-        if (vok[k])
-          *reinterpret_cast<uint2*>(row_ptr<G>(p.q, (size_t)row * p.hidden) + voff[k] / 2) = o;
+        const uint32_t lo = e4m3x4(t[0], t[1], t[2], t[3]);
+        const uint32_t hi = e4m3x4(t[4], t[5], t[6], t[7]);
+        if (vok[k]) st8s<false>(row_ptr<G>(p.q, (size_t)row * p.hidden) + voff[k] / 2, lo, hi);
       } else {
         float am = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(n[i]));
-        am = fmaxf(am, __shfl_xor(am, 1, 64));  // the other half of the 16-element block
+        am = fmaxf(am, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(am))));  // other half of the block
         const float s_b = sc * div_rn(am, 6.0f, kInv6);
         const uint32_t sfc = e4m3_pos(s_b);
         const float mult = mult_tab[sfc];
@@ -277,9 +264,9 @@ tail_kernel(TailParams p) {
         for (int i = 0; i < 8; ++i) t[i] = n[i] * mult;
         const uint32_t w = e2m1x8(t);
         if (vok[k]) {
-          *reinterpret_cast<uint32_t*>(row_ptr<G>(p.q, (size_t)row * (p.hidden / 2)) + voff[k] / 4) = w;
+          st4s<false>(row_ptr<G>(p.q, (size_t)row * (p.hidden / 2)) + voff[k] / 4, w);
           if ((lane & 1) == 0)
-            row_ptr<G>(p.sf, (size_t)row * (p.hidden / 16))[voff[k] / 32] = (uint8_t)sfc;
+            st1s<false>(row_ptr<G>(p.sf, (size_t)row * (p.hidden / 16)) + voff[k] / 32, (uint8_t)sfc);
         }
       }
     }
@@ -303,8 +290,8 @@ int env_int(const char* name, int dflt) {
 //   vec <= 1024       : a workgroup of vec lanes (rounded up to 64) per row
 //   larger            : a workgroup of up to 1024 lanes, 2, 4 or 8 vectors each
 // and rows per lane group chosen so that a small grid still fills the GPU.
-// ANQ_TAIL_TILING="G:K" (G in {0,16,32,64}) and ANQ_ROWS_PER_GROUP override
-// the choice, for sweeps; every choice gives identical results.
+// ANQ_TAIL_TILING="G:K" (G in {0,16,32,64}), ANQ_ROWS_PER_GROUP and ANQ_STREAM
+// override the choice, for sweeps; every choice gives identical results.
 Tiling pick_tail_tiling(int32_t vec, int64_t tokens) {
   Tiling t{};
   if (vec <= 64) {
@@ -337,26 +324,36 @@ Tiling pick_tail_tiling(int32_t vec, int64_t tokens) {
   t.rows = (t.group == 0 && t.block >= 512 && tokens >= 4096) ? 2 : 1;
   const int env_rows = env_int("ANQ_ROWS_PER_GROUP", 0);
   if (env_rows > 0) t.rows = env_rows;
+  // streaming hints once the call is large next to the 256 MB last-level cache
+  // (x alone >= 32 MiB, so >= ~128 MiB of traffic); ANQ_STREAM=0/1 overrides
+  t.stream = (int64_t)vec * 16 * tokens >= ((int64_t)32 << 20);
+  const int env_stream = env_int("ANQ_STREAM", -1);
+  if (env_stream >= 0) t.stream = env_stream != 0;
   const int64_t kMaxGrid = 0x7FFFFFFF;
   while ((tokens + groups_per_block * t.rows - 1) / (groups_per_block * t.rows) > kMaxGrid) t.rows *= 2;
   t.grid = (tokens + groups_per_block * t.rows - 1) / (groups_per_block * t.rows);
   return t;
 }
 
-template <int DT, int EPI, bool NORM>
-static hipError_t launch3(const TailParams& p, const Tiling& t, hipStream_t s) {
+template <int DT, int EPI, bool NORM, bool NT>
+static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
   void* args[] = {const_cast<TailParams*>(&p)};
   const void* fn = nullptr;
-  if (t.group == 16) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 16>;
-  else if (t.group == 32) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 32>;
-  else if (t.group == 64 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 64>;
-  else if (t.group == 64 && t.vec_per_lane == 2) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 64>;
-  else if (t.group == 0 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 0>;
-  else if (t.group == 0 && t.vec_per_lane == 2) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 0>;
-  else if (t.group == 0 && t.vec_per_lane == 4) fn = (const void*)&tail_kernel<DT, EPI, NORM, 4, 0>;
-  else if (t.group == 0 && t.vec_per_lane == 8) fn = (const void*)&tail_kernel<DT, EPI, NORM, 8, 0>;
+  if (t.group == 16) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 16, NT>;
+  else if (t.group == 32) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 32, NT>;
+  else if (t.group == 64 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 64, NT>;
+  else if (t.group == 64 && t.vec_per_lane == 2) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 64, NT>;
+  else if (t.group == 0 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 0, NT>;
+  else if (t.group == 0 && t.vec_per_lane == 2) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 0, NT>;
+  else if (t.group == 0 && t.vec_per_lane == 4) fn = (const void*)&tail_kernel<DT, EPI, NORM, 4, 0, NT>;
+  else if (t.group == 0 && t.vec_per_lane == 8) fn = (const void*)&tail_kernel<DT, EPI, NORM, 8, 0, NT>;
   if (!fn) return hipErrorInvalidConfiguration;
   return hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3((unsigned)t.block), args, 0, s);
+}
+
+template <int DT, int EPI, bool NORM>
+static hipError_t launch3(const TailParams& p, const Tiling& t, hipStream_t s) {
+  return t.stream ? launch4<DT, EPI, NORM, true>(p, t, s) : launch4<DT, EPI, NORM, false>(p, t, s);
 }
 
 template <int DT, int EPI>

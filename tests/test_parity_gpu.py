@@ -193,10 +193,12 @@ def test_non_default_stream_and_repeatability():
 
 # ------------------------------------------------------------------ Q/K ----
 
+@pytest.mark.parametrize("stream", ["", "1"])
 @pytest.mark.parametrize("head_dim", [32, 64, 128, 256, 512])
 @pytest.mark.parametrize("heads", [(4, 2, 2), (3, 1, 0), (0, 2, 1), (1, 0, 0)])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_qk_grid(head_dim, heads, dtype):
+def test_qk_grid(head_dim, heads, dtype, stream, monkeypatch):
+    monkeypatch.setenv("ANQ_STREAM", stream)
     nq, nk, nv = heads
     tokens = 29
     rng = np.random.default_rng(head_dim + 10 * nq + nk)
@@ -222,14 +224,16 @@ def test_qk_grid(head_dim, heads, dtype):
 @pytest.mark.parametrize("op", ["fp8", "nvfp4"])
 def test_every_tiling_matches_the_oracle(hidden, tilings, op, monkeypatch):
     """The lane mapping (lanes per row, vectors per lane, rows per lane group)
-    changes only the order of float64 partial sums, never a result bit."""
+    and the streaming hints change only the order of float64 partial sums and
+    cache behaviour, never a result bit."""
     inp = W.make_tail(900 + hidden, op, "bf16", 67, hidden, norm_out=True,
                       scale=0.03 if op == "fp8" else None, outliers=0.002)
     scale = _scale(inp)
     ref = oracle_tail(inp, scale)
     for t in tilings:
-        for rows in ("", "1", "3", "64"):
+        for rows, stream in (("", ""), ("1", "1"), ("3", "0"), ("64", "1")):
             monkeypatch.setenv("ANQ_TAIL_TILING", t)
             monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
+            monkeypatch.setenv("ANQ_STREAM", stream)
             got = gpu_tail(inp, scale)
             compare_tail(inp, scale, got, ref)
