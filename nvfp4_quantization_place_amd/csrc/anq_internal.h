@@ -54,6 +54,7 @@ struct QKParams {
   int64_t tokens;
   int64_t pairs;  // tokens * (nq + nk + nv)
   int32_t nq, nk, nv, head_dim;
+  int32_t waves_per_token;  // set by the launcher
 };
 
 hipError_t launch_qk(int dtype, const QKParams& p, hipStream_t stream);

@@ -2,13 +2,15 @@
 // buffer (SGLang PR #32975 "fused norm + RoPE + uniform fp8 store"; the Q/K
 // RMSNorm and RoPE of TensorRT-LLM PR #17288, Description).
 //
-// gfx950 mapping: a (token, head) pair is one unit of work for D/16 lanes of a
-// wavefront. Lane j holds elements [8j, 8j+8) of the first half of the head and
-// [D/2 + 8j, D/2 + 8j + 8) of the second half, so every NeoX rotation pair
-// (k, k + D/2) lives in one lane and each lane issues two 16-byte loads and
-// two 8-byte stores. The head's sum of squares meets through a DPP butterfly
-// over the D/16 lanes. cos|sin rows are read per (token, head) and come from
-// cache after the first head of a token.
+// gfx950 mapping: one or a few wavefronts per token. 64 lanes form 64/(D/16) head
+// slots of D/16 lanes; lane j of a slot holds elements [8j, 8j+8) of the first
+// half of a head and [D/2 + 8j, D/2 + 8j + 8) of the second half, so every
+// NeoX rotation pair (k, k + D/2) lives in one lane. A wavefront loads the
+// token's cos|sin slice and both gammas once, then walks its share of the
+// token's head groups, loading the next group while it finishes the current
+// one. A head's sum of squares meets through a DPP butterfly over its
+// D/16 lanes. Q and K heads are normalised, rotated and quantised; V heads
+// are only quantised.
 #include <stdlib.h>
 
 #include "anq_device.h"
@@ -20,28 +22,67 @@ template <int DT, int LPH, bool NT>
 __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
   constexpr int D = LPH * 16;
   constexpr int HALF = D / 2;
-  const int lane = threadIdx.x & (LPH - 1);
-  const int gpb = blockDim.x / LPH;
+  constexpr int HPP = 64 / LPH;  // heads per pass of a wavefront
+  const int lane = threadIdx.x & 63;
+  const int j = lane & (LPH - 1);
+  const int slot = lane / LPH;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t t = wave / p.waves_per_token;
+  const int w = (int)(wave - t * p.waves_per_token);
+  if (t >= p.tokens) return;  // the whole wavefront
   const int heads = p.nq + p.nk + p.nv;
   const int qk_heads = p.nq + p.nk;
   const float sc = *p.scale;
   const float inv_sc = 1.0f / sc;
-  const uint8_t* qkv = static_cast<const uint8_t*>(p.qkv);
+  const size_t row_elems = (size_t)heads * D;
+  const uint8_t* row = static_cast<const uint8_t*>(p.qkv) + (size_t)t * row_elems * 2;
+  uint8_t* orow = p.out + (size_t)t * row_elems;
+  const uint32_t oa_off = 8 * j, ob_off = HALF + 8 * j;  // element offsets inside a head
 
-  for (int64_t pair = (int64_t)blockIdx.x * gpb + threadIdx.x / LPH; pair < p.pairs;
-       pair += (int64_t)gridDim.x * gpb) {
-    const int64_t t = pair / heads;
-    const int hd = (int)(pair - t * heads);
-    const size_t e0 = (size_t)t * heads * D + (size_t)hd * D;  // first element of the head
-    const size_t ea = e0 + 8 * lane, eb = e0 + HALF + 8 * lane;
+  // per-token constants: the lane's cos|sin values and gamma slices
+  float c[8], s[8];
+  U4 gqa{}, gqb{}, gka{}, gkb{};
+  if (qk_heads > 0) {
+    const int64_t pos = p.positions[t];
+    const float* cs = p.cos_sin + (size_t)pos * D;
+    const float4 c0 = *reinterpret_cast<const float4*>(cs + oa_off);
+    const float4 c1 = *reinterpret_cast<const float4*>(cs + oa_off + 4);
+    const float4 s0 = *reinterpret_cast<const float4*>(cs + HALF + oa_off);
+    const float4 s1 = *reinterpret_cast<const float4*>(cs + HALF + oa_off + 4);
+    c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
+    c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
+    s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
+    s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
+    if (p.nq > 0) {
+      gqa = ld16(static_cast<const uint8_t*>(p.gamma_q) + oa_off * 2);
+      gqb = ld16(static_cast<const uint8_t*>(p.gamma_q) + ob_off * 2);
+    }
+    if (p.nk > 0) {
+      gka = ld16(static_cast<const uint8_t*>(p.gamma_k) + oa_off * 2);
+      gkb = ld16(static_cast<const uint8_t*>(p.gamma_k) + ob_off * 2);
+    }
+  }
+
+  const int passes = (heads + HPP - 1) / HPP;
+  const int W = p.waves_per_token;  // this wavefront takes passes w, w + W, ...
+  // loads of the first pass (heads past the end re-read the last head; never stored)
+  int hl = w * HPP + slot < heads ? w * HPP + slot : heads - 1;
+  U4 av = ld16s<NT>(row + ((size_t)hl * D + oa_off) * 2);
+  U4 bv = ld16s<NT>(row + ((size_t)hl * D + ob_off) * 2);
+  for (int pass = w; pass < passes; pass += W) {
+    const int h = pass * HPP + slot;
     float a[8], b[8], oa[8], ob[8];
-    unpack8<DT>(ld16s<NT>(qkv + ea * 2), a);
-    unpack8<DT>(ld16s<NT>(qkv + eb * 2), b);
-    if (hd < qk_heads) {  // uniform over the head's lanes
-      const uint8_t* gp = static_cast<const uint8_t*>(hd < p.nq ? p.gamma_q : p.gamma_k);
+    unpack8<DT>(av, a);
+    unpack8<DT>(bv, b);
+    if (pass + W < passes) {  // next group of heads, landing while this one is processed
+      hl = h + W * HPP < heads ? h + W * HPP : heads - 1;
+      av = ld16s<NT>(row + ((size_t)hl * D + oa_off) * 2);
+      bv = ld16s<NT>(row + ((size_t)hl * D + ob_off) * 2);
+    }
+    if (h < qk_heads) {  // uniform over the head's lanes
       float ga[8], gb[8];
-      unpack8<DT>(ld16(gp + (size_t)(8 * lane) * 2), ga);
-      unpack8<DT>(ld16(gp + (size_t)(HALF + 8 * lane) * 2), gb);
+      unpack8<DT>(h < p.nq ? gqa : gka, ga);
+      unpack8<DT>(h < p.nq ? gqb : gkb, gb);
       double acc = 0.0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -61,14 +102,6 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
         ss = dd_to_f32(hi, lo);
       }
       const float r = 1.0f / sqrtf(ss / (float)D + p.eps);
-      const int64_t pos = p.positions[t];
-      const float* cs = p.cos_sin + (size_t)pos * D;
-      const float4 c0 = *reinterpret_cast<const float4*>(cs + 8 * lane);
-      const float4 c1 = *reinterpret_cast<const float4*>(cs + 8 * lane + 4);
-      const float4 s0 = *reinterpret_cast<const float4*>(cs + HALF + 8 * lane);
-      const float4 s1 = *reinterpret_cast<const float4*>(cs + HALF + 8 * lane + 4);
-      const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float na = (a[i] * r) * ga[i];
@@ -88,8 +121,21 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
       oa[i] = div_rn(oa[i], sc, inv_sc);
       ob[i] = div_rn(ob[i], sc, inv_sc);
     }
-    st8s<NT>(p.out + ea, e4m3x4(oa[0], oa[1], oa[2], oa[3]), e4m3x4(oa[4], oa[5], oa[6], oa[7]));
-    st8s<NT>(p.out + eb, e4m3x4(ob[0], ob[1], ob[2], ob[3]), e4m3x4(ob[4], ob[5], ob[6], ob[7]));
+    // Lanes 2m and 2m+1 swap one 8-byte half so that each stores 16 contiguous
+    // codes: the even lane elements [16m, 16m+16), the odd lane the same range
+    // of the second half. Every head's output then leaves as whole lines.
+    const uint32_t a0 = e4m3x4(oa[0], oa[1], oa[2], oa[3]), a1 = e4m3x4(oa[4], oa[5], oa[6], oa[7]);
+    const uint32_t b0 = e4m3x4(ob[0], ob[1], ob[2], ob[3]), b1 = e4m3x4(ob[4], ob[5], ob[6], ob[7]);
+    const bool odd = (j & 1) != 0;
+    const uint32_t r0 = dpp_u32<0xB1>(odd ? a0 : b0), r1 = dpp_u32<0xB1>(odd ? a1 : b1);
+    if (h < heads) {
+      U4 v;
+      v.w[0] = odd ? r0 : a0;
+      v.w[1] = odd ? r1 : a1;
+      v.w[2] = odd ? b0 : r0;
+      v.w[3] = odd ? b1 : r1;
+      st16s<NT>(orow + (size_t)h * D + (odd ? HALF + 8 * (j - 1) : 8 * j), v);
+    }
   }
 }
 
@@ -106,16 +152,23 @@ static hipError_t launch_qk_nt(const QKParams& p, hipStream_t s) {
     case 32: fn = (const void*)&qk_kernel<DT, 32, NT>; break;
     default: return hipErrorInvalidConfiguration;
   }
-  const int block = 256;
-  const int64_t gpb = block / lph;
-  int64_t grid = (p.pairs + gpb - 1) / gpb;
-  if (grid > (1 << 22)) grid = 1 << 22;
+  const int block = 256;  // four wavefronts
+  const int64_t grid = (p.tokens * p.waves_per_token + 3) / 4;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(block), args, 0, s);
 }
 
 // Streaming hints (see ld16s) once qkv alone is >= 32 MiB; ANQ_STREAM=0/1 overrides.
 template <int DT>
-static hipError_t launch_qk_dt(const QKParams& p, hipStream_t s) {
+static hipError_t launch_qk_dt(QKParams p, hipStream_t s) {
+  // wavefronts per token: enough head groups in flight at once that the
+  // per-token chain of loads stays short (ANQ_QK_WAVES overrides, for sweeps)
+  const int passes = (p.nq + p.nk + p.nv + 64 / (p.head_dim / 16) - 1) / (64 / (p.head_dim / 16));
+  int W = passes < 2 ? 1 : 2;
+  if (const char* e = getenv("ANQ_QK_WAVES")) {
+    if (*e && atoi(e) > 0) W = atoi(e);
+  }
+  p.waves_per_token = W < passes ? W : passes;
   bool stream = p.pairs * (int64_t)p.head_dim * 2 >= ((int64_t)32 << 20);
   if (const char* e = getenv("ANQ_STREAM")) {
     if (*e) stream = atoi(e) != 0;
