@@ -2,7 +2,7 @@
 """Benchmark of the fused add + RMSNorm + FP8/NVFP4 tail (and the Q/K norm +
 RoPE + FP8 store) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-sweep] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload 1..5] [--no-sweep] [--no-cpu] [--no-ab]
 
 A step is one call of the fused op on one batch of the workload's seeded
 synthetic inputs, already resident in HBM. Inputs and outputs rotate over
@@ -16,6 +16,10 @@ Prints ONE JSON line. `value` is achieved algorithmic HBM throughput in GB/s
 on the headline workload (fp16 [64, 8192] add + RMSNorm + NVFP4, the shape the
 pages measure: 0.039 ms on an RTX 5060 Ti, TensorRT-LLM issue #17900,
 Performance result). `all_workloads` holds the same figures for every shape.
+`fusion_ab` times the separated tail (add_rmsnorm, then quant_fp8 or
+quant_nvfp4: two kernels and a T-rounded norm tensor between them) against the
+fused kernel on the tail workloads, the comparison the pages make (0.103 ms
+separated vs 0.039 ms fused, 2.64x).
 """
 from __future__ import annotations
 
@@ -33,6 +37,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fused add+RMSNorm+FP8/NVFP4 quant: µs/call and achieved HBM GB/s (% peak)"
 PEAK_GBS = 8000.0                      # MI355X HBM3E
 PAGES_US = {2: 39.0}                   # the pages' fused-tail latency for this exact workload
+PAGES_SEPARATED_US = {2: 103.0}        # ... and their separated (two-kernel) latency
+AB_WORKLOADS = (2, 3, 4)
 ROTATE_BYTES = 1 << 30
 SCALARS = os.path.join(ROOT, "tests", "golden", "workload_scalars.json")
 TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -62,11 +68,12 @@ def source_hash() -> str:
 class Workload:
     """Device-resident inputs and outputs of one workload, in R rotating sets."""
 
-    def __init__(self, k: int, scalars: dict, steps: int):
+    def __init__(self, k: int, scalars: dict, steps: int, separated: bool = False):
         import torch
 
         import workloads as W
         self.k = k
+        self.separated = separated
         self.inp = W.make_config(k)
         self.bytes = algorithmic_bytes(self.inp)
         # a graph of `steps` calls only ever touches `steps` sets
@@ -102,13 +109,21 @@ class Workload:
         self.q = [torch.empty(M, qcols, dtype=torch.uint8, device=dev) for _ in range(self.sets)]
         self.sf = ([torch.empty(M, H // 16, dtype=torch.uint8, device=dev) for _ in range(self.sets)]
                    if inp.op == "nvfp4" else None)
-        self.norm = ([torch.empty_like(x) for _ in range(self.sets)] if inp.norm_out else None)
+        # the separated path always materialises the norm (the quantiser's input)
+        self.norm = ([torch.empty_like(x) for _ in range(self.sets)]
+                     if inp.norm_out or separated else None)
 
     def call(self, i: int):
         import nvfp4_quantization_place_amd as A
         j = i % self.sets
         inp = self.inp
-        if self.kind == "qk":
+        if self.separated:
+            n = A.add_rmsnorm(self.x[j], self.res[j], self.g, inp.eps, norm=self.norm[j])
+            if self.kind == "fp8":
+                A.quant_fp8(n, self.scale, q=self.q[j])
+            else:
+                A.quant_nvfp4(n, self.scale, q=self.q[j], sf=self.sf[j])
+        elif self.kind == "qk":
             A.qk_norm_rope_fp8(self.qkv[j], self.gq, self.gk, self.pos, self.cs, self.scale, inp.eps,
                                inp.nq, inp.nk, inp.nv, inp.head_dim, out=self.out[j])
         elif self.kind == "fp8":
@@ -247,6 +262,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-sweep", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-ab", action="store_true",
+                    help="skip the fused vs separated (two-kernel) comparison")
     ap.add_argument("--no-eager", action="store_true",
                     help="skip the eager timing (so a kernel trace holds graph launches only)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -283,6 +300,24 @@ def main():
         del w
         torch.cuda.empty_cache()
 
+    ab = {}
+    if not args.no_ab:
+        for k in AB_WORKLOADS:
+            w = Workload(k, scalars, args.steps, separated=True)
+            r = time_workload(w, args.steps, args.warmup, eager=False)
+            fused = results[k]["us_per_call"] if k in results else None
+            e = {"workload": r["workload"], "separated_us": r["us_per_call"], "fused_us": fused,
+                 "speedup": round(r["us_per_call"] / fused, 3) if fused else None}
+            if k in PAGES_US:
+                e["pages_separated_us"] = PAGES_SEPARATED_US[k]
+                e["pages_fused_us"] = PAGES_US[k]
+                e["pages_speedup"] = round(PAGES_SEPARATED_US[k] / PAGES_US[k], 3)
+            ab[str(k)] = e
+            print(f"# separated {k} {r['workload']}: {r['us_per_call']} us/call (graph)",
+                  file=sys.stderr, flush=True)
+            del w
+            torch.cuda.empty_cache()
+
     head = results[args.workload]
     inp_dtype = head["io_dtype"]
     traffic = head["traffic_bytes_per_call"]
@@ -310,6 +345,8 @@ def main():
                                  if traffic else None)},
         "all_workloads": {str(k): v for k, v in results.items()},
     }
+    if ab:
+        line["fusion_ab"] = ab
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload, scalars)
     print(json.dumps(line), flush=True)

@@ -162,6 +162,35 @@ int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
                      void* stream);
 
 /*
+ * The separated local tail, kept as the measured baseline of the fused ops and
+ * as standalone ops. Without the fused kernel the tail launches a
+ * residual/RMSNorm kernel and then a quantisation kernel (TensorRT-LLM issue
+ * #17900, Proposal; Performance result: 0.103 ms separated vs 0.039 ms fused
+ * at FP16 [64, 8192]). The quantiser then reads the norm output rounded to T,
+ * so its codes can differ from the fused ops' (which quantise the binary32 n).
+ *
+ * add_rmsnorm: residual <- RNE_T(x + residual); norm_out <- RNE_T(n), with n
+ *   as in the numerics above. norm_out is required. No scale, no codes.
+ */
+int add_rmsnorm(const void* x, void* residual, const void* gamma, float eps, int64_t tokens,
+                int64_t hidden, int dtype, void* norm_out, void* stream);
+
+/*
+ * quant_fp8: q_i = E4M3(in_i / s) for in [tokens, hidden] T (hidden % 16 == 0),
+ *   s = *scale; q [tokens, hidden] uint8.
+ */
+int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden, int dtype,
+              uint8_t* q, void* stream);
+
+/*
+ * quant_nvfp4: the NVFP4 epilogue above applied to n_i = in_i (T converted to
+ *   binary32, exact): q [tokens, hidden/2] packed E2M1, sf [tokens, hidden/16]
+ *   E4M3, under G = *global_scale.
+ */
+int quant_nvfp4(const void* in, const float* global_scale, int64_t tokens, int64_t hidden,
+                int dtype, uint8_t* q, uint8_t* sf, void* stream);
+
+/*
  * The one place that states the NVFP4 output shapes (the review thread of
  * TensorRT-LLM PR #14361 asks for a single shared shape helper):
  *   q_cols = hidden / 2, sf_cols = hidden / 16, for tokens rows each.

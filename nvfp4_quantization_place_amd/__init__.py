@@ -15,6 +15,7 @@ import os
 import torch  # loads the HIP runtime the library binds to
 
 __all__ = ["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4", "qk_norm_rope_fp8",
+           "add_rmsnorm", "quant_fp8", "quant_nvfp4",
            "nvfp4_shape", "status_string", "lib", "AnqError", "LIB_PATH",
            "ANQ_F16", "ANQ_BF16", "STATUS"]
 
@@ -34,6 +35,9 @@ _SIGS = {
     "add_rmsnorm_quant_nvfp4": [_P, _P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P, _P, _P],
     "qk_norm_rope_fp8": [_P, _P, _P, _P, _P, _I64, _P, _F, _I64, _I32, _I32, _I32, _I32, _I32,
                          ctypes.c_int, _P, _P],
+    "add_rmsnorm": [_P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P],
+    "quant_fp8": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P],
+    "quant_nvfp4": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P],
     "anq_nvfp4_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "anq_status_string": [ctypes.c_int],
 }
@@ -192,3 +196,53 @@ def qk_norm_rope_fp8(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: floa
     if st:
         raise AnqError("qk_norm_rope_fp8", st)
     return out
+
+
+# ------------------------------------------------------------ separated tail
+
+
+def add_rmsnorm(x, residual, gamma, eps: float, norm=None, stream=None):
+    """residual += x (in place, rounded to T); returns norm_out = RMSNorm(residual) * gamma in T.
+    The first kernel of the separated (unfused) tail."""
+    dev = _check_gpu(x, residual, gamma, norm)
+    tokens, hidden = _rows(x)
+    if residual.dtype != x.dtype or gamma.dtype != x.dtype or residual.shape != x.shape:
+        raise ValueError("x, residual and gamma must share the dtype; x and residual the shape")
+    if norm is None:
+        norm = torch.empty_like(x)
+    st = lib().add_rmsnorm(_ptr(x), _ptr(residual), _ptr(gamma), eps, tokens, hidden,
+                           _dtype_code(x), _ptr(norm), _stream(dev, stream))
+    if st:
+        raise AnqError("add_rmsnorm", st)
+    return norm
+
+
+def quant_fp8(t, scale, q=None, stream=None):
+    """E4M3 codes of t / scale for an fp16/bf16 tensor t [..., hidden]."""
+    dev = _check_gpu(t, scale, q)
+    _scalar(scale, "scale")
+    tokens, hidden = _rows(t)
+    if q is None:
+        q = torch.empty(t.shape, dtype=torch.uint8, device=dev)
+    st = lib().quant_fp8(_ptr(t), _ptr(scale), tokens, hidden, _dtype_code(t), _ptr(q),
+                         _stream(dev, stream))
+    if st:
+        raise AnqError("quant_fp8", st)
+    return q
+
+
+def quant_nvfp4(t, global_scale, q=None, sf=None, stream=None):
+    """NVFP4 (packed E2M1 + per-16 E4M3 scales) of an fp16/bf16 tensor t [..., hidden]."""
+    dev = _check_gpu(t, global_scale, q, sf)
+    _scalar(global_scale, "global_scale")
+    tokens, hidden = _rows(t)
+    qc, sc = (hidden // 2, hidden // 16) if hidden % 16 == 0 and hidden > 0 else (1, 1)
+    if q is None:
+        q = torch.empty(*t.shape[:-1], qc, dtype=torch.uint8, device=dev)
+    if sf is None:
+        sf = torch.empty(*t.shape[:-1], sc, dtype=torch.uint8, device=dev)
+    st = lib().quant_nvfp4(_ptr(t), _ptr(global_scale), tokens, hidden, _dtype_code(t), _ptr(q),
+                           _ptr(sf), _stream(dev, stream))
+    if st:
+        raise AnqError("quant_nvfp4", st)
+    return q, sf

@@ -169,6 +169,76 @@ extern "C" int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void
   return launch_status(anq::launch_qk(dtype, p, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int add_rmsnorm(const void* x, void* residual, const void* gamma, float eps,
+                           int64_t tokens, int64_t hidden, int dtype, void* norm_out, void* stream) {
+  if (!gamma || (tokens != 0 && (!x || !residual || !norm_out))) return ANQ_ERR_NULL;
+  if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
+  if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
+  if (hidden > ANQ_MAX_HIDDEN) return ANQ_ERR_UNSUPPORTED;
+  if (tokens > INT64_MAX / (2 * hidden)) return ANQ_ERR_SHAPE;
+  if (!valid_eps(eps)) return ANQ_ERR_VALUE;
+  if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(gamma, 16) || !aligned(norm_out, 16))
+    return ANQ_ERR_ALIGN;
+  const int64_t act = tokens * hidden * 2;
+  const Span outs[2] = {span(residual, act), span(norm_out, act)};
+  const Span ins[2] = {span(x, act), span(gamma, hidden * 2)};
+  if (any_alias(outs, 2, ins, 2)) return ANQ_ERR_ALIAS;
+  if (tokens == 0) return ANQ_OK;
+
+  anq::TailParams p{};
+  p.x = x;
+  p.residual = residual;
+  p.gamma = gamma;
+  p.scale = nullptr;
+  p.norm_out = norm_out;
+  p.q = nullptr;
+  p.sf = nullptr;
+  p.eps = eps;
+  p.tokens = tokens;
+  p.hidden = (int32_t)hidden;
+  p.vec = (int32_t)(hidden / 8);
+  const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
+  p.rows_per_group = t.rows;
+  return launch_status(anq::launch_tail(dtype, anq::kEpiNone, true, p, t,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+int quant_common(const void* in, const float* scale, int64_t tokens, int64_t hidden, int dtype,
+                 uint8_t* q, uint8_t* sf, bool nvfp4, void* stream) {
+  if (!scale || (tokens != 0 && (!in || !q || (nvfp4 && !sf)))) return ANQ_ERR_NULL;
+  if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
+  if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
+  if (tokens > INT64_MAX / (2 * hidden)) return ANQ_ERR_SHAPE;
+  if (!aligned(in, 16) || !aligned(q, 16) || !aligned(scale, 4)) return ANQ_ERR_ALIGN;
+  const int64_t n = tokens * hidden;
+  const Span outs[2] = {span(q, nvfp4 ? n / 2 : n), span(sf, nvfp4 ? n / 16 : 0)};
+  const Span ins[2] = {span(in, n * 2), span(scale, 4)};
+  if (any_alias(outs, 2, ins, 2)) return ANQ_ERR_ALIAS;
+  if (tokens == 0) return ANQ_OK;
+  anq::QuantParams p{};
+  p.in = in;
+  p.scale = scale;
+  p.q = q;
+  p.sf = sf;
+  p.vecs = n / 8;
+  return launch_status(anq::launch_quant(dtype, nvfp4 ? anq::kEpiNvfp4 : anq::kEpiFp8, p,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden,
+                         int dtype, uint8_t* q, void* stream) {
+  return quant_common(in, scale, tokens, hidden, dtype, q, nullptr, false, stream);
+}
+
+extern "C" int quant_nvfp4(const void* in, const float* global_scale, int64_t tokens,
+                           int64_t hidden, int dtype, uint8_t* q, uint8_t* sf, void* stream) {
+  return quant_common(in, global_scale, tokens, hidden, dtype, q, sf, true, stream);
+}
+
 extern "C" int anq_nvfp4_shape(int64_t tokens, int64_t hidden, int64_t* q_cols, int64_t* sf_cols) {
   if (!q_cols || !sf_cols) return ANQ_ERR_NULL;
   if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;

@@ -166,27 +166,38 @@ __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
-// Eight binary32 values -> eight E2M1 codes, element i in bits 4i..4i+3.
+// Eight binary32 values -> eight E2M1 codes, element i in bits 4i..4i+3. The
+// clamp to +-6 (the nearest-even result beyond 6) keeps infinities, which a
+// block's n * mult can reach, out of the converter.
 __device__ __forceinline__ uint32_t e2m1x8(const float (&v)[8]) {
+  float c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(v[i], 6.0f, -6.0f);
   uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[0], c[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[2], c[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[4], c[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[6], c[7], 1.0f, 3);
   return w;
 }
 
 // ---------------------------------------------------------------- division
 
+
 // Correctly rounded a / b from y = RN(1/b): q0 = RN(a*y) is within an ulp of
 // a/b, the remainder a - b*q0 is exact in one FMA, and q0 + rem*y rounded once
-// is RN(a/b) (Markstein's correction theorem; no underflow in this use). The
-// sign of q0 is carried over so that a = -0 keeps its sign like IEEE division.
+// is RN(a/b) (Markstein's correction theorem). Where a/b is below the normal
+// binary32 range the result may be an ulp off, but every encoder here maps all
+// such values to a zero of the quotient's sign. The sign of q0 is carried over
+// so that a = -0 keeps its sign like IEEE division.
 __device__ __forceinline__ float div_rn(float a, float b, float y) {
   const float q0 = a * y;
   const float rem = __builtin_fmaf(-q0, b, a);
   const float q1 = __builtin_fmaf(rem, y, q0);
-  return __builtin_copysignf(q1, q0);
+  // q0 = +-inf (a infinite, or a/b at the top of the range): the correction
+  // would be inf - inf; the quotient is then at least the largest finite value
+  // in magnitude, which every encoder here saturates, so q0 stands.
+  return __builtin_isfinite(q0) ? __builtin_copysignf(q1, q0) : q0;
 }
 
 // ------------------------------------------------------ cross-lane sums
@@ -310,6 +321,48 @@ __device__ __forceinline__ float dd_to_f32(double hi, double lo) {
   const double mid = 0.5 * ((double)flo + (double)fhi);
   if (hi != mid) return f;
   return lo > 0.0 ? fhi : (lo < 0.0 ? flo : f);
+}
+
+// ------------------------------------------------------------- epilogues
+// Shared by the fused tail and the standalone quantisers, so both encode with
+// the same instructions.
+
+constexpr float kInv6 = 0x1.555556p-3f;  // RN(1/6)
+
+// FP8: codes of n_i / s for eight values (s = dequant scale, inv_s = RN(1/s)).
+__device__ __forceinline__ void fp8_codes8(const float (&n)[8], float s, float inv_s, uint32_t& lo,
+                                           uint32_t& hi) {
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = div_rn(n[i], s, inv_s);
+  lo = e4m3x4(t[0], t[1], t[2], t[3]);
+  hi = e4m3x4(t[4], t[5], t[6], t[7]);
+}
+
+// NVFP4 multipliers G / value(c) for the 127 non-negative E4M3 codes (0 for c = 0
+// and the unused slot 127), filled by the workgroup; IEEE divisions.
+__device__ __forceinline__ void fill_mult_tab(float* tab, float G) {
+  for (int c = threadIdx.x; c < 128; c += blockDim.x) {
+    const float S = c < 127 ? e4m3_value_pos((uint32_t)c) : 0.0f;
+    tab[c] = S > 0.0f ? G / S : 0.0f;
+  }
+}
+
+// NVFP4: one lane holds one half (8 values) of a 16-element block, its partner
+// (lane ^ 1) the other half. Returns the lane's eight E2M1 codes packed low
+// nibble first, and the block's E4M3 scale code (the same in both lanes).
+__device__ __forceinline__ void nvfp4_half_block(const float (&n)[8], float G, const float* mult_tab,
+                                                 uint32_t& codes, uint32_t& sfc) {
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(n[i]));
+  am = fmaxf(am, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(am))));  // other half
+  sfc = e4m3_pos(G * div_rn(am, 6.0f, kInv6));
+  const float mult = mult_tab[sfc & 0x7Fu];  // in the table whatever the input (NaN gives 0x7F)
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = n[i] * mult;
+  codes = e2m1x8(t);
 }
 
 }  // namespace anq

@@ -6,7 +6,7 @@
 
 namespace anq {
 
-enum Epilogue { kEpiFp8 = 0, kEpiNvfp4 = 1 };
+enum Epilogue { kEpiFp8 = 0, kEpiNvfp4 = 1, kEpiNone = 2 };
 
 struct TailParams {
   const void* x;
@@ -58,5 +58,17 @@ struct QKParams {
 };
 
 hipError_t launch_qk(int dtype, const QKParams& p, hipStream_t stream);
+
+// Standalone quantisation of an activation tensor [tokens, hidden] (the second
+// kernel of the separated tail).
+struct QuantParams {
+  const void* in;
+  const float* scale;  // FP8: s; NVFP4: G
+  uint8_t* q;
+  uint8_t* sf;         // NVFP4 only
+  int64_t vecs;        // tokens * hidden / 8
+};
+
+hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t stream);
 
 }  // namespace anq

@@ -1,0 +1,68 @@
+// Standalone FP8 / NVFP4 quantisation of an activation tensor: the second
+// kernel of the separated local tail, which launches a residual/RMSNorm
+// kernel and then a quantisation kernel (TensorRT-LLM issue #17900 "Fuse local
+// NVFP4 tail after NCCL fallback", Proposal). Together with add_rmsnorm it is
+// the baseline the fused kernel is measured against.
+//
+// gfx950 mapping: one thread per 16-byte vector of 8 activations, one pass over
+// the tensor (no grid-stride loop: single-pass stores stream best on MI355X).
+// An NVFP4 block of 16 is two vectors in adjacent lanes; rows are multiples of
+// 16 elements, so flattening [tokens, hidden] keeps every block inside a row.
+// The encoders are the fused kernel's own (fp8_codes8, nvfp4_half_block).
+#include <stdlib.h>
+
+#include "anq_device.h"
+#include "anq_internal.h"
+
+namespace anq {
+
+template <int DT, int EPI, bool NT>
+__global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
+  __shared__ float mult_tab[128];
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const float sc = *p.scale;  // FP8: s, NVFP4: G
+  const float inv_sc = 1.0f / sc;
+  if constexpr (EPI == kEpiNvfp4) {
+    fill_mult_tab(mult_tab, sc);
+    __syncthreads();
+  }
+  const bool ok = v < p.vecs;
+  const int64_t vv = ok ? v : p.vecs - 1;  // past the end: a clamped load, no store
+  float f[8];
+  unpack8<DT>(ld16s<NT>(static_cast<const uint8_t*>(p.in) + (size_t)vv * 16), f);
+  if constexpr (EPI == kEpiFp8) {
+    uint32_t lo, hi;
+    fp8_codes8(f, sc, inv_sc, lo, hi);
+    if (ok) st8s<false>(p.q + (size_t)v * 8, lo, hi);
+  } else {
+    uint32_t w, sfc;
+    nvfp4_half_block(f, sc, mult_tab, w, sfc);
+    if (ok) {
+      st4s<false>(p.q + (size_t)v * 4, w);
+      if ((v & 1) == 0) st1s<false>(p.sf + (size_t)(v >> 1), (uint8_t)sfc);
+    }
+  }
+}
+
+template <int DT, int EPI>
+static hipError_t launch_quant_epi(const QuantParams& p, hipStream_t s) {
+  void* args[] = {const_cast<QuantParams*>(&p)};
+  // streaming hint on the input once it is >= 32 MiB; ANQ_STREAM=0/1 overrides
+  bool stream = p.vecs * 16 >= ((int64_t)32 << 20);
+  if (const char* e = getenv("ANQ_STREAM")) {
+    if (*e) stream = atoi(e) != 0;
+  }
+  const void* fn = stream ? (const void*)&quant_kernel<DT, EPI, true>
+                          : (const void*)&quant_kernel<DT, EPI, false>;
+  const int64_t grid = (p.vecs + 255) / 256;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s);
+}
+
+hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t s) {
+  if (dtype == kBF16)
+    return epi == kEpiFp8 ? launch_quant_epi<kBF16, kEpiFp8>(p, s) : launch_quant_epi<kBF16, kEpiNvfp4>(p, s);
+  return epi == kEpiFp8 ? launch_quant_epi<kF16, kEpiFp8>(p, s) : launch_quant_epi<kF16, kEpiNvfp4>(p, s);
+}
+
+}  // namespace anq

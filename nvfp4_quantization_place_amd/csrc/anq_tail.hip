@@ -180,14 +180,13 @@ tail_kernel(TailParams p) {
       rv[k] = ld16s<NT>(res + rb + voff[k]);
     }
   }
-  const float sc = *p.scale;       // FP8: s, NVFP4: G
-  const float inv_sc = 1.0f / sc;  // RN(1/s), correctly rounded division
-  constexpr float kInv6 = 0x1.555556p-3f;  // RN(1/6)
+  float sc = 0.0f, inv_sc = 0.0f;  // FP8: s and RN(1/s); NVFP4: G
+  if constexpr (EPI != kEpiNone) {
+    sc = *p.scale;
+    inv_sc = 1.0f / sc;  // correctly rounded division
+  }
   if constexpr (EPI == kEpiNvfp4) {
-    for (int c = threadIdx.x; c < 128; c += blockDim.x) {
-      const float S = c < 127 ? e4m3_value_pos((uint32_t)c) : 0.0f;
-      mult_tab[c] = S > 0.0f ? sc / S : 0.0f;
-    }
+    fill_mult_tab(mult_tab, sc);
     __syncthreads();
   }
   // gamma stays packed in registers (4 per vector) and is unpacked per row:
@@ -245,24 +244,12 @@ tail_kernel(TailParams p) {
         if (vok[k]) st16s<NT>(row_ptr<G>(nout, (size_t)row * row_bytes) + voff[k], pack8<DT>(n));
       }
       if constexpr (EPI == kEpiFp8) {
-        float t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = div_rn(n[i], sc, inv_sc);
-        const uint32_t lo = e4m3x4(t[0], t[1], t[2], t[3]);
-        const uint32_t hi = e4m3x4(t[4], t[5], t[6], t[7]);
+        uint32_t lo, hi;
+        fp8_codes8(n, sc, inv_sc, lo, hi);
         if (vok[k]) st8s<false>(row_ptr<G>(p.q, (size_t)row * p.hidden) + voff[k] / 2, lo, hi);
-      } else {
-        float am = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(n[i]));
-        am = fmaxf(am, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(am))));  // other half of the block
-        const float s_b = sc * div_rn(am, 6.0f, kInv6);
-        const uint32_t sfc = e4m3_pos(s_b);
-        const float mult = mult_tab[sfc];
-        float t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = n[i] * mult;
-        const uint32_t w = e2m1x8(t);
+      } else if constexpr (EPI == kEpiNvfp4) {
+        uint32_t w, sfc;
+        nvfp4_half_block(n, sc, mult_tab, w, sfc);
         if (vok[k]) {
           st4s<false>(row_ptr<G>(p.q, (size_t)row * (p.hidden / 2)) + voff[k] / 4, w);
           if ((lane & 1) == 0)
@@ -363,6 +350,7 @@ static hipError_t launch2(bool norm, const TailParams& p, const Tiling& t, hipSt
 
 template <int DT>
 static hipError_t launch1(int epi, bool norm, const TailParams& p, const Tiling& t, hipStream_t s) {
+  if (epi == kEpiNone) return launch3<DT, kEpiNone, true>(p, t, s);  // add + RMSNorm only
   return epi == kEpiFp8 ? launch2<DT, kEpiFp8>(norm, p, t, s) : launch2<DT, kEpiNvfp4>(norm, p, t, s);
 }
 

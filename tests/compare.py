@@ -65,7 +65,10 @@ def check_residual(gpu_bits, ref_bits, what="residual"):
 def norm_stats(gpu_bits, ref_bits, dtype):
     g = O.t_decode(gpu_bits, dtype).astype(np.float64)
     r = O.t_decode(ref_bits, dtype).astype(np.float64)
-    err = np.abs(g - r)
+    same = np.asarray(gpu_bits) == np.asarray(ref_bits)
+    with np.errstate(invalid="ignore"):
+        err = np.where(same, 0.0, np.abs(g - r))      # equal infinities: no error
+    err = np.where(np.isnan(err), np.inf, err)        # differing non-finite values fail
     return dict(max_abs_err=float(err.max()) if err.size else 0.0,
                 bit_exact=bool(np.array_equal(np.asarray(gpu_bits), np.asarray(ref_bits))),
                 n_diff=int(np.count_nonzero(np.asarray(gpu_bits) != np.asarray(ref_bits))))

@@ -40,7 +40,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4",
-                                           "qk_norm_rope_fp8", "anq_nvfp4_shape",
+                                           "qk_norm_rope_fp8", "add_rmsnorm", "quant_fp8",
+                                           "quant_nvfp4", "anq_nvfp4_shape",
                                            "anq_status_string"])
 
 
@@ -163,3 +164,54 @@ def test_qk_validation(L):
     assert qk(L, tokens=4, out=addr(0)) == ALIAS        # rejected before any HIP call
     assert qk(L, tokens=4, cs=addr(6)) == ALIAS
     assert qk(L, tokens=4, pos=addr(6, 8)) == ALIAS
+
+
+def addnorm(L, **kw):
+    a = dict(x=addr(0), res=addr(1), gamma=addr(2), eps=1e-6, tokens=0, hidden=128, dtype=1,
+             norm=addr(5), stream=None)
+    a.update(kw)
+    return L.add_rmsnorm(a["x"], a["res"], a["gamma"], a["eps"], a["tokens"], a["hidden"],
+                         a["dtype"], a["norm"], a["stream"])
+
+
+def qfp8(L, **kw):
+    a = dict(t=addr(0), scale=addr(3), tokens=0, hidden=128, dtype=0, q=addr(4), stream=None)
+    a.update(kw)
+    return L.quant_fp8(a["t"], a["scale"], a["tokens"], a["hidden"], a["dtype"], a["q"], a["stream"])
+
+
+def qnv(L, **kw):
+    a = dict(t=addr(0), scale=addr(3), tokens=0, hidden=128, dtype=1, q=addr(4), sf=addr(6),
+             stream=None)
+    a.update(kw)
+    return L.quant_nvfp4(a["t"], a["scale"], a["tokens"], a["hidden"], a["dtype"], a["q"], a["sf"],
+                         a["stream"])
+
+
+def test_separated_tail_validation(L):
+    assert addnorm(L) == OK
+    for k in ("x", "res", "norm"):
+        assert addnorm(L, tokens=4, **{k: None}) == NULL, k
+        assert addnorm(L, tokens=0, **{k: None}) == OK, k
+    assert addnorm(L, gamma=None) == NULL
+    assert addnorm(L, hidden=24) == SHAPE
+    assert addnorm(L, hidden=65536 + 16) == UNSUP
+    assert addnorm(L, dtype=7) == DTYPE
+    assert addnorm(L, eps=-1.0) == VALUE
+    assert addnorm(L, norm=addr(5, 8)) == ALIGN
+    assert addnorm(L, tokens=4, norm=addr(1)) == ALIAS      # norm over residual
+    assert addnorm(L, tokens=4, res=addr(0)) == ALIAS       # residual over x
+    for op in (qfp8, qnv):
+        assert op(L) == OK
+        assert op(L, tokens=4, t=None) == NULL
+        assert op(L, tokens=0, t=None, q=None) == OK
+        assert op(L, scale=None) == NULL
+        assert op(L, hidden=40) == SHAPE
+        assert op(L, hidden=1 << 20) == OK                  # no row-width limit
+        assert op(L, dtype=9) == DTYPE
+        assert op(L, t=addr(0, 8)) == ALIGN
+        assert op(L, scale=addr(3, 2)) == ALIGN
+        assert op(L, tokens=4, q=addr(0, 16)) == ALIAS       # codes over the input
+        assert op(L, tokens=4, scale=addr(4, 4)) == ALIAS
+    assert qnv(L, tokens=4, sf=None) == NULL
+    assert qnv(L, tokens=4, sf=addr(4, 32)) == ALIAS         # scales over the codes

@@ -161,6 +161,31 @@ def test_edge_rows(op, dtype, hidden):
         assert np.any(got["q"][0] == 0x80) and np.any(got["q"][0] == 0x00)  # signed zeros
 
 
+@pytest.mark.parametrize("op,scale", [("fp8", 1e-36), ("fp8", 0.05), ("nvfp4", 1e30),
+                                      ("nvfp4", 1.0)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_overflow_saturates(op, scale, dtype):
+    """gamma entries at the top of T's range drive n (binary32), n / s, G * amax / 6
+    and n * mult past the largest finite value: every code saturates (E4M3 to
+    448, E2M1 to 6) as the definitions say, never a NaN code."""
+    rng = np.random.default_rng(17)
+    H = 1024
+    x = rng.standard_normal((6, H)).astype(np.float32)
+    x[1, 3] = 200.0                                        # |h r| near sqrt(H)
+    top = 65504.0 if dtype == "f16" else 3.3895313892515355e38
+    gamma = (1.0 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    gamma[::5] = top
+    gamma[3::10] = -top
+    inp = _tail_from_arrays(op, dtype, x, np.zeros_like(x), gamma, scale=scale)
+    got = gpu_tail(inp, scale)
+    ref = oracle_tail(inp, scale)
+    compare_tail(inp, scale, got, ref)
+    if op == "fp8":
+        assert np.any((got["q"] & 0x7F) == 0x7E) and not np.any((got["q"] & 0x7F) == 0x7F)
+    else:
+        assert np.any(got["sf"] == 0x7E) and not np.any((got["sf"] & 0x7F) == 0x7F)
+
+
 def test_zero_tokens_is_a_noop_and_errors_raise():
     import nvfp4_quantization_place_amd as A
     x = torch.zeros(0, 128, dtype=torch.bfloat16, device="cuda")
