@@ -16,6 +16,8 @@ Prints ONE JSON line. `value` is achieved algorithmic HBM throughput in GB/s
 on the headline workload (fp16 [64, 8192] add + RMSNorm + NVFP4, the shape the
 pages measure: 0.039 ms on an RTX 5060 Ti, TensorRT-LLM issue #17900,
 Performance result). `all_workloads` holds the same figures for every shape.
+`kv_store` times the Q/K op with its KV-cache store epilogue (SGLang PR
+#32975) on the Q/K workload, writing K|V codes into a shuffled paged pool.
 `fusion_ab` times the separated tail (add_rmsnorm, then quant_fp8 or
 quant_nvfp4: two kernels and a T-rounded norm tensor between them) against the
 fused kernel on the tail workloads, the comparison the pages make (0.103 ms
@@ -68,14 +70,17 @@ def source_hash() -> str:
 class Workload:
     """Device-resident inputs and outputs of one workload, in R rotating sets."""
 
-    def __init__(self, k: int, scalars: dict, steps: int, separated: bool = False):
+    def __init__(self, k: int, scalars: dict, steps: int, separated: bool = False,
+                 kv_store: bool = False):
+        import numpy as np
         import torch
 
         import workloads as W
         self.k = k
         self.separated = separated
+        self.kv_store = kv_store
         self.inp = W.make_config(k)
-        self.bytes = algorithmic_bytes(self.inp)
+        self.bytes = algorithmic_bytes(self.inp) + (self.inp.tokens * 8 if kv_store else 0)
         # a graph of `steps` calls only ever touches `steps` sets
         self.sets = max(2, min(math.ceil(ROTATE_BYTES / self.bytes), steps))
         dev = "cuda"
@@ -91,6 +96,16 @@ class Workload:
             self.scale = torch.tensor([inp.scale], dtype=torch.float32, device=dev)
             self.dtype = inp.dtype
             self.name = inp.name
+            if kv_store:  # pool of 1.25x the tokens' slots, shuffled; Q codes dense
+                D = inp.head_dim
+                nslots = inp.tokens * 5 // 4
+                rng = np.random.default_rng(k)
+                self.slots = torch.from_numpy(rng.permutation(nslots)[:inp.tokens].astype(np.int64)).to(dev)
+                self.pool = [torch.zeros(nslots, (inp.nk + inp.nv) * D, dtype=torch.uint8, device=dev)
+                             for _ in range(self.sets)]
+                self.out = [torch.empty(inp.tokens, inp.nq * D, dtype=torch.uint8, device=dev)
+                            for _ in range(self.sets)]
+                self.name = inp.name + "_kv_store"
             return
         self.kind = inp.op
         self.name = inp.name
@@ -123,6 +138,10 @@ class Workload:
                 A.quant_fp8(n, self.scale, q=self.q[j])
             else:
                 A.quant_nvfp4(n, self.scale, q=self.q[j], sf=self.sf[j])
+        elif self.kv_store:
+            A.qk_norm_rope_fp8_kv_store(self.qkv[j], self.gq, self.gk, self.pos, self.cs, self.scale,
+                                        inp.eps, inp.nq, inp.nk, inp.nv, inp.head_dim, self.slots,
+                                        self.pool[j], q_out=self.out[j])
         elif self.kind == "qk":
             A.qk_norm_rope_fp8(self.qkv[j], self.gq, self.gk, self.pos, self.cs, self.scale, inp.eps,
                                inp.nq, inp.nk, inp.nv, inp.head_dim, out=self.out[j])
@@ -263,7 +282,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-ab", action="store_true",
-                    help="skip the fused vs separated (two-kernel) comparison")
+                    help="skip the fused vs separated (two-kernel) comparison and the KV-store timing")
     ap.add_argument("--no-eager", action="store_true",
                     help="skip the eager timing (so a kernel trace holds graph launches only)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -318,6 +337,19 @@ def main():
             del w
             torch.cuda.empty_cache()
 
+    kv = None
+    if not args.no_ab:
+        w = Workload(5, scalars, args.steps, kv_store=True)
+        r = time_workload(w, args.steps, args.warmup, eager=False)
+        kv = {"workload": r["workload"], "us_per_call": r["us_per_call"],
+              "bytes_per_call": r["bytes_per_call"], "gbs": r["gbs"],
+              "frac_of_peak": r["frac_of_peak"],
+              "plain_us_per_call": results[5]["us_per_call"] if 5 in results else None}
+        print(f"# kv store 5 {r['workload']}: {r['us_per_call']} us/call (graph), {r['gbs']} GB/s",
+              file=sys.stderr, flush=True)
+        del w
+        torch.cuda.empty_cache()
+
     head = results[args.workload]
     inp_dtype = head["io_dtype"]
     traffic = head["traffic_bytes_per_call"]
@@ -347,6 +379,8 @@ def main():
     }
     if ab:
         line["fusion_ab"] = ab
+    if kv:
+        line["kv_store"] = kv
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload, scalars)
     print(json.dumps(line), flush=True)

@@ -62,15 +62,22 @@
  *  - Arguments are validated on the host before any HIP call. A rejected call
  *    returns a nonzero status and enqueues nothing. tokens == 0 returns ANQ_OK
  *    and enqueues nothing; the token-sized buffers (x, residual, q, sf,
- *    norm_out, qkv, positions, out) may then be NULL, as empty tensors are.
+ *    norm_out, qkv, positions, out, slot_mapping) may then be NULL, as empty
+ *    tensors are.
  *  - residual is the only in/out buffer. Every output must be disjoint from
  *    every other buffer of the call; x must be disjoint from residual; the
  *    read-only inputs may overlap each other. Violations return ANQ_ERR_ALIAS.
  *  - 16-byte alignment is required for x, residual, gamma, norm_out, q and
- *    qkv/out/cos_sin; 4 bytes for scalars; 8 for positions; sf has none.
- *  - Left to the caller (not checked): finite inputs, a finite nonzero scale,
- *    0 <= positions[t] < max_pos. Breaking them gives unspecified codes, never
- *    an out-of-bounds access except for positions outside [0, max_pos).
+ *    qkv/out/cos_sin/q_out/kv_cache; 4 bytes for scalars; 8 for positions and
+ *    slot_mapping; sf has none.
+ *  - Left to the caller (not checked): finite inputs, a positive normal
+ *    binary32 scale (s or G, so that 1/s is finite), 0 <= positions[t] < max_pos,
+ *    distinct KV slots. Breaking them gives unspecified codes, never an
+ *    out-of-bounds access: a position outside [0, max_pos) is clamped into it
+ *    and a slot outside [0, num_slots) stores nothing.
+ *  - Intermediate binary32 results that overflow (n, n / s, G * amax / 6,
+ *    n * mult, reachable with bf16 gamma near its maximum) are infinities, and
+ *    the encoders saturate them like any value past the top code.
  *  - Calls that share output buffers and overlap in time on different streams
  *    race; calls on one stream are ordered.
  */
@@ -97,7 +104,7 @@ enum {
   ANQ_ERR_ALIAS = 5,       /* buffers overlap where they must not */
   ANQ_ERR_UNSUPPORTED = 6, /* hidden > ANQ_MAX_HIDDEN, head_dim not supported, rotary_dim != head_dim */
   ANQ_ERR_LAUNCH = 7,      /* the HIP launch failed (message via anq_status_string) */
-  ANQ_ERR_VALUE = 8        /* eps negative or not finite, max_pos < 1, negative head counts */
+  ANQ_ERR_VALUE = 8        /* eps negative or not finite, max_pos < 1, negative head counts or num_slots */
 };
 
 /* Largest hidden size the fused row kernels take (a row is held in registers). */
@@ -160,6 +167,30 @@ int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
                      const float* scale, float eps, int64_t tokens, int32_t nq, int32_t nk,
                      int32_t nv, int32_t head_dim, int32_t rotary_dim, int dtype, uint8_t* out,
                      void* stream);
+
+/*
+ * The same op with the KV-cache store as its epilogue: the norm + RoPE + store
+ * kernel of SGLang PR #32975, whose new epilogue writes a uniform FP8 pool
+ * (every element of K and V an E4M3 code, no separate BF16 RoPE part).
+ * The codes are those of qk_norm_rope_fp8; only where they go differs:
+ *
+ *   q_out        [tokens, nq*D] uint8: the Q heads' codes (may be NULL if nq == 0)
+ *   kv_cache     [num_slots, (nk+nv)*D] uint8, in/out: the pool. Token t's K
+ *                heads then V heads go to row slot_mapping[t]; every other
+ *                row keeps its contents. A paged pool [blocks, block_size,
+ *                (nk+nv)*D] is this layout with slot = block * block_size + offset.
+ *   slot_mapping [tokens] int64 (device): the token's slot; a value outside
+ *                [0, num_slots) (e.g. -1 for a padding token) stores nothing
+ *   num_slots    rows of the pool (>= 0)
+ * kv_cache and slot_mapping may be NULL if nk + nv == 0. Other arguments as
+ * for qk_norm_rope_fp8. Two tokens with the same slot race.
+ */
+int qk_norm_rope_fp8_kv_store(const void* qkv, const void* gamma_q, const void* gamma_k,
+                              const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                              const float* scale, float eps, int64_t tokens, int32_t nq,
+                              int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
+                              int dtype, const int64_t* slot_mapping, int64_t num_slots,
+                              uint8_t* q_out, uint8_t* kv_cache, void* stream);
 
 /*
  * The separated local tail, kept as the measured baseline of the fused ops and

@@ -15,7 +15,7 @@ import os
 import torch  # loads the HIP runtime the library binds to
 
 __all__ = ["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4", "qk_norm_rope_fp8",
-           "add_rmsnorm", "quant_fp8", "quant_nvfp4",
+           "qk_norm_rope_fp8_kv_store", "add_rmsnorm", "quant_fp8", "quant_nvfp4",
            "nvfp4_shape", "status_string", "lib", "AnqError", "LIB_PATH",
            "ANQ_F16", "ANQ_BF16", "STATUS"]
 
@@ -35,6 +35,8 @@ _SIGS = {
     "add_rmsnorm_quant_nvfp4": [_P, _P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P, _P, _P],
     "qk_norm_rope_fp8": [_P, _P, _P, _P, _P, _I64, _P, _F, _I64, _I32, _I32, _I32, _I32, _I32,
                          ctypes.c_int, _P, _P],
+    "qk_norm_rope_fp8_kv_store": [_P, _P, _P, _P, _P, _I64, _P, _F, _I64, _I32, _I32, _I32, _I32,
+                                  _I32, ctypes.c_int, _P, _I64, _P, _P, _P],
     "add_rmsnorm": [_P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P],
     "quant_fp8": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P],
     "quant_nvfp4": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P],
@@ -196,6 +198,43 @@ def qk_norm_rope_fp8(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: floa
     if st:
         raise AnqError("qk_norm_rope_fp8", st)
     return out
+
+
+def qk_norm_rope_fp8_kv_store(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: float,
+                              nq: int, nk: int, nv: int, head_dim: int, slot_mapping, kv_cache,
+                              rotary_dim: int | None = None, q_out=None, stream=None):
+    """qk_norm_rope_fp8 with the KV-cache store epilogue: Q codes to q_out
+    [.., nq*head_dim]; token t's K and V codes to kv_cache[slot_mapping[t]]
+    (a [num_slots, (nk+nv)*head_dim] uint8 pool, updated in place; slots
+    outside [0, num_slots) store nothing). Returns q_out."""
+    dev = _check_gpu(qkv, gamma_q, gamma_k, positions, cos_sin, scale, slot_mapping, kv_cache,
+                     q_out)
+    _scalar(scale, "scale")
+    if positions.dtype != torch.int64 or cos_sin.dtype != torch.float32:
+        raise ValueError("positions must be int64 and cos_sin float32")
+    if slot_mapping.dtype != torch.int64 or kv_cache.dtype != torch.uint8:
+        raise ValueError("slot_mapping must be int64 and kv_cache uint8")
+    cols = (nq + nk + nv) * head_dim
+    if qkv.shape[-1] != cols:
+        raise ValueError(f"qkv last dim {qkv.shape[-1]} != (nq+nk+nv)*head_dim = {cols}")
+    kv_cols = (nk + nv) * head_dim
+    if kv_cache.dim() < 1 or (kv_cols and kv_cache.numel() % kv_cols):
+        raise ValueError("kv_cache must hold whole rows of (nk+nv)*head_dim bytes")
+    num_slots = kv_cache.numel() // kv_cols if kv_cols else 0
+    tokens = qkv.numel() // cols if cols else 0
+    if slot_mapping.numel() != tokens:
+        raise ValueError("slot_mapping must hold one slot per token")
+    if q_out is None:
+        q_out = torch.empty(*qkv.shape[:-1], nq * head_dim, dtype=torch.uint8, device=dev)
+    st = lib().qk_norm_rope_fp8_kv_store(
+        _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), _ptr(positions), _ptr(cos_sin), cos_sin.shape[0],
+        _ptr(scale), eps, tokens, nq, nk, nv, head_dim,
+        head_dim if rotary_dim is None else rotary_dim, _dtype_code(qkv), _ptr(slot_mapping),
+        num_slots, _ptr(q_out) if q_out.numel() else None, _ptr(kv_cache) if kv_cache.numel() else None,
+        _stream(dev, stream))
+    if st:
+        raise AnqError("qk_norm_rope_fp8_kv_store", st)
+    return q_out
 
 
 # ------------------------------------------------------------ separated tail

@@ -123,40 +123,61 @@ extern "C" int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void
                                         static_cast<hipStream_t>(stream)));
 }
 
-extern "C" int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
-                                const int64_t* positions, const float* cos_sin, int64_t max_pos,
-                                const float* scale, float eps, int64_t tokens, int32_t nq,
-                                int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
-                                int dtype, uint8_t* out, void* stream) {
-  if (!cos_sin || !scale || (tokens != 0 && (!qkv || !positions || !out))) return ANQ_ERR_NULL;
+namespace {
+
+// Checks shared by the two Q/K entry points. q_cols is the width of `out` in
+// bytes per token (all heads, or the Q heads with a KV store); kv_bytes the
+// pool size (0 without a store).
+int check_qk(const void* qkv, const void* gamma_q, const void* gamma_k, const int64_t* positions,
+             const float* cos_sin, int64_t max_pos, const float* scale, float eps, int64_t tokens,
+             int32_t nq, int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim, int dtype,
+             const uint8_t* out, bool kv_store, const int64_t* slots, int64_t num_slots,
+             const uint8_t* kv) {
+  const bool need_out = !kv_store || nq > 0;
+  const bool need_kv = kv_store && nk + nv > 0;
+  if (!cos_sin || !scale ||
+      (tokens != 0 && (!qkv || !positions || (need_out && !out) || (need_kv && (!slots || !kv)))))
+    return ANQ_ERR_NULL;
   if (nq > 0 && !gamma_q) return ANQ_ERR_NULL;
   if (nk > 0 && !gamma_k) return ANQ_ERR_NULL;
   if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
-  if (nq < 0 || nk < 0 || nv < 0 || max_pos < 1) return ANQ_ERR_VALUE;
+  if (nq < 0 || nk < 0 || nv < 0 || max_pos < 1 || (kv_store && num_slots < 0))
+    return ANQ_ERR_VALUE;
   if (tokens < 0 || head_dim <= 0 || nq + nk + nv == 0) return ANQ_ERR_SHAPE;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
     return ANQ_ERR_UNSUPPORTED;
   if (rotary_dim != head_dim) return ANQ_ERR_UNSUPPORTED;
   if (!valid_eps(eps)) return ANQ_ERR_VALUE;
   const int64_t cols = (int64_t)(nq + nk + nv) * head_dim;
-  if (tokens > INT64_MAX / (2 * cols) || max_pos > INT64_MAX / (4 * (int64_t)head_dim))
+  if (tokens > INT64_MAX / (2 * cols) || max_pos > INT64_MAX / (4 * (int64_t)head_dim) ||
+      (kv_store && num_slots > INT64_MAX / cols))
     return ANQ_ERR_SHAPE;
   if (!aligned(qkv, 16) || !aligned(out, 16) || !aligned(cos_sin, 16) || !aligned(positions, 8) ||
-      !aligned(scale, 4) || (nq > 0 && !aligned(gamma_q, 16)) || (nk > 0 && !aligned(gamma_k, 16)))
+      !aligned(scale, 4) || (nq > 0 && !aligned(gamma_q, 16)) || (nk > 0 && !aligned(gamma_k, 16)) ||
+      (kv_store && (!aligned(kv, 16) || !aligned(slots, 8))))
     return ANQ_ERR_ALIGN;
-  const Span outs[1] = {span(out, tokens * cols)};
-  const Span ins[6] = {span(qkv, tokens * cols * 2), span(nq ? gamma_q : nullptr, nq ? head_dim * 2 : 0),
+  const int64_t out_cols = kv_store ? (int64_t)nq * head_dim : cols;
+  const int64_t kv_bytes = need_kv ? num_slots * (int64_t)(nk + nv) * head_dim : 0;
+  const Span outs[2] = {span(out, tokens * out_cols), span(kv, kv_bytes)};
+  const Span ins[7] = {span(qkv, tokens * cols * 2), span(nq ? gamma_q : nullptr, nq ? head_dim * 2 : 0),
                        span(nk ? gamma_k : nullptr, nk ? head_dim * 2 : 0), span(positions, tokens * 8),
-                       span(cos_sin, max_pos * head_dim * 4), span(scale, 4)};
-  if (any_alias(outs, 1, ins, 6)) return ANQ_ERR_ALIAS;
-  if (tokens == 0) return ANQ_OK;
+                       span(cos_sin, max_pos * head_dim * 4), span(scale, 4),
+                       span(need_kv ? slots : nullptr, need_kv ? tokens * 8 : 0)};
+  if (any_alias(outs, 2, ins, 7)) return ANQ_ERR_ALIAS;
+  return ANQ_OK;
+}
 
+anq::QKParams qk_params(const void* qkv, const void* gamma_q, const void* gamma_k,
+                        const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                        const float* scale, float eps, int64_t tokens, int32_t nq, int32_t nk,
+                        int32_t nv, int32_t head_dim, uint8_t* out) {
   anq::QKParams p{};
   p.qkv = qkv;
   p.gamma_q = gamma_q;
   p.gamma_k = gamma_k;
   p.positions = positions;
   p.cos_sin = cos_sin;
+  p.max_pos = max_pos;
   p.scale = scale;
   p.out = out;
   p.eps = eps;
@@ -166,7 +187,41 @@ extern "C" int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void
   p.nk = nk;
   p.nv = nv;
   p.head_dim = head_dim;
-  return launch_status(anq::launch_qk(dtype, p, static_cast<hipStream_t>(stream)));
+  return p;
+}
+
+}  // namespace
+
+extern "C" int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
+                                const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                const float* scale, float eps, int64_t tokens, int32_t nq,
+                                int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
+                                int dtype, uint8_t* out, void* stream) {
+  const int st = check_qk(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens, nq,
+                          nk, nv, head_dim, rotary_dim, dtype, out, false, nullptr, 0, nullptr);
+  if (st != ANQ_OK || tokens == 0) return st;
+  const anq::QKParams p = qk_params(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps,
+                                    tokens, nq, nk, nv, head_dim, out);
+  return launch_status(anq::launch_qk(dtype, false, p, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int qk_norm_rope_fp8_kv_store(const void* qkv, const void* gamma_q, const void* gamma_k,
+                                         const int64_t* positions, const float* cos_sin,
+                                         int64_t max_pos, const float* scale, float eps,
+                                         int64_t tokens, int32_t nq, int32_t nk, int32_t nv,
+                                         int32_t head_dim, int32_t rotary_dim, int dtype,
+                                         const int64_t* slot_mapping, int64_t num_slots,
+                                         uint8_t* q_out, uint8_t* kv_cache, void* stream) {
+  const int st = check_qk(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens, nq,
+                          nk, nv, head_dim, rotary_dim, dtype, q_out, true, slot_mapping, num_slots,
+                          kv_cache);
+  if (st != ANQ_OK || tokens == 0) return st;
+  anq::QKParams p = qk_params(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens,
+                              nq, nk, nv, head_dim, q_out);
+  p.kv = kv_cache;
+  p.slots = slot_mapping;
+  p.num_slots = nk + nv > 0 ? num_slots : 0;
+  return launch_status(anq::launch_qk(dtype, true, p, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int add_rmsnorm(const void* x, void* residual, const void* gamma, float eps,
@@ -257,7 +312,7 @@ extern "C" const char* anq_status_string(int status) {
     case ANQ_ERR_ALIAS: return "output buffers overlap another buffer";
     case ANQ_ERR_UNSUPPORTED: return "unsupported case (hidden > 65536, head_dim not in {32..512}, rotary_dim != head_dim): use a separated path";
     case ANQ_ERR_LAUNCH: return "HIP kernel launch failed";
-    case ANQ_ERR_VALUE: return "bad scalar argument (eps < 0 or not finite, max_pos < 1, negative head count)";
+    case ANQ_ERR_VALUE: return "bad scalar argument (eps < 0 or not finite, max_pos < 1, negative head count or num_slots)";
     default: return "unknown status";
   }
 }

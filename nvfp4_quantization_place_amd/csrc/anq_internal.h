@@ -49,7 +49,11 @@ struct QKParams {
   const int64_t* positions;
   const float* cos_sin;
   const float* scale;
-  uint8_t* out;
+  uint8_t* out;            // [tokens, heads*D]; with a KV store: Q codes [tokens, nq*D]
+  uint8_t* kv;             // KV store only: [num_slots, (nk+nv)*D] pool
+  const int64_t* slots;    // KV store only: [tokens] slot of each token (< 0: no store)
+  int64_t num_slots;
+  int64_t max_pos;
   float eps;
   int64_t tokens;
   int64_t pairs;  // tokens * (nq + nk + nv)
@@ -57,7 +61,7 @@ struct QKParams {
   int32_t waves_per_token;  // set by the launcher
 };
 
-hipError_t launch_qk(int dtype, const QKParams& p, hipStream_t stream);
+hipError_t launch_qk(int dtype, bool kv_store, const QKParams& p, hipStream_t stream);
 
 // Standalone quantisation of an activation tensor [tokens, hidden] (the second
 // kernel of the separated tail).

@@ -11,6 +11,12 @@
 // one. A head's sum of squares meets through a DPP butterfly over its
 // D/16 lanes. Q and K heads are normalised, rotated and quantised; V heads
 // are only quantised.
+//
+// STORE selects the KV-store epilogue (the "store" of the norm + RoPE + store
+// kernel in SGLang PR #32975, with its uniform FP8 pool): Q codes go to a
+// dense [tokens, nq*D] buffer, and the token's K and V codes go to its slot of
+// the pool, a row of (nk+nv)*D bytes; a slot outside [0, num_slots) stores
+// nothing.
 #include <stdlib.h>
 
 #include "anq_device.h"
@@ -18,7 +24,7 @@
 
 namespace anq {
 
-template <int DT, int LPH, bool NT>
+template <int DT, int LPH, bool NT, bool STORE>
 __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
   constexpr int D = LPH * 16;
   constexpr int HALF = D / 2;
@@ -36,14 +42,22 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
   const float inv_sc = 1.0f / sc;
   const size_t row_elems = (size_t)heads * D;
   const uint8_t* row = static_cast<const uint8_t*>(p.qkv) + (size_t)t * row_elems * 2;
-  uint8_t* orow = p.out + (size_t)t * row_elems;
+  uint8_t* orow = p.out + (size_t)t * (STORE ? (size_t)p.nq * D : row_elems);
+  uint8_t* kvrow = nullptr;  // KV store: the token's pool row, or none
+  if constexpr (STORE) {
+    if (p.num_slots > 0) {  // 0 also when there are no K/V heads (slots may then be NULL)
+      const int64_t sl = p.slots[t];
+      if (sl >= 0 && sl < p.num_slots) kvrow = p.kv + (size_t)sl * (size_t)(heads - p.nq) * D;
+    }
+  }
   const uint32_t oa_off = 8 * j, ob_off = HALF + 8 * j;  // element offsets inside a head
 
   // per-token constants: the lane's cos|sin values and gamma slices
   float c[8], s[8];
   U4 gqa{}, gqb{}, gka{}, gkb{};
   if (qk_heads > 0) {
-    const int64_t pos = p.positions[t];
+    int64_t pos = p.positions[t];
+    pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);  // never read outside the table
     const float* cs = p.cos_sin + (size_t)pos * D;
     const float4 c0 = *reinterpret_cast<const float4*>(cs + oa_off);
     const float4 c1 = *reinterpret_cast<const float4*>(cs + oa_off + 4);
@@ -128,28 +142,32 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
     const uint32_t b0 = e4m3x4(ob[0], ob[1], ob[2], ob[3]), b1 = e4m3x4(ob[4], ob[5], ob[6], ob[7]);
     const bool odd = (j & 1) != 0;
     const uint32_t r0 = dpp_u32<0xB1>(odd ? a0 : b0), r1 = dpp_u32<0xB1>(odd ? a1 : b1);
-    if (h < heads) {
+    uint8_t* dst = orow + (size_t)h * D;
+    if constexpr (STORE) {
+      if (h >= p.nq) dst = kvrow ? kvrow + (size_t)(h - p.nq) * D : nullptr;
+    }
+    if (h < heads && dst) {
       U4 v;
       v.w[0] = odd ? r0 : a0;
       v.w[1] = odd ? r1 : a1;
       v.w[2] = odd ? b0 : r0;
       v.w[3] = odd ? b1 : r1;
-      st16s<NT>(orow + (size_t)h * D + (odd ? HALF + 8 * (j - 1) : 8 * j), v);
+      st16s<NT>(dst + (odd ? HALF + 8 * (j - 1) : 8 * j), v);
     }
   }
 }
 
-template <int DT, bool NT>
+template <int DT, bool NT, bool STORE>
 static hipError_t launch_qk_nt(const QKParams& p, hipStream_t s) {
   void* args[] = {const_cast<QKParams*>(&p)};
   const void* fn = nullptr;
   const int lph = p.head_dim / 16;
   switch (lph) {
-    case 2: fn = (const void*)&qk_kernel<DT, 2, NT>; break;
-    case 4: fn = (const void*)&qk_kernel<DT, 4, NT>; break;
-    case 8: fn = (const void*)&qk_kernel<DT, 8, NT>; break;
-    case 16: fn = (const void*)&qk_kernel<DT, 16, NT>; break;
-    case 32: fn = (const void*)&qk_kernel<DT, 32, NT>; break;
+    case 2: fn = (const void*)&qk_kernel<DT, 2, NT, STORE>; break;
+    case 4: fn = (const void*)&qk_kernel<DT, 4, NT, STORE>; break;
+    case 8: fn = (const void*)&qk_kernel<DT, 8, NT, STORE>; break;
+    case 16: fn = (const void*)&qk_kernel<DT, 16, NT, STORE>; break;
+    case 32: fn = (const void*)&qk_kernel<DT, 32, NT, STORE>; break;
     default: return hipErrorInvalidConfiguration;
   }
   const int block = 256;  // four wavefronts
@@ -159,7 +177,7 @@ static hipError_t launch_qk_nt(const QKParams& p, hipStream_t s) {
 }
 
 // Streaming hints (see ld16s) once qkv alone is >= 32 MiB; ANQ_STREAM=0/1 overrides.
-template <int DT>
+template <int DT, bool STORE>
 static hipError_t launch_qk_dt(QKParams p, hipStream_t s) {
   // wavefronts per token: enough head groups in flight at once that the
   // per-token chain of loads stays short (ANQ_QK_WAVES overrides, for sweeps)
@@ -173,11 +191,13 @@ static hipError_t launch_qk_dt(QKParams p, hipStream_t s) {
   if (const char* e = getenv("ANQ_STREAM")) {
     if (*e) stream = atoi(e) != 0;
   }
-  return stream ? launch_qk_nt<DT, true>(p, s) : launch_qk_nt<DT, false>(p, s);
+  return stream ? launch_qk_nt<DT, true, STORE>(p, s) : launch_qk_nt<DT, false, STORE>(p, s);
 }
 
-hipError_t launch_qk(int dtype, const QKParams& p, hipStream_t s) {
-  return dtype == kBF16 ? launch_qk_dt<kBF16>(p, s) : launch_qk_dt<kF16>(p, s);
+hipError_t launch_qk(int dtype, bool kv_store, const QKParams& p, hipStream_t s) {
+  if (kv_store)
+    return dtype == kBF16 ? launch_qk_dt<kBF16, true>(p, s) : launch_qk_dt<kF16, true>(p, s);
+  return dtype == kBF16 ? launch_qk_dt<kBF16, false>(p, s) : launch_qk_dt<kF16, false>(p, s);
 }
 
 }  // namespace anq

@@ -220,3 +220,24 @@ def qk_norm_rope_fp8(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin, s
         o_all[:, nq + nk:] = v
         out[:, nq + nk:] = e4m3_encode(v / F32(scale))
     return dict(out=out.reshape(tokens, heads * D), o=o_all.reshape(tokens, heads * D))
+
+
+def qk_norm_rope_fp8_kv_store(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin,
+                              scale: float, eps: float, nq: int, nk: int, nv: int, head_dim: int,
+                              dtype: str, slot_mapping, kv_cache) -> dict:
+    """The Q/K op with the KV-cache store as its epilogue (SGLang PR #32975:
+    norm + RoPE + store into a uniform FP8 pool).
+
+    The codes are those of qk_norm_rope_fp8. Q codes come back dense
+    [tokens, nq*D]; token t's K then V codes overwrite row slot_mapping[t] of a
+    copy of kv_cache [num_slots, (nk+nv)*D]; a slot outside [0, num_slots)
+    stores nothing, and rows no token names keep their contents."""
+    D = head_dim
+    codes = qk_norm_rope_fp8(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin, scale, eps,
+                             nq, nk, nv, D, dtype)["out"]
+    kv = np.array(kv_cache, dtype=np.uint8, copy=True)
+    num_slots = kv.shape[0]
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if 0 <= slot < num_slots:
+            kv[slot] = codes[t, nq * D:]
+    return dict(q=codes[:, :nq * D].copy(), kv=kv)

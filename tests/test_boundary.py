@@ -40,7 +40,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4",
-                                           "qk_norm_rope_fp8", "add_rmsnorm", "quant_fp8",
+                                           "qk_norm_rope_fp8", "qk_norm_rope_fp8_kv_store",
+                                           "add_rmsnorm", "quant_fp8",
                                            "quant_nvfp4", "anq_nvfp4_shape",
                                            "anq_status_string"])
 
@@ -164,6 +165,34 @@ def test_qk_validation(L):
     assert qk(L, tokens=4, out=addr(0)) == ALIAS        # rejected before any HIP call
     assert qk(L, tokens=4, cs=addr(6)) == ALIAS
     assert qk(L, tokens=4, pos=addr(6, 8)) == ALIAS
+
+
+def qks(L, **kw):
+    a = dict(qkv=addr(0), gq=addr(1), gk=addr(2), pos=addr(3), cs=addr(4), max_pos=4096,
+             scale=addr(5), eps=1e-6, tokens=0, nq=16, nk=8, nv=8, D=128, rot=128, dtype=1,
+             slots=addr(8), num_slots=1024, q=addr(6), kv=addr(9), stream=None)
+    a.update(kw)
+    return L.qk_norm_rope_fp8_kv_store(a["qkv"], a["gq"], a["gk"], a["pos"], a["cs"], a["max_pos"],
+                                       a["scale"], a["eps"], a["tokens"], a["nq"], a["nk"], a["nv"],
+                                       a["D"], a["rot"], a["dtype"], a["slots"], a["num_slots"],
+                                       a["q"], a["kv"], a["stream"])
+
+
+def test_qk_kv_store_validation(L):
+    assert qks(L) == OK
+    for k in ("qkv", "pos", "q", "slots", "kv"):
+        assert qks(L, tokens=4, **{k: None}) == NULL, k
+        assert qks(L, tokens=0, **{k: None}) == OK, k
+    assert qks(L, nq=0, q=None, gq=None) == OK           # no Q heads: q_out unused
+    assert qks(L, nk=0, nv=0, slots=None, kv=None) == OK  # no K/V heads: no pool
+    assert qks(L, num_slots=-1) == VALUE
+    assert qks(L, rot=64) == UNSUP
+    assert qks(L, kv=addr(9, 8)) == ALIGN
+    assert qks(L, slots=addr(8, 4)) == ALIGN
+    assert qks(L, tokens=4, kv=addr(0)) == ALIAS         # pool over qkv
+    assert qks(L, tokens=4, kv=addr(6)) == ALIAS         # pool over q_out
+    assert qks(L, tokens=4, slots=addr(9)) == ALIAS      # slots inside the pool
+    assert qks(L, tokens=4, num_slots=1 << 62) == SHAPE  # pool size overflow
 
 
 def addnorm(L, **kw):

@@ -331,6 +331,33 @@ def test_qk_heads_match_per_head_composition():
             assert np.array_equal(out[t, hd * D:(hd + 1) * D], want), (t, hd)
 
 
+def test_qk_kv_store_is_a_scatter_of_the_plain_op():
+    """The store epilogue moves the plain op's codes and nothing else: with the
+    identity mapping the pool is the K|V columns of the plain output; with a
+    permutation row perm[t] holds token t's K|V codes; a padding slot (-1) or
+    one past the pool stores nothing, and rows no token names keep their bytes."""
+    import workloads as W
+    inp = W.make_qk(8, "f16", tokens=6, nq=2, nk=1, nv=2, head_dim=32)
+    D, nq, kvw = 32, 2, 3 * 32
+    args = (W.bits(inp.qkv), W.bits(inp.gamma_q), W.bits(inp.gamma_k), inp.positions.numpy(),
+            inp.cos_sin, inp.scale, inp.eps, nq, 1, 2, D, "f16")
+    plain = O.qk_norm_rope_fp8(*args)["out"]
+    r = O.qk_norm_rope_fp8_kv_store(*args, np.arange(6), np.zeros((6, kvw), np.uint8))
+    assert np.array_equal(r["q"], plain[:, :nq * D]) and np.array_equal(r["kv"], plain[:, nq * D:])
+    perm = np.array([4, 0, 5, 2, 1, 3])
+    r = O.qk_norm_rope_fp8_kv_store(*args, perm, np.zeros((6, kvw), np.uint8))
+    for t in range(6):
+        assert np.array_equal(r["kv"][perm[t]], plain[t, nq * D:])
+    pool = np.full((9, kvw), 0xAB, np.uint8)
+    slots = np.array([7, -1, 0, 9, 3, -5])
+    r = O.qk_norm_rope_fp8_kv_store(*args, slots, pool)
+    written = {7: 0, 0: 2, 3: 4}
+    for row in range(9):
+        want = plain[written[row], nq * D:] if row in written else pool[row]
+        assert np.array_equal(r["kv"][row], want), row
+    assert np.all(pool == 0xAB)                      # the input pool is not modified
+
+
 # ------------------------------------------------- planted mistakes fail ---
 
 def test_pins_catch_planted_mistakes(monkeypatch):
