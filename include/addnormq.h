@@ -68,8 +68,8 @@
  *    every other buffer of the call; x must be disjoint from residual; the
  *    read-only inputs may overlap each other. Violations return ANQ_ERR_ALIAS.
  *  - 16-byte alignment is required for x, residual, gamma, norm_out, q and
- *    qkv/out/cos_sin/q_out/kv_cache; 4 bytes for scalars; 8 for positions and
- *    slot_mapping; sf has none.
+ *    qkv/out/cos_sin/q_out/kv_cache; 4 bytes for scalars and swizzled sf; 8 for
+ *    positions and slot_mapping; linear sf has none.
  *  - Left to the caller (not checked): finite inputs, a positive normal
  *    binary32 scale (s or G, so that 1/s is finite), 0 <= positions[t] < max_pos,
  *    distinct KV slots. Breaking them gives unspecified codes, never an
@@ -220,6 +220,36 @@ int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden
  */
 int quant_nvfp4(const void* in, const float* global_scale, int64_t tokens, int64_t hidden,
                 int dtype, uint8_t* q, uint8_t* sf, void* stream);
+
+/*
+ * NVFP4 with the block scales in the swizzled layout a block-scaled GEMM reads
+ * (the fused ops feed "prequant GEMM" consumers, TensorRT-LLM PR #14361,
+ * Changes table; its review thread names the sf_size packing math of that
+ * layout). The pages do not spell the layout out; it is the 128x4-tiled
+ * scale layout of NVFP4 GEMM operands:
+ *   rows padded to R = roundup(tokens, 128), scale columns to C = roundup(hidden/16, 4);
+ *   the scale of (row r, block column c) is at byte
+ *     ((r / 128) * (C / 4) + c / 4) * 512 + (r % 32) * 16 + ((r / 32) % 4) * 4 + c % 4.
+ * Every padding byte (rows >= tokens, columns >= hidden/16) is written as 0.
+ * sf holds R * C bytes and must be 4-byte aligned. Codes, q, residual and
+ * norm_out are exactly those of the linear-layout op.
+ */
+int add_rmsnorm_quant_nvfp4_swizzled(const void* x, void* residual, const void* gamma,
+                                     const float* global_scale, float eps, int64_t tokens,
+                                     int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
+                                     void* norm_out, void* stream);
+
+/* quant_nvfp4 with the swizzled block-scale layout above. */
+int quant_nvfp4_swizzled(const void* in, const float* global_scale, int64_t tokens,
+                         int64_t hidden, int dtype, uint8_t* q, uint8_t* sf, void* stream);
+
+/*
+ * Padded shape [sf_rows, sf_cols] of the swizzled block-scale buffer:
+ * sf_rows = roundup(tokens, 128), sf_cols = roundup(hidden/16, 4).
+ * Host only. Returns ANQ_OK, or ANQ_ERR_NULL / ANQ_ERR_SHAPE.
+ */
+int anq_nvfp4_swizzled_sf_shape(int64_t tokens, int64_t hidden, int64_t* sf_rows,
+                                int64_t* sf_cols);
 
 /*
  * The one place that states the NVFP4 output shapes (the review thread of

@@ -15,7 +15,8 @@ import os
 import torch  # loads the HIP runtime the library binds to
 
 __all__ = ["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4", "qk_norm_rope_fp8",
-           "qk_norm_rope_fp8_kv_store", "add_rmsnorm", "quant_fp8", "quant_nvfp4",
+           "qk_norm_rope_fp8_kv_store", "add_rmsnorm_quant_nvfp4_swizzled",
+           "quant_nvfp4_swizzled", "nvfp4_swizzled_sf_shape", "add_rmsnorm", "quant_fp8", "quant_nvfp4",
            "nvfp4_shape", "status_string", "lib", "AnqError", "LIB_PATH",
            "ANQ_F16", "ANQ_BF16", "STATUS"]
 
@@ -40,6 +41,10 @@ _SIGS = {
     "add_rmsnorm": [_P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P],
     "quant_fp8": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P],
     "quant_nvfp4": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P],
+    "add_rmsnorm_quant_nvfp4_swizzled": [_P, _P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P, _P,
+                                         _P],
+    "quant_nvfp4_swizzled": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P],
+    "anq_nvfp4_swizzled_sf_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "anq_nvfp4_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "anq_status_string": [ctypes.c_int],
 }
@@ -80,6 +85,16 @@ def nvfp4_shape(tokens: int, hidden: int) -> tuple[int, int]:
     if st:
         raise AnqError("anq_nvfp4_shape", st)
     return q.value, s.value
+
+
+def nvfp4_swizzled_sf_shape(tokens: int, hidden: int) -> tuple[int, int]:
+    """(rows, cols) of the swizzled block-scale buffer: tokens padded to 128,
+    hidden/16 padded to 4."""
+    r, c = _I64(), _I64()
+    st = lib().anq_nvfp4_swizzled_sf_shape(tokens, hidden, ctypes.byref(r), ctypes.byref(c))
+    if st:
+        raise AnqError("anq_nvfp4_swizzled_sf_shape", st)
+    return r.value, c.value
 
 
 _DT = {torch.float16: ANQ_F16, torch.bfloat16: ANQ_BF16}
@@ -284,4 +299,52 @@ def quant_nvfp4(t, global_scale, q=None, sf=None, stream=None):
                            _ptr(sf), _stream(dev, stream))
     if st:
         raise AnqError("quant_nvfp4", st)
+    return q, sf
+
+
+# ------------------------------------------------------------ swizzled block scales
+
+
+def _swizzled_sf(t, dev, sf, tokens, hidden):
+    if sf is None and hidden > 0 and hidden % 16 == 0:
+        r, c = nvfp4_swizzled_sf_shape(tokens, hidden)
+        sf = torch.empty(r, c, dtype=torch.uint8, device=dev)
+    return sf if sf is not None else torch.empty(1, dtype=torch.uint8, device=dev)
+
+
+def add_rmsnorm_quant_nvfp4_swizzled(x, residual, gamma, global_scale, eps: float,
+                                     norm_out: bool = False, q=None, sf=None, norm=None,
+                                     stream=None):
+    """add_rmsnorm_quant_nvfp4 with the block scales in the 128x4-tiled GEMM
+    layout: sf [roundup(tokens,128), roundup(hidden/16,4)] uint8, padding zeroed."""
+    dev = _check_gpu(x, residual, gamma, global_scale, q, sf, norm)
+    _scalar(global_scale, "global_scale")
+    tokens, hidden = _rows(x)
+    if residual.dtype != x.dtype or gamma.dtype != x.dtype or residual.shape != x.shape:
+        raise ValueError("x, residual and gamma must share the dtype; x and residual the shape")
+    if q is None:
+        q = torch.empty(*x.shape[:-1], max(hidden // 2, 1), dtype=torch.uint8, device=dev)
+    sf = _swizzled_sf(x, dev, sf, tokens, hidden)
+    if norm_out and norm is None:
+        norm = torch.empty_like(x)
+    st = lib().add_rmsnorm_quant_nvfp4_swizzled(
+        _ptr(x), _ptr(residual), _ptr(gamma), _ptr(global_scale), eps, tokens, hidden,
+        _dtype_code(x), _ptr(q), _ptr(sf), _ptr(norm), _stream(dev, stream))
+    if st:
+        raise AnqError("add_rmsnorm_quant_nvfp4_swizzled", st)
+    return q, sf, norm
+
+
+def quant_nvfp4_swizzled(t, global_scale, q=None, sf=None, stream=None):
+    """quant_nvfp4 with the swizzled block-scale layout."""
+    dev = _check_gpu(t, global_scale, q, sf)
+    _scalar(global_scale, "global_scale")
+    tokens, hidden = _rows(t)
+    if q is None:
+        q = torch.empty(*t.shape[:-1], max(hidden // 2, 1), dtype=torch.uint8, device=dev)
+    sf = _swizzled_sf(t, dev, sf, tokens, hidden)
+    st = lib().quant_nvfp4_swizzled(_ptr(t), _ptr(global_scale), tokens, hidden, _dtype_code(t),
+                                    _ptr(q), _ptr(sf), _stream(dev, stream))
+    if st:
+        raise AnqError("quant_nvfp4_swizzled", st)
     return q, sf

@@ -90,17 +90,27 @@ extern "C" int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* 
                                         static_cast<hipStream_t>(stream)));
 }
 
-extern "C" int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
-                                       const float* global_scale, float eps, int64_t tokens,
-                                       int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
-                                       void* norm_out, void* stream) {
+namespace {
+
+int64_t sf_tiles_of(int64_t hidden) { return (hidden / 16 + 3) / 4; }
+
+int64_t sf_bytes(int64_t tokens, int64_t hidden, bool swizzled) {
+  if (!swizzled) return tokens * (hidden / 16);
+  return ((tokens + 127) / 128) * 128 * sf_tiles_of(hidden) * 4;
+}
+
+int rmsnorm_nvfp4(const void* x, void* residual, const void* gamma, const float* global_scale,
+                  float eps, int64_t tokens, int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
+                  void* norm_out, bool swizzled, void* stream) {
   if (!sf && tokens != 0) return ANQ_ERR_NULL;
   int64_t act = 0;
   int st = check_tail(x, residual, gamma, global_scale, eps, tokens, hidden, dtype, q, norm_out,
                       &act);
   if (st != ANQ_OK) return st;
+  if (swizzled && !aligned(sf, 4)) return ANQ_ERR_ALIGN;
   const Span outs[4] = {span(residual, act), span(q, tokens * (hidden / 2)),
-                        span(sf, tokens * (hidden / 16)), span(norm_out, norm_out ? act : 0)};
+                        span(sf, sf_bytes(tokens, hidden, swizzled)),
+                        span(norm_out, norm_out ? act : 0)};
   const Span ins[3] = {span(x, act), span(gamma, hidden * 2), span(global_scale, 4)};
   if (any_alias(outs, 4, ins, 3)) return ANQ_ERR_ALIAS;
   if (tokens == 0) return ANQ_OK;
@@ -117,10 +127,30 @@ extern "C" int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void
   p.tokens = tokens;
   p.hidden = (int32_t)hidden;
   p.vec = (int32_t)(hidden / 8);
+  p.sf_tiles = swizzled ? (int32_t)sf_tiles_of(hidden) : 0;
   const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
   p.rows_per_group = t.rows;
   return launch_status(anq::launch_tail(dtype, anq::kEpiNvfp4, norm_out != nullptr, p, t,
                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
+                                       const float* global_scale, float eps, int64_t tokens,
+                                       int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
+                                       void* norm_out, void* stream) {
+  return rmsnorm_nvfp4(x, residual, gamma, global_scale, eps, tokens, hidden, dtype, q, sf,
+                       norm_out, false, stream);
+}
+
+extern "C" int add_rmsnorm_quant_nvfp4_swizzled(const void* x, void* residual, const void* gamma,
+                                                const float* global_scale, float eps,
+                                                int64_t tokens, int64_t hidden, int dtype,
+                                                uint8_t* q, uint8_t* sf, void* norm_out,
+                                                void* stream) {
+  return rmsnorm_nvfp4(x, residual, gamma, global_scale, eps, tokens, hidden, dtype, q, sf,
+                       norm_out, true, stream);
 }
 
 namespace {
@@ -261,14 +291,15 @@ extern "C" int add_rmsnorm(const void* x, void* residual, const void* gamma, flo
 namespace {
 
 int quant_common(const void* in, const float* scale, int64_t tokens, int64_t hidden, int dtype,
-                 uint8_t* q, uint8_t* sf, bool nvfp4, void* stream) {
+                 uint8_t* q, uint8_t* sf, bool nvfp4, bool swizzled, void* stream) {
   if (!scale || (tokens != 0 && (!in || !q || (nvfp4 && !sf)))) return ANQ_ERR_NULL;
   if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
   if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
   if (tokens > INT64_MAX / (2 * hidden)) return ANQ_ERR_SHAPE;
-  if (!aligned(in, 16) || !aligned(q, 16) || !aligned(scale, 4)) return ANQ_ERR_ALIGN;
+  if (!aligned(in, 16) || !aligned(q, 16) || !aligned(scale, 4) || (swizzled && !aligned(sf, 4)))
+    return ANQ_ERR_ALIGN;
   const int64_t n = tokens * hidden;
-  const Span outs[2] = {span(q, nvfp4 ? n / 2 : n), span(sf, nvfp4 ? n / 16 : 0)};
+  const Span outs[2] = {span(q, nvfp4 ? n / 2 : n), span(sf, nvfp4 ? sf_bytes(tokens, hidden, swizzled) : 0)};
   const Span ins[2] = {span(in, n * 2), span(scale, 4)};
   if (any_alias(outs, 2, ins, 2)) return ANQ_ERR_ALIAS;
   if (tokens == 0) return ANQ_OK;
@@ -278,6 +309,10 @@ int quant_common(const void* in, const float* scale, int64_t tokens, int64_t hid
   p.q = q;
   p.sf = sf;
   p.vecs = n / 8;
+  p.tokens = tokens;
+  p.vec = (int32_t)(hidden / 8);
+  p.sf_tiles = swizzled ? (int32_t)sf_tiles_of(hidden) : 0;
+  p.pad_rows = swizzled ? ((tokens + 127) / 128) * 128 - tokens : 0;
   return launch_status(anq::launch_quant(dtype, nvfp4 ? anq::kEpiNvfp4 : anq::kEpiFp8, p,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -286,12 +321,18 @@ int quant_common(const void* in, const float* scale, int64_t tokens, int64_t hid
 
 extern "C" int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden,
                          int dtype, uint8_t* q, void* stream) {
-  return quant_common(in, scale, tokens, hidden, dtype, q, nullptr, false, stream);
+  return quant_common(in, scale, tokens, hidden, dtype, q, nullptr, false, false, stream);
 }
 
 extern "C" int quant_nvfp4(const void* in, const float* global_scale, int64_t tokens,
                            int64_t hidden, int dtype, uint8_t* q, uint8_t* sf, void* stream) {
-  return quant_common(in, global_scale, tokens, hidden, dtype, q, sf, true, stream);
+  return quant_common(in, global_scale, tokens, hidden, dtype, q, sf, true, false, stream);
+}
+
+extern "C" int quant_nvfp4_swizzled(const void* in, const float* global_scale, int64_t tokens,
+                                    int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
+                                    void* stream) {
+  return quant_common(in, global_scale, tokens, hidden, dtype, q, sf, true, true, stream);
 }
 
 extern "C" int anq_nvfp4_shape(int64_t tokens, int64_t hidden, int64_t* q_cols, int64_t* sf_cols) {
@@ -299,6 +340,16 @@ extern "C" int anq_nvfp4_shape(int64_t tokens, int64_t hidden, int64_t* q_cols, 
   if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
   *q_cols = hidden / 2;
   *sf_cols = hidden / 16;
+  return ANQ_OK;
+}
+
+extern "C" int anq_nvfp4_swizzled_sf_shape(int64_t tokens, int64_t hidden, int64_t* sf_rows,
+                                           int64_t* sf_cols) {
+  if (!sf_rows || !sf_cols) return ANQ_ERR_NULL;
+  if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
+  if (tokens > INT64_MAX - 127) return ANQ_ERR_SHAPE;
+  *sf_rows = (tokens + 127) / 128 * 128;
+  *sf_cols = sf_tiles_of(hidden) * 4;
   return ANQ_OK;
 }
 

@@ -365,4 +365,42 @@ __device__ __forceinline__ void nvfp4_half_block(const float (&n)[8], float G, c
   codes = e2m1x8(t);
 }
 
+// Byte offset of the block scale of row r, block column c in the 128x4-tiled
+// scale layout of block-scaled GEMM operands: rows padded to 128, scale
+// columns to 4; tile (r / 128, c / 4) is 512 contiguous bytes, tiles row-major
+// with `tiles_c` tiles per tile row; inside a tile, (r % 32, (r / 32) % 4, c % 4)
+// with strides 16, 4, 1. The four columns of a tile row are one 4-byte word.
+__device__ __forceinline__ size_t sf_swizzled_offset(int64_t r, int32_t c, int32_t tiles_c) {
+  return ((size_t)(r >> 7) * (size_t)tiles_c + (size_t)(c >> 2)) * 512u + (size_t)(r & 31) * 16u +
+         (size_t)((r >> 5) & 3) * 4u + (size_t)(c & 3);
+}
+
+// Store the block scale of (row, c). Linear layout when tiles_c == 0. In the
+// swizzled layout the owner of a row's last block also zeroes the (at most 3)
+// padding columns of that row's last tile.
+__device__ __forceinline__ void store_block_scale(uint8_t* sf, int64_t row, int32_t c,
+                                                  int32_t nblk, int32_t tiles_c, uint8_t code) {
+  if (tiles_c == 0) {
+    sf[(size_t)row * (size_t)nblk + (size_t)c] = code;
+    return;
+  }
+  const size_t o = sf_swizzled_offset(row, c, tiles_c);
+  sf[o] = code;
+  if (c == nblk - 1) {
+    for (int32_t z = c + 1; z < tiles_c * 4; ++z) sf[o + (size_t)(z - c)] = 0;
+  }
+}
+
+// Zero the scale words of padded rows [tokens, roundup(tokens, 128)) in the
+// swizzled layout: the caller's `worker` of `workers` takes rows tokens + worker,
+// tokens + worker + workers, ...; `lane` of `lanes` takes tile columns.
+__device__ __forceinline__ void zero_padded_scale_rows(uint8_t* sf, int64_t tokens, int32_t tiles_c,
+                                                       int64_t worker, int64_t workers, int lane,
+                                                       int lanes) {
+  const int64_t rows_pad = (tokens + 127) & ~(int64_t)127;
+  for (int64_t r = tokens + worker; r < rows_pad; r += workers)
+    for (int32_t t = lane; t < tiles_c; t += lanes)
+      *reinterpret_cast<uint32_t*>(sf + sf_swizzled_offset(r, 4 * t, tiles_c)) = 0u;
+}
+
 }  // namespace anq

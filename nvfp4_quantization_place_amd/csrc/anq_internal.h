@@ -21,6 +21,7 @@ struct TailParams {
   int32_t hidden;
   int32_t vec;         // hidden / 8: 16-byte vectors per row
   int32_t rows_per_group;  // consecutive rows each lane group processes
+  int32_t sf_tiles;    // NVFP4 scale layout: 0 linear, else 128x4 tiles per tile row
 };
 
 // How a row is spread over lanes: `group` lanes of one wavefront per row
@@ -71,6 +72,10 @@ struct QuantParams {
   uint8_t* q;
   uint8_t* sf;         // NVFP4 only
   int64_t vecs;        // tokens * hidden / 8
+  int64_t tokens;
+  int32_t vec;         // hidden / 8
+  int32_t sf_tiles;    // NVFP4 scale layout: 0 linear, else 128x4 tiles per tile row
+  int64_t pad_rows;    // swizzled: padded rows past tokens (threads past vecs zero them)
 };
 
 hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t stream);

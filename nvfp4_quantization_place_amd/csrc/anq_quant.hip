@@ -9,6 +9,8 @@
 // An NVFP4 block of 16 is two vectors in adjacent lanes; rows are multiples of
 // 16 elements, so flattening [tokens, hidden] keeps every block inside a row.
 // The encoders are the fused kernel's own (fp8_codes8, nvfp4_half_block).
+// With the swizzled scale layout, threads past the last vector zero the
+// scale words of the padded rows (one 4-byte word each).
 #include <stdlib.h>
 
 #include "anq_device.h"
@@ -26,6 +28,15 @@ __global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
     fill_mult_tab(mult_tab, sc);
     __syncthreads();
   }
+  if constexpr (EPI == kEpiNvfp4) {
+    if (v >= p.vecs) {  // threads past the tensor zero the padded scale rows (swizzled layout)
+      const int64_t e = v - p.vecs;
+      if (p.sf_tiles > 0 && e < p.pad_rows * p.sf_tiles)
+        *reinterpret_cast<uint32_t*>(p.sf + sf_swizzled_offset(p.tokens + e / p.sf_tiles,
+                                                               4 * (int32_t)(e % p.sf_tiles),
+                                                               p.sf_tiles)) = 0u;
+    }
+  }
   const bool ok = v < p.vecs;
   const int64_t vv = ok ? v : p.vecs - 1;  // past the end: a clamped load, no store
   float f[8];
@@ -39,7 +50,15 @@ __global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
     nvfp4_half_block(f, sc, mult_tab, w, sfc);
     if (ok) {
       st4s<false>(p.q + (size_t)v * 4, w);
-      if ((v & 1) == 0) st1s<false>(p.sf + (size_t)(v >> 1), (uint8_t)sfc);
+      if ((v & 1) == 0) {
+        if (p.sf_tiles == 0) {  // linear [tokens, hidden/16]: block v/2 of the flat tensor
+          st1s<false>(p.sf + (size_t)(v >> 1), (uint8_t)sfc);
+        } else {
+          const int64_t row = v / p.vec;
+          store_block_scale(p.sf, row, (int32_t)((v - row * p.vec) >> 1), p.vec / 2, p.sf_tiles,
+                            (uint8_t)sfc);
+        }
+      }
     }
   }
 }
@@ -54,7 +73,8 @@ static hipError_t launch_quant_epi(const QuantParams& p, hipStream_t s) {
   }
   const void* fn = stream ? (const void*)&quant_kernel<DT, EPI, true>
                           : (const void*)&quant_kernel<DT, EPI, false>;
-  const int64_t grid = (p.vecs + 255) / 256;
+  const int64_t threads = p.vecs + (EPI == kEpiNvfp4 && p.sf_tiles > 0 ? p.pad_rows * p.sf_tiles : 0);
+  const int64_t grid = (threads + 255) / 256;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s);
 }

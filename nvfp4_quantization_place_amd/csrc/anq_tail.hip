@@ -253,9 +253,16 @@ tail_kernel(TailParams p) {
         if (vok[k]) {
           st4s<false>(row_ptr<G>(p.q, (size_t)row * (p.hidden / 2)) + voff[k] / 4, w);
           if ((lane & 1) == 0)
-            st1s<false>(row_ptr<G>(p.sf, (size_t)row * (p.hidden / 16)) + voff[k] / 32, (uint8_t)sfc);
+            store_block_scale(p.sf, row, (int32_t)(voff[k] / 32), p.hidden / 16, p.sf_tiles,
+                              (uint8_t)sfc);
         }
       }
+    }
+  }
+  if constexpr (EPI == kEpiNvfp4) {
+    if (p.sf_tiles > 0) {  // swizzled layout: lane groups share the padded rows
+      const int64_t groups = G > 0 ? (int64_t)gridDim.x * (blockDim.x / G) : (int64_t)gridDim.x;
+      zero_padded_scale_rows(p.sf, p.tokens, p.sf_tiles, group, groups, lane, L);
     }
   }
 }

@@ -19,7 +19,8 @@ from .codecs import (E2M1_VALUES, E4M3_MAX, e2m1_decode, e2m1_encode, e4m3_decod
 from .tail import (add_rmsnorm_quant_fp8, add_rmsnorm_quant_nvfp4, exact_sum_to_f32,
                    normalize, nvfp4_global_scale, qk_norm_rope_fp8, qk_norm_rope_fp8_kv_store,
                    quant_fp8, quant_nvfp4,
-                   residual_add, rmsnorm_f32, rope_neox, row_scale, sum_of_squares)
+                   residual_add, rmsnorm_f32, rope_neox, row_scale, sum_of_squares,
+                   swizzle_block_scales)
 
 __all__ = [
     "E2M1_VALUES", "E4M3_MAX", "e2m1_decode", "e2m1_encode", "e4m3_decode", "e4m3_encode",
@@ -27,4 +28,5 @@ __all__ = [
     "exact_sum_to_f32", "normalize", "nvfp4_global_scale", "qk_norm_rope_fp8",
     "qk_norm_rope_fp8_kv_store", "quant_fp8",
     "quant_nvfp4", "residual_add", "rmsnorm_f32", "rope_neox", "row_scale", "sum_of_squares",
+    "swizzle_block_scales",
 ]

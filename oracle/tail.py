@@ -241,3 +241,26 @@ def qk_norm_rope_fp8_kv_store(qkv_bits, gamma_q_bits, gamma_k_bits, positions, c
         if 0 <= slot < num_slots:
             kv[slot] = codes[t, nq * D:]
     return dict(q=codes[:, :nq * D].copy(), kv=kv)
+
+
+def swizzle_block_scales(sf: np.ndarray) -> np.ndarray:
+    """Linear block scales [M, nb] -> the 128x4-tiled layout of block-scaled GEMM
+    operands, returned as the buffer's bytes shaped [R, C] (R = M rounded up to
+    128, C = nb rounded up to 4; padding bytes 0).
+
+    The layout is the consumer's, which the NVFP4 pages only refer to through
+    its sf_size packing math (TensorRT-LLM PR #14361, review thread): scales
+    are grouped in tiles of 128 rows x 4 columns, each tile 512 contiguous
+    bytes, tiles in row-major order; inside a tile the bytes run over column
+    (fastest, 4), then row // 32 (4), then row % 32 (32)."""
+    sf = np.asarray(sf, dtype=np.uint8)
+    m, nb = sf.shape
+    R = -(-m // 128) * 128
+    C = -(-nb // 4) * 4
+    out = np.zeros(R * C, dtype=np.uint8)
+    r = np.arange(m, dtype=np.int64)[:, None]
+    c = np.arange(nb, dtype=np.int64)[None, :]
+    tile = (r // 128) * (C // 4) + c // 4
+    inner = (r % 32) * 16 + ((r % 128) // 32) * 4 + c % 4
+    out[tile * 512 + inner] = sf
+    return out.reshape(R, C)

@@ -42,7 +42,9 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4",
                                            "qk_norm_rope_fp8", "qk_norm_rope_fp8_kv_store",
                                            "add_rmsnorm", "quant_fp8",
-                                           "quant_nvfp4", "anq_nvfp4_shape",
+                                           "quant_nvfp4", "add_rmsnorm_quant_nvfp4_swizzled",
+                                           "quant_nvfp4_swizzled", "anq_nvfp4_swizzled_sf_shape",
+                                           "anq_nvfp4_shape",
                                            "anq_status_string"])
 
 
@@ -73,6 +75,46 @@ def test_nvfp4_shape_helper(L):
     assert L.anq_nvfp4_shape(4, 0, ctypes.byref(q), ctypes.byref(s)) == SHAPE
     assert L.anq_nvfp4_shape(-1, 16, ctypes.byref(q), ctypes.byref(s)) == SHAPE
     assert L.anq_nvfp4_shape(4, 16, None, ctypes.byref(s)) == NULL
+
+
+def test_swizzled_sf_shape_helper(L):
+    assert A.nvfp4_swizzled_sf_shape(64, 8192) == (128, 512)
+    assert A.nvfp4_swizzled_sf_shape(8192, 7168) == (8192, 448)
+    assert A.nvfp4_swizzled_sf_shape(300, 1040) == (384, 68)     # 65 blocks -> 68
+    assert A.nvfp4_swizzled_sf_shape(0, 16) == (0, 4)
+    assert A.nvfp4_swizzled_sf_shape(1, 16) == (128, 4)
+    r, c = ctypes.c_int64(), ctypes.c_int64()
+    assert L.anq_nvfp4_swizzled_sf_shape(4, 24, ctypes.byref(r), ctypes.byref(c)) == SHAPE
+    assert L.anq_nvfp4_swizzled_sf_shape(-1, 16, ctypes.byref(r), ctypes.byref(c)) == SHAPE
+    assert L.anq_nvfp4_swizzled_sf_shape(4, 16, ctypes.byref(r), None) == NULL
+
+
+def test_swizzled_nvfp4_validation(L):
+    def sw(**kw):
+        a = dict(x=addr(0), res=addr(1), gamma=addr(2), scale=addr(3), eps=1e-6, tokens=0,
+                 hidden=128, dtype=1, q=addr(4), sf=addr(6), norm=addr(5), stream=None)
+        a.update(kw)
+        return L.add_rmsnorm_quant_nvfp4_swizzled(a["x"], a["res"], a["gamma"], a["scale"],
+                                                  a["eps"], a["tokens"], a["hidden"], a["dtype"],
+                                                  a["q"], a["sf"], a["norm"], a["stream"])
+
+    def qs(**kw):
+        a = dict(t=addr(0), scale=addr(3), tokens=0, hidden=128, dtype=1, q=addr(4), sf=addr(6))
+        a.update(kw)
+        return L.quant_nvfp4_swizzled(a["t"], a["scale"], a["tokens"], a["hidden"], a["dtype"],
+                                      a["q"], a["sf"], None)
+
+    for op in (sw, qs):
+        assert op() == OK
+        assert op(sf=addr(6, 2)) == ALIGN                 # swizzled scales: 4-byte words
+        assert op(sf=addr(6, 4)) == OK
+        assert op(tokens=4, sf=None) == NULL
+        assert op(hidden=40) == SHAPE
+        # the padded scale buffer (128 rows x 8 cols = 1 KiB for 1 token) may not reach q,
+        # although the 8 linear scale bytes of that token would end 992 bytes before it
+        assert op(tokens=1, sf=addr(4) - 1000) == ALIAS
+    assert sw(hidden=65536 + 16) == UNSUP
+    assert nvfp4(L, sf=addr(6, 2)) == OK                  # the linear layout has no alignment rule
 
 
 def fp8(L, **kw):

@@ -358,6 +358,39 @@ def test_qk_kv_store_is_a_scatter_of_the_plain_op():
     assert np.all(pool == 0xAB)                      # the input pool is not modified
 
 
+def test_swizzled_scale_layout():
+    """Offsets worked by hand from the tile description (128x4 tiles of 512
+    bytes, row-major tiles; inside a tile column fastest, then row // 32, then
+    row % 32), and the structure that follows: a bijection onto the padded
+    buffer, 16-byte groups holding rows k, k+32, k+64, k+96, zero padding."""
+    m, nb = 300, 10                                  # R = 384, C = 12: 3 x 3 tiles
+    sf = (np.arange(m * nb, dtype=np.int64) % 251 + 1).astype(np.uint8).reshape(m, nb)
+    out = O.swizzle_block_scales(sf)
+    assert out.shape == (384, 12)
+    flat = out.reshape(-1)
+    # (row, col) -> byte, by hand: tile (r//128)*3 + c//4; inner (r%32)*16 + ((r%128)//32)*4 + c%4
+    hand = {(0, 0): 0, (0, 3): 3, (1, 0): 16, (31, 2): 498, (32, 0): 4, (33, 1): 21, (64, 0): 8,
+            (127, 3): 511, (0, 4): 512, (5, 9): 1024 + 80 + 1, (128, 0): 1536,
+            (299, 9): (2 * 3 + 2) * 512 + (299 % 32) * 16 + ((299 % 128) // 32) * 4 + 1}
+    assert hand[(299, 9)] == 4096 + 11 * 16 + 1 * 4 + 1
+    for (r, c), off in hand.items():
+        assert flat[off] == sf[r, c], (r, c, off)
+    # every real scale lands exactly once (two byte planes carry the flat index + 1)
+    idx = np.arange(1, m * nb + 1, dtype=np.int64).reshape(m, nb)
+    lo = O.swizzle_block_scales((idx % 256).astype(np.uint8)).reshape(-1).astype(np.int64)
+    hi = O.swizzle_block_scales((idx // 256).astype(np.uint8)).reshape(-1).astype(np.int64)
+    got = hi * 256 + lo
+    assert np.array_equal(np.sort(got[got > 0]), np.arange(1, m * nb + 1))
+    assert np.count_nonzero(got) == m * nb        # everything else is padding (0)
+    # the 4 bytes at 16k + 4j of tile (0, 0) are row k + 32j, columns 0..3
+    for k in (0, 7, 31):
+        for j in range(4):
+            assert np.array_equal(flat[16 * k + 4 * j: 16 * k + 4 * j + 4], sf[k + 32 * j, :4])
+    # column padding (cols 10, 11) and row padding (rows 300..383) are zero
+    assert not flat[[2 * 512 + 16 * 3 + 2, 2 * 512 + 16 * 3 + 3]].any()
+    assert not flat[8 * 512 + (300 % 32) * 16 + ((300 % 128) // 32) * 4:][:4].any()
+
+
 # ------------------------------------------------- planted mistakes fail ---
 
 def test_pins_catch_planted_mistakes(monkeypatch):
