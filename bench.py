@@ -18,7 +18,8 @@ pages measure: 0.039 ms on an RTX 5060 Ti, TensorRT-LLM issue #17900,
 Performance result). `all_workloads` holds the same figures for every shape.
 `kv_store` times the Q/K op with its KV-cache store epilogue (SGLang PR
 #32975) on the Q/K workload, writing K|V codes into a shuffled paged pool.
-`fusion_ab` times the separated tail (add_rmsnorm, then quant_fp8 or
+`sf_swizzled` times the NVFP4 op writing its block scales in the 128x4-tiled
+GEMM layout. `fusion_ab` times the separated tail (add_rmsnorm, then quant_fp8 or
 quant_nvfp4: two kernels and a T-rounded norm tensor between them) against the
 fused kernel on the tail workloads, the comparison the pages make (0.103 ms
 separated vs 0.039 ms fused, 2.64x).
@@ -71,7 +72,7 @@ class Workload:
     """Device-resident inputs and outputs of one workload, in R rotating sets."""
 
     def __init__(self, k: int, scalars: dict, steps: int, separated: bool = False,
-                 kv_store: bool = False):
+                 kv_store: bool = False, swizzled: bool = False):
         import numpy as np
         import torch
 
@@ -79,6 +80,7 @@ class Workload:
         self.k = k
         self.separated = separated
         self.kv_store = kv_store
+        self.swizzled = swizzled
         self.inp = W.make_config(k)
         self.bytes = algorithmic_bytes(self.inp) + (self.inp.tokens * 8 if kv_store else 0)
         # a graph of `steps` calls only ever touches `steps` sets
@@ -122,7 +124,12 @@ class Workload:
         M, H = inp.tokens, inp.hidden
         qcols = H if inp.op == "fp8" else H // 2
         self.q = [torch.empty(M, qcols, dtype=torch.uint8, device=dev) for _ in range(self.sets)]
-        self.sf = ([torch.empty(M, H // 16, dtype=torch.uint8, device=dev) for _ in range(self.sets)]
+        sf_shape = (M, H // 16)
+        if swizzled:
+            import nvfp4_quantization_place_amd as A
+            sf_shape = A.nvfp4_swizzled_sf_shape(M, H)
+            self.name = inp.name + "_sf_swizzled"
+        self.sf = ([torch.empty(*sf_shape, dtype=torch.uint8, device=dev) for _ in range(self.sets)]
                    if inp.op == "nvfp4" else None)
         # the separated path always materialises the norm (the quantiser's input)
         self.norm = ([torch.empty_like(x) for _ in range(self.sets)]
@@ -145,6 +152,10 @@ class Workload:
         elif self.kind == "qk":
             A.qk_norm_rope_fp8(self.qkv[j], self.gq, self.gk, self.pos, self.cs, self.scale, inp.eps,
                                inp.nq, inp.nk, inp.nv, inp.head_dim, out=self.out[j])
+        elif self.swizzled:
+            A.add_rmsnorm_quant_nvfp4_swizzled(self.x[j], self.res[j], self.g, self.scale, inp.eps,
+                                               q=self.q[j], sf=self.sf[j],
+                                               norm=self.norm[j] if self.norm else None)
         elif self.kind == "fp8":
             A.add_rmsnorm_quant_fp8(self.x[j], self.res[j], self.g, self.scale, inp.eps,
                                     q=self.q[j], norm=self.norm[j] if self.norm else None)
@@ -350,6 +361,18 @@ def main():
         del w
         torch.cuda.empty_cache()
 
+    swz = {}
+    if not args.no_ab:
+        for k in (2, 4):
+            w = Workload(k, scalars, args.steps, swizzled=True)
+            r = time_workload(w, args.steps, args.warmup, eager=False)
+            swz[str(k)] = {"workload": r["workload"], "us_per_call": r["us_per_call"],
+                           "linear_us_per_call": results[k]["us_per_call"] if k in results else None}
+            print(f"# swizzled scales {k} {r['workload']}: {r['us_per_call']} us/call (graph)",
+                  file=sys.stderr, flush=True)
+            del w
+            torch.cuda.empty_cache()
+
     head = results[args.workload]
     inp_dtype = head["io_dtype"]
     traffic = head["traffic_bytes_per_call"]
@@ -381,6 +404,8 @@ def main():
         line["fusion_ab"] = ab
     if kv:
         line["kv_store"] = kv
+    if swz:
+        line["sf_swizzled"] = swz
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload, scalars)
     print(json.dumps(line), flush=True)

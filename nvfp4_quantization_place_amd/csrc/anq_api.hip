@@ -130,7 +130,8 @@ int rmsnorm_nvfp4(const void* x, void* residual, const void* gamma, const float*
   p.sf_tiles = swizzled ? (int32_t)sf_tiles_of(hidden) : 0;
   const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
   p.rows_per_group = t.rows;
-  return launch_status(anq::launch_tail(dtype, anq::kEpiNvfp4, norm_out != nullptr, p, t,
+  return launch_status(anq::launch_tail(dtype, swizzled ? anq::kEpiNvfp4Swz : anq::kEpiNvfp4,
+                                        norm_out != nullptr, p, t,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -313,7 +314,8 @@ int quant_common(const void* in, const float* scale, int64_t tokens, int64_t hid
   p.vec = (int32_t)(hidden / 8);
   p.sf_tiles = swizzled ? (int32_t)sf_tiles_of(hidden) : 0;
   p.pad_rows = swizzled ? ((tokens + 127) / 128) * 128 - tokens : 0;
-  return launch_status(anq::launch_quant(dtype, nvfp4 ? anq::kEpiNvfp4 : anq::kEpiFp8, p,
+  const int epi = !nvfp4 ? anq::kEpiFp8 : (swizzled ? anq::kEpiNvfp4Swz : anq::kEpiNvfp4);
+  return launch_status(anq::launch_quant(dtype, epi, p,
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -375,15 +375,12 @@ __device__ __forceinline__ size_t sf_swizzled_offset(int64_t r, int32_t c, int32
          (size_t)((r >> 5) & 3) * 4u + (size_t)(c & 3);
 }
 
-// Store the block scale of (row, c). Linear layout when tiles_c == 0. In the
-// swizzled layout the owner of a row's last block also zeroes the (at most 3)
-// padding columns of that row's last tile.
-__device__ __forceinline__ void store_block_scale(uint8_t* sf, int64_t row, int32_t c,
-                                                  int32_t nblk, int32_t tiles_c, uint8_t code) {
-  if (tiles_c == 0) {
-    sf[(size_t)row * (size_t)nblk + (size_t)c] = code;
-    return;
-  }
+// Store the block scale of (row, c) in the swizzled layout. The owner of a
+// row's last block also zeroes the (at most 3) padding columns of that row's
+// last tile.
+__device__ __forceinline__ void store_block_scale_swizzled(uint8_t* sf, int64_t row, int32_t c,
+                                                           int32_t nblk, int32_t tiles_c,
+                                                           uint8_t code) {
   const size_t o = sf_swizzled_offset(row, c, tiles_c);
   sf[o] = code;
   if (c == nblk - 1) {

@@ -6,7 +6,9 @@
 
 namespace anq {
 
-enum Epilogue { kEpiFp8 = 0, kEpiNvfp4 = 1, kEpiNone = 2 };
+// kEpiNvfp4Swz: NVFP4 with the block scales in the 128x4-tiled GEMM layout
+// (its own instantiation, so the linear-layout kernel carries none of its code).
+enum Epilogue { kEpiFp8 = 0, kEpiNvfp4 = 1, kEpiNone = 2, kEpiNvfp4Swz = 3 };
 
 struct TailParams {
   const void* x;
@@ -21,7 +23,7 @@ struct TailParams {
   int32_t hidden;
   int32_t vec;         // hidden / 8: 16-byte vectors per row
   int32_t rows_per_group;  // consecutive rows each lane group processes
-  int32_t sf_tiles;    // NVFP4 scale layout: 0 linear, else 128x4 tiles per tile row
+  int32_t sf_tiles;    // swizzled NVFP4 scales: 128x4 tiles per tile row
 };
 
 // How a row is spread over lanes: `group` lanes of one wavefront per row
@@ -74,7 +76,7 @@ struct QuantParams {
   int64_t vecs;        // tokens * hidden / 8
   int64_t tokens;
   int32_t vec;         // hidden / 8
-  int32_t sf_tiles;    // NVFP4 scale layout: 0 linear, else 128x4 tiles per tile row
+  int32_t sf_tiles;    // swizzled NVFP4 scales: 128x4 tiles per tile row
   int64_t pad_rows;    // swizzled: padded rows past tokens (threads past vecs zero them)
 };
 

@@ -9,8 +9,8 @@
 // An NVFP4 block of 16 is two vectors in adjacent lanes; rows are multiples of
 // 16 elements, so flattening [tokens, hidden] keeps every block inside a row.
 // The encoders are the fused kernel's own (fp8_codes8, nvfp4_half_block).
-// With the swizzled scale layout, threads past the last vector zero the
-// scale words of the padded rows (one 4-byte word each).
+// With the swizzled scale layout (its own instantiation), threads past the
+// last vector zero the scale words of the padded rows (one 4-byte word each).
 #include <stdlib.h>
 
 #include "anq_device.h"
@@ -20,18 +20,19 @@ namespace anq {
 
 template <int DT, int EPI, bool NT>
 __global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
+  constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz;
   __shared__ float mult_tab[128];
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const float sc = *p.scale;  // FP8: s, NVFP4: G
   const float inv_sc = 1.0f / sc;
-  if constexpr (EPI == kEpiNvfp4) {
+  if constexpr (kNvfp4) {
     fill_mult_tab(mult_tab, sc);
     __syncthreads();
   }
-  if constexpr (EPI == kEpiNvfp4) {
-    if (v >= p.vecs) {  // threads past the tensor zero the padded scale rows (swizzled layout)
+  if constexpr (EPI == kEpiNvfp4Swz) {
+    if (v >= p.vecs) {  // threads past the tensor zero the padded scale rows, a word each
       const int64_t e = v - p.vecs;
-      if (p.sf_tiles > 0 && e < p.pad_rows * p.sf_tiles)
+      if (e < p.pad_rows * p.sf_tiles)
         *reinterpret_cast<uint32_t*>(p.sf + sf_swizzled_offset(p.tokens + e / p.sf_tiles,
                                                                4 * (int32_t)(e % p.sf_tiles),
                                                                p.sf_tiles)) = 0u;
@@ -51,12 +52,12 @@ __global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
     if (ok) {
       st4s<false>(p.q + (size_t)v * 4, w);
       if ((v & 1) == 0) {
-        if (p.sf_tiles == 0) {  // linear [tokens, hidden/16]: block v/2 of the flat tensor
+        if constexpr (EPI == kEpiNvfp4) {  // linear [tokens, hidden/16]: block v/2 of the tensor
           st1s<false>(p.sf + (size_t)(v >> 1), (uint8_t)sfc);
         } else {
           const int64_t row = v / p.vec;
-          store_block_scale(p.sf, row, (int32_t)((v - row * p.vec) >> 1), p.vec / 2, p.sf_tiles,
-                            (uint8_t)sfc);
+          store_block_scale_swizzled(p.sf, row, (int32_t)((v - row * p.vec) >> 1), p.vec / 2,
+                                     p.sf_tiles, (uint8_t)sfc);
         }
       }
     }
@@ -73,16 +74,24 @@ static hipError_t launch_quant_epi(const QuantParams& p, hipStream_t s) {
   }
   const void* fn = stream ? (const void*)&quant_kernel<DT, EPI, true>
                           : (const void*)&quant_kernel<DT, EPI, false>;
-  const int64_t threads = p.vecs + (EPI == kEpiNvfp4 && p.sf_tiles > 0 ? p.pad_rows * p.sf_tiles : 0);
+  const int64_t threads = p.vecs + (EPI == kEpiNvfp4Swz ? p.pad_rows * p.sf_tiles : 0);
   const int64_t grid = (threads + 255) / 256;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
+template <int DT>
+static hipError_t launch_quant_dt(int epi, const QuantParams& p, hipStream_t s) {
+  switch (epi) {
+    case kEpiFp8: return launch_quant_epi<DT, kEpiFp8>(p, s);
+    case kEpiNvfp4: return launch_quant_epi<DT, kEpiNvfp4>(p, s);
+    case kEpiNvfp4Swz: return launch_quant_epi<DT, kEpiNvfp4Swz>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t s) {
-  if (dtype == kBF16)
-    return epi == kEpiFp8 ? launch_quant_epi<kBF16, kEpiFp8>(p, s) : launch_quant_epi<kBF16, kEpiNvfp4>(p, s);
-  return epi == kEpiFp8 ? launch_quant_epi<kF16, kEpiFp8>(p, s) : launch_quant_epi<kF16, kEpiNvfp4>(p, s);
+  return dtype == kBF16 ? launch_quant_dt<kBF16>(epi, p, s) : launch_quant_dt<kF16>(epi, p, s);
 }
 
 }  // namespace anq

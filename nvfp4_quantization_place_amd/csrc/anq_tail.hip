@@ -185,7 +185,8 @@ tail_kernel(TailParams p) {
     sc = *p.scale;
     inv_sc = 1.0f / sc;  // correctly rounded division
   }
-  if constexpr (EPI == kEpiNvfp4) {
+  constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz;
+  if constexpr (kNvfp4) {
     fill_mult_tab(mult_tab, sc);
     __syncthreads();
   }
@@ -247,23 +248,26 @@ tail_kernel(TailParams p) {
         uint32_t lo, hi;
         fp8_codes8(n, sc, inv_sc, lo, hi);
         if (vok[k]) st8s<false>(row_ptr<G>(p.q, (size_t)row * p.hidden) + voff[k] / 2, lo, hi);
-      } else if constexpr (EPI == kEpiNvfp4) {
+      } else if constexpr (kNvfp4) {
         uint32_t w, sfc;
         nvfp4_half_block(n, sc, mult_tab, w, sfc);
         if (vok[k]) {
           st4s<false>(row_ptr<G>(p.q, (size_t)row * (p.hidden / 2)) + voff[k] / 4, w);
-          if ((lane & 1) == 0)
-            store_block_scale(p.sf, row, (int32_t)(voff[k] / 32), p.hidden / 16, p.sf_tiles,
-                              (uint8_t)sfc);
+          if ((lane & 1) == 0) {
+            if constexpr (EPI == kEpiNvfp4)
+              st1s<false>(row_ptr<G>(p.sf, (size_t)row * (p.hidden / 16)) + voff[k] / 32,
+                          (uint8_t)sfc);
+            else
+              store_block_scale_swizzled(p.sf, row, (int32_t)(voff[k] / 32), p.hidden / 16,
+                                         p.sf_tiles, (uint8_t)sfc);
+          }
         }
       }
     }
   }
-  if constexpr (EPI == kEpiNvfp4) {
-    if (p.sf_tiles > 0) {  // swizzled layout: lane groups share the padded rows
-      const int64_t groups = G > 0 ? (int64_t)gridDim.x * (blockDim.x / G) : (int64_t)gridDim.x;
-      zero_padded_scale_rows(p.sf, p.tokens, p.sf_tiles, group, groups, lane, L);
-    }
+  if constexpr (EPI == kEpiNvfp4Swz) {  // lane groups share the padded rows
+    const int64_t groups = G > 0 ? (int64_t)gridDim.x * (blockDim.x / G) : (int64_t)gridDim.x;
+    zero_padded_scale_rows(p.sf, p.tokens, p.sf_tiles, group, groups, lane, L);
   }
 }
 
@@ -358,6 +362,7 @@ static hipError_t launch2(bool norm, const TailParams& p, const Tiling& t, hipSt
 template <int DT>
 static hipError_t launch1(int epi, bool norm, const TailParams& p, const Tiling& t, hipStream_t s) {
   if (epi == kEpiNone) return launch3<DT, kEpiNone, true>(p, t, s);  // add + RMSNorm only
+  if (epi == kEpiNvfp4Swz) return launch2<DT, kEpiNvfp4Swz>(norm, p, t, s);
   return epi == kEpiFp8 ? launch2<DT, kEpiFp8>(norm, p, t, s) : launch2<DT, kEpiNvfp4>(norm, p, t, s);
 }
 
