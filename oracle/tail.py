@@ -81,7 +81,8 @@ def exact_sum_to_f32(terms: list[float]) -> np.float32:
 
 def sum_of_squares(h: np.ndarray) -> np.ndarray:
     """ss per row of float32 h [rows, H]: exact sum of h_i^2, rounded once.
-    Squares of fp16/bf16 values are exact in float64."""
+    Squares of binary32 values (fp16/bf16 ones included) are exact in float64:
+    a 24-bit significand squared needs 48 bits."""
     h64 = np.asarray(h, dtype=np.float64)
     sq = h64 * h64
     return np.array([exact_sum_to_f32(row.tolist()) for row in sq.reshape(len(sq), -1)],
@@ -264,3 +265,95 @@ def swizzle_block_scales(sf: np.ndarray) -> np.ndarray:
     inner = (r % 32) * 16 + ((r % 128) // 32) * 4 + c % 4
     out[tile * 512 + inner] = sf
     return out.reshape(R, C)
+
+
+# ----------------------------------------------------------------------------
+# gated RMSNorm + NVFP4
+# ----------------------------------------------------------------------------
+
+_EXP_NEG_CACHE: dict = {}
+
+
+def _rn32_of_decimal(d) -> np.float32:
+    """Round a positive decimal.Decimal (far more precise than binary64) to
+    binary32, nearest even, without double rounding: float(d) is the correctly
+    rounded binary64; only when that lands exactly on a binary32 midpoint can
+    rounding it again go the wrong way, and then d itself is compared with the
+    midpoint."""
+    from decimal import Decimal
+    f64 = float(d)
+    f32 = np.float32(f64)
+    if not np.isfinite(f32) or f32 == 0:
+        return f32
+    lo = np.nextafter(f32, np.float32(0.0)) if f64 < float(f32) else f32
+    hi = np.nextafter(lo, np.float32(np.inf))
+    mid = (float(lo) + float(hi)) / 2.0          # exact in binary64
+    if f64 == mid:
+        md = Decimal(mid)
+        if d < md:
+            return lo
+        if d > md:
+            return hi
+    return f32
+
+
+def exp_neg_rn32(z: np.ndarray) -> np.ndarray:
+    """E = exp(-z) correctly rounded to binary32 (overflow to inf, underflow
+    through the subnormals to 0), for binary32 inputs z. Evaluated with
+    Python's decimal module at 40 significant digits, whose exp is correctly
+    rounded at that precision, then rounded once more to binary32."""
+    from decimal import Decimal, localcontext
+    z = np.asarray(z, dtype=F32)
+    flat = z.reshape(-1)
+    out = np.empty(flat.shape, dtype=F32)
+    with localcontext() as ctx:
+        ctx.prec = 40
+        for i, v in enumerate(flat):
+            key = float(v)
+            e = _EXP_NEG_CACHE.get(key)
+            if e is None:
+                if key <= -200.0:      # exp(200) > 2^128: rounds to inf
+                    e = F32(np.inf)
+                elif key >= 200.0:     # exp(-200) < 2^-150: rounds to 0
+                    e = F32(0.0)
+                else:
+                    e = _rn32_of_decimal((-Decimal(key)).exp())
+                _EXP_NEG_CACHE[key] = e
+            out[i] = e
+    return out.reshape(z.shape)
+
+
+def silu_gate(x: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """u = x * SiLU(z) in binary32 steps: E = RN(exp(-z)), d = 1 + E,
+    sigma = 1 / d, s = z * sigma, u = x * s, each rounded once."""
+    x = np.asarray(x, dtype=F32)
+    z = np.asarray(z, dtype=F32)
+    e = exp_neg_rn32(z)
+    with np.errstate(over="ignore", divide="ignore"):
+        d = F32(1.0) + e
+        sigma = F32(1.0) / d
+        s = z * sigma
+        return x * s
+
+
+def gated_rmsnorm_quant_nvfp4(x_bits, z_bits, gamma_bits, dtype: str, group: int,
+                              global_scale: float, eps: float) -> dict:
+    """Gated RMSNorm + NVFP4 (the gated variant of the fused NVFP4 norm ops,
+    TensorRT-LLM PR #14361, Changes table). The pages name it but do not define
+    the gate; the reading taken is the Mamba-2 gated RMSNorm with the norm
+    after the gate: over each group of `group` consecutive elements of a row,
+    n = RMSNorm(x * SiLU(z)) * gamma, then the NVFP4 epilogue. No residual.
+
+    x, z [tokens, hidden] T; gamma [hidden] T; hidden % group == 0,
+    group % 16 == 0. Returns dict(q, sf, n, u, ss, r)."""
+    x = t_decode(x_bits, dtype)
+    z = t_decode(z_bits, dtype)
+    tokens, hidden = x.shape
+    u = silu_gate(x, z)
+    ug = u.reshape(-1, group)                                  # one row per group
+    ss = sum_of_squares(ug)
+    r = row_scale(ss, group, eps)
+    g = np.tile(t_decode(gamma_bits, dtype).reshape(hidden // group, group), (tokens, 1))
+    n = normalize(ug, r, g)
+    q, sf = quant_nvfp4(n.reshape(tokens, hidden), global_scale)
+    return dict(q=q, sf=sf, n=n.reshape(tokens, hidden), u=u, ss=ss, r=r)
