@@ -130,7 +130,7 @@ class Workload:
             sf_shape = A.nvfp4_swizzled_sf_shape(M, H)
             self.name = inp.name + "_sf_swizzled"
         self.sf = ([torch.empty(*sf_shape, dtype=torch.uint8, device=dev) for _ in range(self.sets)]
-                   if inp.op == "nvfp4" else None)
+                   if inp.op in ("nvfp4", "gated") else None)
         # the separated path always materialises the norm (the quantiser's input)
         self.norm = ([torch.empty_like(x) for _ in range(self.sets)]
                      if inp.norm_out or separated else None)
@@ -230,6 +230,10 @@ def cpu_baseline(k: int, scalars: dict, budget_s: float = 10.0) -> dict:
         if inp.op == "fp8":
             fn = lambda: O.add_rmsnorm_quant_fp8(xb, rb, gb, inp.dtype, inp.scale, inp.eps,  # noqa
                                                  inp.norm_out)
+        elif inp.op == "gated":
+            G = scalars[str(k)]["global_scale"]
+            fn = lambda: O.gated_rmsnorm_quant_nvfp4(xb, rb, gb, inp.dtype,  # noqa
+                                                     inp.meta["group"], G, inp.eps)
         else:
             G = scalars[str(k)]["global_scale"]
             fn = lambda: O.add_rmsnorm_quant_nvfp4(xb, rb, gb, inp.dtype, G, inp.eps,  # noqa
@@ -289,7 +293,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--no-sweep", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-ab", action="store_true",
@@ -318,7 +322,8 @@ def main():
     with open(SCALARS) as fh:
         scalars = json.load(fh)
 
-    todo = [args.workload] + ([] if args.no_sweep else [k for k in (1, 2, 3, 4, 5) if k != args.workload])
+    todo = [args.workload] + ([] if args.no_sweep else
+                              [k for k in (1, 2, 3, 4, 5, 6) if k != args.workload])
     results = {}
     for k in todo:
         w = Workload(k, scalars, args.steps)

@@ -61,7 +61,7 @@
  *    so a producer kernel on the same stream may write them.
  *  - Arguments are validated on the host before any HIP call. A rejected call
  *    returns a nonzero status and enqueues nothing. tokens == 0 returns ANQ_OK
- *    and enqueues nothing; the token-sized buffers (x, residual, q, sf,
+ *    and enqueues nothing; the token-sized buffers (x, z, residual, q, sf,
  *    norm_out, qkv, positions, out, slot_mapping) may then be NULL, as empty
  *    tensors are.
  *  - residual is the only in/out buffer. Every output must be disjoint from
@@ -98,7 +98,7 @@ typedef enum { ANQ_F16 = 0, ANQ_BF16 = 1 } anq_dtype;
 enum {
   ANQ_OK = 0,
   ANQ_ERR_NULL = 1,        /* a required pointer is NULL */
-  ANQ_ERR_SHAPE = 2,       /* tokens < 0, hidden <= 0, hidden % 16 != 0, size overflow */
+  ANQ_ERR_SHAPE = 2,       /* tokens < 0, hidden <= 0, hidden % 16 != 0, bad group, size overflow */
   ANQ_ERR_DTYPE = 3,       /* dtype is not ANQ_F16 / ANQ_BF16 */
   ANQ_ERR_ALIGN = 4,       /* a pointer breaks the alignment rule above */
   ANQ_ERR_ALIAS = 5,       /* buffers overlap where they must not */
@@ -220,6 +220,31 @@ int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden
  */
 int quant_nvfp4(const void* in, const float* global_scale, int64_t tokens, int64_t hidden,
                 int dtype, uint8_t* q, uint8_t* sf, void* stream);
+
+/*
+ * Gated RMSNorm + NVFP4: the gated variant among the fused NVFP4 norm ops
+ * (TensorRT-LLM PR #14361, Changes table). The pages name the op but not the
+ * gate; this is the Mamba-2 gated RMSNorm with the norm after the gate, over
+ * groups of `group` consecutive elements of a row:
+ *   E_i = exp(-z_i) rounded once to binary32 (correctly rounded);
+ *   u_i = x_i * (z_i * (1 / (1 + E_i)))       each operation rounded, binary32;
+ *   ss  = sum of u_i^2 over the group, exact, rounded once; r = 1 / sqrt(ss / group + eps);
+ *   n_i = (u_i * r) * gamma_i;  then the NVFP4 epilogue above (q, sf linear).
+ * No residual. x, z [tokens, hidden] T (read only; they may overlap each other);
+ * gamma [hidden] T; hidden % group == 0, group % 16 == 0, group <= ANQ_MAX_HIDDEN
+ * (group == hidden: one group per row). q [tokens, hidden/2], sf [tokens, hidden/16].
+ */
+int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const void* gamma,
+                              const float* global_scale, float eps, int64_t tokens,
+                              int64_t hidden, int64_t group, int dtype, uint8_t* q, uint8_t* sf,
+                              void* stream);
+
+/*
+ * The gate of gated_rmsnorm_quant_nvfp4 alone: u_i = x_i * SiLU(z_i) in the
+ * binary32 steps stated there, for n elements (n % 8 == 0) of T; u [n]
+ * binary32 (output). x, z and u 16-byte aligned.
+ */
+int silu_gate_f32(const void* x, const void* z, int64_t n, int dtype, float* u, void* stream);
 
 /*
  * NVFP4 with the block scales in the swizzled layout a block-scaled GEMM reads

@@ -16,6 +16,7 @@ import torch  # loads the HIP runtime the library binds to
 
 __all__ = ["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4", "qk_norm_rope_fp8",
            "qk_norm_rope_fp8_kv_store", "add_rmsnorm_quant_nvfp4_swizzled",
+           "gated_rmsnorm_quant_nvfp4", "silu_gate_f32",
            "quant_nvfp4_swizzled", "nvfp4_swizzled_sf_shape", "add_rmsnorm", "quant_fp8", "quant_nvfp4",
            "nvfp4_shape", "status_string", "lib", "AnqError", "LIB_PATH",
            "ANQ_F16", "ANQ_BF16", "STATUS"]
@@ -44,6 +45,8 @@ _SIGS = {
     "add_rmsnorm_quant_nvfp4_swizzled": [_P, _P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P, _P,
                                          _P],
     "quant_nvfp4_swizzled": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P],
+    "gated_rmsnorm_quant_nvfp4": [_P, _P, _P, _P, _F, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P],
+    "silu_gate_f32": [_P, _P, _I64, ctypes.c_int, _P, _P],
     "anq_nvfp4_swizzled_sf_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "anq_nvfp4_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "anq_status_string": [ctypes.c_int],
@@ -348,3 +351,43 @@ def quant_nvfp4_swizzled(t, global_scale, q=None, sf=None, stream=None):
     if st:
         raise AnqError("quant_nvfp4_swizzled", st)
     return q, sf
+
+
+# ------------------------------------------------------------ gated RMSNorm
+
+
+def gated_rmsnorm_quant_nvfp4(x, z, gamma, global_scale, eps: float, group: int | None = None,
+                              q=None, sf=None, stream=None):
+    """n = RMSNorm(x * SiLU(z)) * gamma over groups of `group` elements (default:
+    the whole row), then NVFP4: returns (q [.., hidden/2], sf [.., hidden/16])."""
+    dev = _check_gpu(x, z, gamma, global_scale, q, sf)
+    _scalar(global_scale, "global_scale")
+    tokens, hidden = _rows(x)
+    if z.dtype != x.dtype or gamma.dtype != x.dtype or z.shape != x.shape:
+        raise ValueError("x, z and gamma must share the dtype; x and z the shape")
+    group = hidden if group is None else group
+    qc, sc = (hidden // 2, hidden // 16) if hidden % 16 == 0 and hidden > 0 else (1, 1)
+    if q is None:
+        q = torch.empty(*x.shape[:-1], qc, dtype=torch.uint8, device=dev)
+    if sf is None:
+        sf = torch.empty(*x.shape[:-1], sc, dtype=torch.uint8, device=dev)
+    st = lib().gated_rmsnorm_quant_nvfp4(_ptr(x), _ptr(z), _ptr(gamma), _ptr(global_scale), eps,
+                                         tokens, hidden, group, _dtype_code(x), _ptr(q), _ptr(sf),
+                                         _stream(dev, stream))
+    if st:
+        raise AnqError("gated_rmsnorm_quant_nvfp4", st)
+    return q, sf
+
+
+def silu_gate_f32(x, z, u=None, stream=None):
+    """u = x * SiLU(z) in binary32 steps (the gate of gated_rmsnorm_quant_nvfp4)."""
+    dev = _check_gpu(x, z, u)
+    if z.dtype != x.dtype or z.shape != x.shape:
+        raise ValueError("x and z must share dtype and shape")
+    if u is None:
+        u = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    st = lib().silu_gate_f32(_ptr(x), _ptr(z), x.numel(), _dtype_code(x), _ptr(u),
+                             _stream(dev, stream))
+    if st:
+        raise AnqError("silu_gate_f32", st)
+    return u

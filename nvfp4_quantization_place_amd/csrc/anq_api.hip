@@ -154,6 +154,58 @@ extern "C" int add_rmsnorm_quant_nvfp4_swizzled(const void* x, void* residual, c
                        norm_out, true, stream);
 }
 
+extern "C" int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const void* gamma,
+                                         const float* global_scale, float eps, int64_t tokens,
+                                         int64_t hidden, int64_t group, int dtype, uint8_t* q,
+                                         uint8_t* sf, void* stream) {
+  if (!gamma || !global_scale || (tokens != 0 && (!x || !z || !q || !sf))) return ANQ_ERR_NULL;
+  if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
+  if (tokens < 0 || hidden <= 0 || group <= 0 || hidden % 16 != 0 || group % 16 != 0 ||
+      hidden % group != 0)
+    return ANQ_ERR_SHAPE;
+  if (group > ANQ_MAX_HIDDEN) return ANQ_ERR_UNSUPPORTED;
+  if (tokens > INT64_MAX / (2 * hidden) || hidden / group > INT32_MAX) return ANQ_ERR_SHAPE;
+  if (!valid_eps(eps)) return ANQ_ERR_VALUE;
+  if (!aligned(x, 16) || !aligned(z, 16) || !aligned(gamma, 16) || !aligned(q, 16) ||
+      !aligned(global_scale, 4))
+    return ANQ_ERR_ALIGN;
+  const int64_t act = tokens * hidden * 2;
+  const Span outs[2] = {span(q, tokens * (hidden / 2)), span(sf, tokens * (hidden / 16))};
+  const Span ins[4] = {span(x, act), span(z, act), span(gamma, hidden * 2), span(global_scale, 4)};
+  if (any_alias(outs, 2, ins, 4)) return ANQ_ERR_ALIAS;
+  if (tokens == 0) return ANQ_OK;
+
+  anq::TailParams p{};  // one row per group: [tokens * hidden / group, group]
+  p.x = x;
+  p.residual = const_cast<void*>(z);  // read only in the gated variant
+  p.gamma = gamma;
+  p.scale = global_scale;
+  p.q = q;
+  p.sf = sf;
+  p.eps = eps;
+  p.tokens = tokens * (hidden / group);
+  p.hidden = (int32_t)group;
+  p.vec = (int32_t)(group / 8);
+  p.gamma_period = (int32_t)(hidden / group);
+  const anq::Tiling t = anq::pick_tail_tiling(p.vec, p.tokens);
+  p.rows_per_group = t.rows;
+  return launch_status(anq::launch_tail(dtype, anq::kEpiGatedNvfp4, false, p, t,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int silu_gate_f32(const void* x, const void* z, int64_t n, int dtype, float* u,
+                             void* stream) {
+  if (n != 0 && (!x || !z || !u)) return ANQ_ERR_NULL;
+  if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
+  if (n < 0 || n % 8 != 0 || n > INT64_MAX / 4) return ANQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(z, 16) || !aligned(u, 16)) return ANQ_ERR_ALIGN;
+  const Span outs[1] = {span(u, n * 4)};
+  const Span ins[2] = {span(x, n * 2), span(z, n * 2)};
+  if (any_alias(outs, 1, ins, 2)) return ANQ_ERR_ALIAS;
+  if (n == 0) return ANQ_OK;
+  return launch_status(anq::launch_gate(dtype, x, z, u, n / 8, static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 // Checks shared by the two Q/K entry points. q_cols is the width of `out` in

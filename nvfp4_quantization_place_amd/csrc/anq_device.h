@@ -365,6 +365,17 @@ __device__ __forceinline__ void nvfp4_half_block(const float (&n)[8], float G, c
   codes = e2m1x8(t);
 }
 
+// The SiLU gate applied to x, in binary32 steps: E = exp(-z) rounded once to
+// binary32 (evaluated in binary64, whose error is far below the binary32
+// rounding step; checked over every fp16 and bf16 z), d = 1 + E, sigma = 1 / d
+// (IEEE division), s = z * sigma, u = x * s.
+__device__ __forceinline__ float silu_gate(float x, float z) {
+  const float e = (float)exp(-(double)z);
+  const float d = 1.0f + e;
+  const float sigma = 1.0f / d;
+  return x * (z * sigma);
+}
+
 // Byte offset of the block scale of row r, block column c in the 128x4-tiled
 // scale layout of block-scaled GEMM operands: rows padded to 128, scale
 // columns to 4; tile (r / 128, c / 4) is 512 contiguous bytes, tiles row-major

@@ -8,7 +8,9 @@ namespace anq {
 
 // kEpiNvfp4Swz: NVFP4 with the block scales in the 128x4-tiled GEMM layout
 // (its own instantiation, so the linear-layout kernel carries none of its code).
-enum Epilogue { kEpiFp8 = 0, kEpiNvfp4 = 1, kEpiNone = 2, kEpiNvfp4Swz = 3 };
+// kEpiGatedNvfp4: the gated variant, n = RMSNorm(x * SiLU(z)) * gamma per row
+// of `hidden` (a group), NVFP4 codes; `residual` then holds z (read only).
+enum Epilogue { kEpiFp8 = 0, kEpiNvfp4 = 1, kEpiNone = 2, kEpiNvfp4Swz = 3, kEpiGatedNvfp4 = 4 };
 
 struct TailParams {
   const void* x;
@@ -24,6 +26,7 @@ struct TailParams {
   int32_t vec;         // hidden / 8: 16-byte vectors per row
   int32_t rows_per_group;  // consecutive rows each lane group processes
   int32_t sf_tiles;    // swizzled NVFP4 scales: 128x4 tiles per tile row
+  int32_t gamma_period;  // gated: groups per token; row r uses gamma slice r % period
 };
 
 // How a row is spread over lanes: `group` lanes of one wavefront per row
@@ -81,5 +84,9 @@ struct QuantParams {
 };
 
 hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t stream);
+
+// u = x * SiLU(z) for vecs * 8 elements (the gate of the gated RMSNorm).
+hipError_t launch_gate(int dtype, const void* x, const void* z, float* u, int64_t vecs,
+                       hipStream_t stream);
 
 }  // namespace anq

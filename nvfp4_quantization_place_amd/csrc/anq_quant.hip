@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
     if (ok) {
       st4s<false>(p.q + (size_t)v * 4, w);
       if ((v & 1) == 0) {
-        if constexpr (EPI == kEpiNvfp4) {  // linear [tokens, hidden/16]: block v/2 of the tensor
+        if constexpr (EPI != kEpiNvfp4Swz) {  // linear [tokens, hidden/16]: block v/2 of the tensor
           st1s<false>(p.sf + (size_t)(v >> 1), (uint8_t)sfc);
         } else {
           const int64_t row = v / p.vec;
@@ -92,6 +92,43 @@ static hipError_t launch_quant_dt(int epi, const QuantParams& p, hipStream_t s) 
 
 hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t s) {
   return dtype == kBF16 ? launch_quant_dt<kBF16>(epi, p, s) : launch_quant_dt<kF16>(epi, p, s);
+}
+
+// u = x * SiLU(z) in binary32 (silu_gate), one thread per 8 elements: the gate
+// of the gated RMSNorm as a standalone op.
+template <int DT>
+__global__ void __launch_bounds__(256) gate_kernel(const uint8_t* x, const uint8_t* z, float* u,
+                                                   int64_t vecs) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= vecs) return;
+  float xf[8], zf[8];
+  unpack8<DT>(ld16(x + (size_t)v * 16), xf);
+  unpack8<DT>(ld16(z + (size_t)v * 16), zf);
+  float4 a, b;
+  a.x = silu_gate(xf[0], zf[0]);
+  a.y = silu_gate(xf[1], zf[1]);
+  a.z = silu_gate(xf[2], zf[2]);
+  a.w = silu_gate(xf[3], zf[3]);
+  b.x = silu_gate(xf[4], zf[4]);
+  b.y = silu_gate(xf[5], zf[5]);
+  b.z = silu_gate(xf[6], zf[6]);
+  b.w = silu_gate(xf[7], zf[7]);
+  float4* o = reinterpret_cast<float4*>(u + (size_t)v * 8);
+  o[0] = a;
+  o[1] = b;
+}
+
+hipError_t launch_gate(int dtype, const void* x, const void* z, float* u, int64_t vecs,
+                       hipStream_t s) {
+  const int64_t grid = (vecs + 255) / 256;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  const uint8_t* zb = static_cast<const uint8_t*>(z);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(gate_kernel<kBF16>, dim3((unsigned)grid), dim3(256), 0, s, xb, zb, u, vecs);
+  else
+    hipLaunchKernelGGL(gate_kernel<kF16>, dim3((unsigned)grid), dim3(256), 0, s, xb, zb, u, vecs);
+  return hipGetLastError();
 }
 
 }  // namespace anq

@@ -88,22 +88,19 @@ __device__ __forceinline__ T* row_ptr(T* base, size_t off) {
 }
 
 // Rounded-once binary32 sum of squares of a row (see above). The rare
-// double-double pass re-reads the lane's own h values from the residual row it
-// has just stored (a thread always observes its own earlier stores), one
-// element at a time, so it adds no registers to the common path.
-template <int DT, int K, class Red>
-__device__ __forceinline__ float row_sum_squares_dd(const uint8_t* res_row, const uint32_t* voff,
-                                                 const bool* vok, const Red& red) {
+// double-double pass recomputes the lane's own row values one element at a
+// time through `elem(k, i)` (re-reading memory, not registers), so it adds no
+// registers to the common path.
+template <int K, class Red, class Elem>
+__device__ __forceinline__ float row_sum_squares_dd(const bool* vok, const Red& red,
+                                                    const Elem& elem) {
   double hi = 0.0, lo = 0.0;
 #pragma unroll 1
   for (int k = 0; k < K; ++k) {
     if (!vok[k]) continue;
 #pragma unroll 1
     for (int i = 0; i < 8; ++i) {
-      const uint16_t b = *reinterpret_cast<const volatile uint16_t*>(res_row + voff[k] + 2 * i);
-      float f, unused;
-      unpack2<DT>((uint32_t)b, f, unused);
-      const double d = (double)f;
+      const double d = (double)elem(k, i);
       dd_add(hi, lo, d * d, 0.0);
     }
   }
@@ -111,15 +108,15 @@ __device__ __forceinline__ float row_sum_squares_dd(const uint8_t* res_row, cons
   return dd_to_f32(hi, lo);
 }
 
-template <int DT, int K, class Red>
+template <int K, class Red, class Elem>
 __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int parity,
-                                                 const uint8_t* res_row, const uint32_t* voff,
-                                                 const bool* vok, const Red& red) {
+                                                 const bool* vok, const Red& red,
+                                                 const Elem& elem) {
   const double S = red.sum(acc, parity);
   const float ss = (float)S;
   // float64 error of a sum of `width` non-negative terms is below width * 2^-53 * S
   if (near_f32_midpoint(S, ss, S * (double)width * 0x1p-52))  // uniform over the row
-    return row_sum_squares_dd<DT, K>(res_row, voff, vok, red);
+    return row_sum_squares_dd<K>(vok, red, elem);
   return ss;
 }
 
@@ -132,10 +129,11 @@ __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int 
 // the row end (hidden not a multiple of 8 * lanes) are skipped.
 //
 // Register budget: 7 wavefronts per SIMD (<= 72 VGPRs) for one vector per
-// lane, which then needs no spills; 4 (<= 128) for rows wider than 8192.
+// lane, which then needs no spills; 4 (<= 128) for rows wider than 8192 and
+// for the gated variant (its binary64 exp needs the registers).
 template <int DT, int EPI, bool NORM, int K, int G, bool NT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 ? 256 : 1024),
-                               amdgpu_waves_per_eu(K == 1 ? 7 : 4)))
+                               amdgpu_waves_per_eu(K == 1 && EPI != kEpiGatedNvfp4 ? 7 : 4)))
 tail_kernel(TailParams p) {
   __shared__ double lds[64];
   __shared__ float mult_tab[128];  // NVFP4: G / value(sf) for every block-scale code
@@ -185,7 +183,8 @@ tail_kernel(TailParams p) {
     sc = *p.scale;
     inv_sc = 1.0f / sc;  // correctly rounded division
   }
-  constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz;
+  constexpr bool kGated = EPI == kEpiGatedNvfp4;  // `res` is z: read only, never stored
+  constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz || kGated;
   if constexpr (kNvfp4) {
     fill_mult_tab(mult_tab, sc);
     __syncthreads();
@@ -200,18 +199,31 @@ tail_kernel(TailParams p) {
   int parity = 0;
   for (; row < row_end; ++row, parity ^= 1) {
     uint8_t* rrow = row_ptr<G>(res, (size_t)row * row_bytes);
+    if constexpr (kGated) {  // each group of a token has its own gamma slice
+      if (p.gamma_period > 1) {
+        const uint8_t* grow = gam + (size_t)(row % p.gamma_period) * row_bytes;
+#pragma unroll
+        for (int k = 0; k < K; ++k) gv[k] = ld16(grow + voff[k]);
+      }
+    }
     float h[K][8];
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      float xf[8], rf[8], s[8];
+      float xf[8], rf[8];
       unpack8<DT>(xv[k], xf);
       unpack8<DT>(rv[k], rf);
+      if constexpr (kGated) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] = xf[i] + rf[i];
-      const U4 hv = pack8<DT>(s);
-      if (vok[k]) st16s<NT>(rrow + voff[k], hv);
-      unpack8<DT>(hv, h[k]);
+        for (int i = 0; i < 8; ++i) h[k][i] = silu_gate(xf[i], rf[i]);  // binary32 u
+      } else {
+        float s[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] = xf[i] + rf[i];
+        const U4 hv = pack8<DT>(s);
+        if (vok[k]) st16s<NT>(rrow + voff[k], hv);
+        unpack8<DT>(hv, h[k]);
+      }
       double a = 0.0;  // vectors past the row end hold a clamped copy: not counted
 #pragma unroll
       for (int i = 0; i < 8; ++i) a = __builtin_fma((double)h[k][i], (double)h[k][i], a);
@@ -229,7 +241,22 @@ tail_kernel(TailParams p) {
       }
     }
 
-    const float ss = row_sum_squares<DT, K>(acc, p.hidden, parity, rrow, voff, vok, red);
+    float ss;
+    if constexpr (kGated) {  // the fallback recomputes u from x and z
+      const uint8_t* xrow = row_ptr<G>(x, (size_t)row * row_bytes);
+      ss = row_sum_squares<K>(acc, p.hidden, parity, vok, red, [&](int k, int i) {
+        float xf, zf, unused;
+        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(xrow + voff[k] + 2 * i), xf, unused);
+        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + voff[k] + 2 * i), zf, unused);
+        return silu_gate(xf, zf);
+      });
+    } else {  // the fallback re-reads the lane's own just-stored residual elements
+      ss = row_sum_squares<K>(acc, p.hidden, parity, vok, red, [&](int k, int i) {
+        float f, unused;
+        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + voff[k] + 2 * i), f, unused);
+        return f;
+      });
+    }
     const float r = 1.0f / sqrtf(ss / (float)p.hidden + p.eps);
 
     // Codes and block scales are stored without the streaming hint: their 8-,
@@ -254,12 +281,12 @@ tail_kernel(TailParams p) {
         if (vok[k]) {
           st4s<false>(row_ptr<G>(p.q, (size_t)row * (p.hidden / 2)) + voff[k] / 4, w);
           if ((lane & 1) == 0) {
-            if constexpr (EPI == kEpiNvfp4)
-              st1s<false>(row_ptr<G>(p.sf, (size_t)row * (p.hidden / 16)) + voff[k] / 32,
-                          (uint8_t)sfc);
-            else
+            if constexpr (EPI == kEpiNvfp4Swz)
               store_block_scale_swizzled(p.sf, row, (int32_t)(voff[k] / 32), p.hidden / 16,
                                          p.sf_tiles, (uint8_t)sfc);
+            else  // linear [rows, width/16] (the plain and the gated variants)
+              st1s<false>(row_ptr<G>(p.sf, (size_t)row * (p.hidden / 16)) + voff[k] / 32,
+                          (uint8_t)sfc);
           }
         }
       }
@@ -363,6 +390,7 @@ template <int DT>
 static hipError_t launch1(int epi, bool norm, const TailParams& p, const Tiling& t, hipStream_t s) {
   if (epi == kEpiNone) return launch3<DT, kEpiNone, true>(p, t, s);  // add + RMSNorm only
   if (epi == kEpiNvfp4Swz) return launch2<DT, kEpiNvfp4Swz>(norm, p, t, s);
+  if (epi == kEpiGatedNvfp4) return launch3<DT, kEpiGatedNvfp4, false>(p, t, s);  // no norm out
   return epi == kEpiFp8 ? launch2<DT, kEpiFp8>(norm, p, t, s) : launch2<DT, kEpiNvfp4>(norm, p, t, s);
 }
 

@@ -304,11 +304,11 @@ def exp_neg_rn32(z: np.ndarray) -> np.ndarray:
     rounded at that precision, then rounded once more to binary32."""
     from decimal import Decimal, localcontext
     z = np.asarray(z, dtype=F32)
-    flat = z.reshape(-1)
-    out = np.empty(flat.shape, dtype=F32)
+    uniq, inv = np.unique(z.reshape(-1), return_inverse=True)   # at most 2^16 values from T
+    out = np.empty(uniq.shape, dtype=F32)
     with localcontext() as ctx:
         ctx.prec = 40
-        for i, v in enumerate(flat):
+        for i, v in enumerate(uniq):
             key = float(v)
             e = _EXP_NEG_CACHE.get(key)
             if e is None:
@@ -320,7 +320,7 @@ def exp_neg_rn32(z: np.ndarray) -> np.ndarray:
                     e = _rn32_of_decimal((-Decimal(key)).exp())
                 _EXP_NEG_CACHE[key] = e
             out[i] = e
-    return out.reshape(z.shape)
+    return out[inv].reshape(z.shape)
 
 
 def silu_gate(x: np.ndarray, z: np.ndarray) -> np.ndarray:

@@ -1,5 +1,5 @@
-"""Write tests/golden/workload_scalars.json: for each of the five workloads the
-checksums of its seeded inputs, and for the NVFP4 workloads the global scale
+"""Write tests/golden/workload_scalars.json: for each workload the checksums
+of its seeded inputs, and for the NVFP4 workloads (gated included) the global scale
 G = fl32(448 * 6 / amax|n|) over the oracle's binary32 normed tensor (the
 reading of "global fp32 scale = 448*6/amax(normed)"). Calls only the oracle
 and the input generator.
@@ -30,9 +30,14 @@ def main():
         else:
             e["checksums"] = {"x": W.checksum(inp.x), "residual": W.checksum(inp.residual),
                               "gamma": W.checksum(inp.gamma)}
-            if inp.op == "nvfp4":
-                n = O.rmsnorm_f32(W.bits(inp.x), W.bits(inp.residual), W.bits(inp.gamma),
-                                  inp.dtype, inp.eps)
+            if inp.op in ("nvfp4", "gated"):
+                if inp.op == "gated":
+                    n = O.gated_rmsnorm_quant_nvfp4(W.bits(inp.x), W.bits(inp.residual),
+                                                    W.bits(inp.gamma), inp.dtype,
+                                                    inp.meta["group"], 1.0, inp.eps)["n"]
+                else:
+                    n = O.rmsnorm_f32(W.bits(inp.x), W.bits(inp.residual), W.bits(inp.gamma),
+                                      inp.dtype, inp.eps)
                 G = O.nvfp4_global_scale(n)
                 e["global_scale"] = float(G)
                 e["global_scale_bits"] = "0x%08X" % int(G.view("uint32"))

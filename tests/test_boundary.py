@@ -44,6 +44,7 @@ def test_header_declares_the_entry_points():
                                            "add_rmsnorm", "quant_fp8",
                                            "quant_nvfp4", "add_rmsnorm_quant_nvfp4_swizzled",
                                            "quant_nvfp4_swizzled", "anq_nvfp4_swizzled_sf_shape",
+                                           "gated_rmsnorm_quant_nvfp4", "silu_gate_f32",
                                            "anq_nvfp4_shape",
                                            "anq_status_string"])
 
@@ -115,6 +116,38 @@ def test_swizzled_nvfp4_validation(L):
         assert op(tokens=1, sf=addr(4) - 1000) == ALIAS
     assert sw(hidden=65536 + 16) == UNSUP
     assert nvfp4(L, sf=addr(6, 2)) == OK                  # the linear layout has no alignment rule
+
+
+def test_gated_validation(L):
+    def g(**kw):
+        a = dict(x=addr(0), z=addr(1), gamma=addr(2), scale=addr(3), eps=1e-6, tokens=0,
+                 hidden=1024, group=256, dtype=1, q=addr(4), sf=addr(6))
+        a.update(kw)
+        return L.gated_rmsnorm_quant_nvfp4(a["x"], a["z"], a["gamma"], a["scale"], a["eps"],
+                                           a["tokens"], a["hidden"], a["group"], a["dtype"],
+                                           a["q"], a["sf"], None)
+
+    assert g() == OK
+    for k in ("x", "z", "q", "sf"):
+        assert g(tokens=4, **{k: None}) == NULL, k
+        assert g(tokens=0, **{k: None}) == OK, k
+    assert g(gamma=None) == NULL and g(scale=None) == NULL
+    for grp in (0, -16, 24, 384, 2048):       # not a multiple of 16, or not dividing hidden
+        assert g(group=grp) == SHAPE, grp
+    assert g(hidden=1 << 17, group=1 << 17) == UNSUP        # one group wider than a row kernel takes
+    assert g(hidden=1 << 17, group=1024) == OK              # wide rows of narrow groups are fine
+    assert g(dtype=4) == DTYPE
+    assert g(eps=float("nan")) == VALUE
+    assert g(z=addr(1, 8)) == ALIGN
+    assert g(tokens=4, q=addr(1)) == ALIAS                   # codes over z
+    gate = L.silu_gate_f32
+    assert gate(addr(0), addr(1), 0, 1, addr(2), None) == OK
+    assert gate(None, addr(1), 8, 1, addr(2), None) == NULL
+    assert gate(addr(0), addr(1), 12, 1, addr(2), None) == SHAPE
+    assert gate(addr(0), addr(1), 8, 2, addr(2), None) == DTYPE
+    assert gate(addr(0), addr(1), 8, 1, addr(2, 4), None) == ALIGN
+    assert gate(addr(0), addr(1), 8, 1, addr(1), None) == ALIAS
+    assert g(tokens=4, sf=addr(4, 16)) == ALIAS              # scales over the codes
 
 
 def fp8(L, **kw):

@@ -111,7 +111,7 @@ def rope_table(max_pos: int, head_dim: int, theta: float) -> np.ndarray:
 class TailInputs:
     """Inputs of one add + RMSNorm + quant call. Tensors are CPU, contiguous."""
     name: str
-    op: str                 # "fp8" or "nvfp4"
+    op: str                 # "fp8", "nvfp4", or "gated" (residual then holds the gate z)
     dtype: str              # "f16" or "bf16"
     tokens: int
     hidden: int
@@ -142,7 +142,7 @@ class QKInputs:
     scale: float
 
 
-# The five workloads. "sizes" are the shapes the pages name or that are fixed here.
+# The workloads. "sizes" are the shapes the pages name or that are fixed here.
 CONFIGS = {
     1: dict(name="fp8_f16_16x128", op="fp8", dtype="f16", tokens=16, hidden=128,
             x=("normal", 1.0), res=("normal", 1.0), gamma=("one_plus", 0.1),
@@ -158,6 +158,11 @@ CONFIGS = {
             eps=1e-5, scale=None, norm_out=True, outliers=0.001),
     5: dict(name="qk_norm_rope_fp8_bf16_4096x32x128", op="qk", dtype="bf16", tokens=4096,
             nq=16, nk=8, nv=8, head_dim=128, theta=1e6, eps=1e-6, scale=0.05),
+    # gated RMSNorm + NVFP4 at a Mamba-2 mixer's shape (inner width 8192, 8 groups);
+    # the pages name the op but no workload for it
+    6: dict(name="gated_nvfp4_bf16_8192x8192_g1024", op="gated", dtype="bf16", tokens=8192,
+            hidden=8192, group=1024, x=("normal", 1.0), z=("normal", 2.0),
+            gamma=("one_plus", 0.1), eps=1e-5),
 }
 
 
@@ -213,10 +218,27 @@ def make_qk(seed: int, dtype: str, tokens: int, nq: int, nk: int, nv: int, head_
                     cos_sin=rope_table(max_pos, head_dim, theta), eps=eps, scale=scale)
 
 
+def make_gated(seed: int, dtype: str, tokens: int, hidden: int, group: int, *,
+               x=("normal", 1.0), z=("normal", 2.0), gamma=("one_plus", 0.1),
+               eps: float = 1e-5, name: str = "custom") -> TailInputs:
+    """Inputs of one gated RMSNorm + NVFP4 call: x, the gate z (in `residual`),
+    gamma; meta["group"] is the normalisation group width."""
+    n = tokens * hidden
+    return TailInputs(
+        name=name, op="gated", dtype=dtype, tokens=tokens, hidden=hidden,
+        x=to_dtype(_draw(x, seed, TID_X, n), dtype).reshape(tokens, hidden),
+        residual=to_dtype(_draw(z, seed, TID_RES, n), dtype).reshape(tokens, hidden),
+        gamma=to_dtype(_draw(gamma, seed, TID_GAMMA, hidden), dtype), eps=eps, scale=None,
+        norm_out=False, meta={"group": group})
+
+
 def make_config(k: int):
     """Inputs of workload k (1..5), seed k. NVFP4 global scales are not drawn:
     they are derived from the normed tensor and stored beside the tests."""
     c = dict(CONFIGS[k])
+    if c["op"] == "gated":
+        return make_gated(k, c["dtype"], c["tokens"], c["hidden"], c["group"], x=c["x"], z=c["z"],
+                          gamma=c["gamma"], eps=c["eps"], name=c["name"])
     if c["op"] == "qk":
         return make_qk(k, c["dtype"], c["tokens"], c["nq"], c["nk"], c["nv"], c["head_dim"],
                        theta=c["theta"], eps=c["eps"], scale=c["scale"], name=c["name"])
