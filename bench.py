@@ -56,6 +56,8 @@ def algorithmic_bytes(inp) -> int:
         C = (inp.nq + inp.nk + inp.nv) * D
         return inp.tokens * C * 3 + inp.tokens * (4 * D + 8) + 4 * D + 4
     M, H = inp.tokens, inp.hidden
+    if inp.op == "gated":  # reads x and z, writes codes and scales; no residual
+        return int(round(M * H * (2 + 2 + 0.5 + 1 / 16))) + 2 * H + 4
     per = 2 + 2 + 2 + (1 if inp.op == "fp8" else 0.5 + 1 / 16) + (2 if inp.norm_out else 0)
     return int(round(M * H * per)) + 2 * H + 4
 
@@ -156,13 +158,18 @@ class Workload:
             A.add_rmsnorm_quant_nvfp4_swizzled(self.x[j], self.res[j], self.g, self.scale, inp.eps,
                                                q=self.q[j], sf=self.sf[j],
                                                norm=self.norm[j] if self.norm else None)
+        elif self.kind == "gated":
+            A.gated_rmsnorm_quant_nvfp4(self.x[j], self.res[j], self.g, self.scale, inp.eps,
+                                        group=inp.meta["group"], q=self.q[j], sf=self.sf[j])
         elif self.kind == "fp8":
             A.add_rmsnorm_quant_fp8(self.x[j], self.res[j], self.g, self.scale, inp.eps,
                                     q=self.q[j], norm=self.norm[j] if self.norm else None)
-        else:
+        elif self.kind == "nvfp4":
             A.add_rmsnorm_quant_nvfp4(self.x[j], self.res[j], self.g, self.scale, inp.eps,
                                       q=self.q[j], sf=self.sf[j],
                                       norm=self.norm[j] if self.norm else None)
+        else:
+            raise ValueError(f"no call for workload kind {self.kind!r}")
 
 
 def time_workload(w: Workload, steps: int, warmup: int, eager: bool = True) -> dict:

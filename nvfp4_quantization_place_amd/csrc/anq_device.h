@@ -365,15 +365,95 @@ __device__ __forceinline__ void nvfp4_half_block(const float (&n)[8], float G, c
   codes = e2m1x8(t);
 }
 
-// The SiLU gate applied to x, in binary32 steps: E = exp(-z) rounded once to
-// binary32 (evaluated in binary64, whose error is far below the binary32
-// rounding step; checked over every fp16 and bf16 z), d = 1 + E, sigma = 1 / d
-// (IEEE division), s = z * sigma, u = x * s.
-__device__ __forceinline__ float silu_gate(float x, float z) {
-  const float e = (float)exp(-(double)z);
-  const float d = 1.0f + e;
-  const float sigma = 1.0f / d;
+// ------------------------------------------------------------ SiLU gate
+
+// 2^(j/64) for j < 64, each rounded to the nearest binary64: the table of the
+// gate's exp. Each workgroup copies it into LDS.
+__device__ const double kExp2Tab[64] = {
+    0x1.0000000000000p+0, 0x1.02c9a3e778061p+0, 0x1.059b0d3158574p+0, 0x1.0874518759bc8p+0,
+    0x1.0b5586cf9890fp+0, 0x1.0e3ec32d3d1a2p+0, 0x1.11301d0125b51p+0, 0x1.1429aaea92de0p+0,
+    0x1.172b83c7d517bp+0, 0x1.1a35beb6fcb75p+0, 0x1.1d4873168b9aap+0, 0x1.2063b88628cd6p+0,
+    0x1.2387a6e756238p+0, 0x1.26b4565e27cddp+0, 0x1.29e9df51fdee1p+0, 0x1.2d285a6e4030bp+0,
+    0x1.306fe0a31b715p+0, 0x1.33c08b26416ffp+0, 0x1.371a7373aa9cbp+0, 0x1.3a7db34e59ff7p+0,
+    0x1.3dea64c123422p+0, 0x1.4160a21f72e2ap+0, 0x1.44e086061892dp+0, 0x1.486a2b5c13cd0p+0,
+    0x1.4bfdad5362a27p+0, 0x1.4f9b2769d2ca7p+0, 0x1.5342b569d4f82p+0, 0x1.56f4736b527dap+0,
+    0x1.5ab07dd485429p+0, 0x1.5e76f15ad2148p+0, 0x1.6247eb03a5585p+0, 0x1.6623882552225p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.6dfb23c651a2fp+0, 0x1.71f75e8ec5f74p+0, 0x1.75feb564267c9p+0,
+    0x1.7a11473eb0187p+0, 0x1.7e2f336cf4e62p+0, 0x1.82589994cce13p+0, 0x1.868d99b4492edp+0,
+    0x1.8ace5422aa0dbp+0, 0x1.8f1ae99157736p+0, 0x1.93737b0cdc5e5p+0, 0x1.97d829fde4e50p+0,
+    0x1.9c49182a3f090p+0, 0x1.a0c667b5de565p+0, 0x1.a5503b23e255dp+0, 0x1.a9e6b5579fdbfp+0,
+    0x1.ae89f995ad3adp+0, 0x1.b33a2b84f15fbp+0, 0x1.b7f76f2fb5e47p+0, 0x1.bcc1e904bc1d2p+0,
+    0x1.c199bdd85529cp+0, 0x1.c67f12e57d14bp+0, 0x1.cb720dcef9069p+0, 0x1.d072d4a07897cp+0,
+    0x1.d5818dcfba487p+0, 0x1.da9e603db3285p+0, 0x1.dfc97337b9b5fp+0, 0x1.e502ee78b3ff6p+0,
+    0x1.ea4afa2a490dap+0, 0x1.efa1bee615a27p+0, 0x1.f50765b6e4540p+0, 0x1.fa7c1819e90d8p+0,
+};
+
+__device__ __forceinline__ void fill_exp2_tab(double* tab) {
+  for (int j = threadIdx.x; j < 64; j += blockDim.x) tab[j] = kExp2Tab[j];
+}
+
+// exp(-z) rounded once to binary32, for binary32 z. Table-driven in binary64:
+// -z = (n / 64) ln 2 + r with n = rint(-z 64 / ln 2) and a two-part ln 2 / 64
+// (its high part has 37 bits, so n * high is exact for |n| < 2^15), |r| <= ln 2 / 128;
+// exp(-z) = 2^(n >> 6) * 2^((n & 63) / 64) * p(r), p the degree-5 Taylor
+// polynomial (truncation below 2^-54 relative). The binary64 value is within
+// about 2^-50 of exp(-z), far inside a binary32 rounding step; that the one
+// final rounding then lands where exp(-z) itself would is checked over every
+// fp16 and bf16 z. |z| >= 200 is clamped: exp(-+200) already round to 0 / inf.
+__device__ __forceinline__ float exp_neg_rn(float z, const double* exp2_tab) {
+  const double zc = (double)__builtin_amdgcn_fmed3f(z, 200.0f, -200.0f);
+  const double n = __builtin_rint(-zc * 0x1.71547652b82fep+6);  // -z * 64 / ln 2
+  double r = __builtin_fma(-n, 0x1.62e42fefa0000p-7, -zc);       // exact
+  r = __builtin_fma(-n, 0x1.cf79abc9e3b3ap-46, r);
+  double p = __builtin_fma(0x1.1111111111111p-7, r, 0x1.5555555555555p-5);
+  p = __builtin_fma(p, r, 0x1.5555555555555p-3);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  const int ni = (int)n;
+  return (float)__builtin_ldexp(exp2_tab[ni & 63] * p, ni >> 6);
+}
+
+// 1 / d rounded once, for 1 <= d < 2^126: the hardware reciprocal estimate
+// and one residual correction. Below 2^-126 the estimate flushes to zero, so
+// d >= 2^126 (and d = inf) goes through recip_big instead. Checked, with the
+// exp above, over every d that an fp16 or bf16 z produces.
+__device__ __forceinline__ float recip_rn(float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  const float e = __builtin_fmaf(-d, y, 1.0f);
+  return __builtin_fmaf(e, y, y);
+}
+constexpr float kRecipBig = 0x1p126f;
+__device__ __forceinline__ float recip_big(float d) { return (float)(1.0 / (double)d); }
+
+// The SiLU gate applied to x, in binary32 steps: E = exp(-z) rounded once,
+// d = 1 + E, sigma = 1 / d rounded once, s = z * sigma, u = x * s.
+__device__ __forceinline__ float silu_gate(float x, float z, const double* exp2_tab) {
+  const float d = 1.0f + exp_neg_rn(z, exp2_tab);
+  const float sigma = d >= kRecipBig ? recip_big(d) : recip_rn(d);
   return x * (z * sigma);
+}
+
+// Eight gates at once: the common path is branch-free so the eight exp
+// chains interleave; one branch per vector (never taken unless some z is
+// below about -87.3) redoes the reciprocals of d >= 2^126.
+__device__ __forceinline__ void silu_gate8(const float (&x)[8], const float (&z)[8],
+                                           const double* exp2_tab, float (&u)[8]) {
+  float d[8], sigma[8];
+  bool big = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    d[i] = 1.0f + exp_neg_rn(z[i], exp2_tab);
+    sigma[i] = recip_rn(d[i]);
+    big |= d[i] >= kRecipBig;
+  }
+  if (big) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (d[i] >= kRecipBig) sigma[i] = recip_big(d[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = x[i] * (z[i] * sigma[i]);
 }
 
 // Byte offset of the block scale of row r, block column c in the 128x4-tiled

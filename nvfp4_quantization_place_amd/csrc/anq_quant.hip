@@ -99,23 +99,18 @@ hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t s)
 template <int DT>
 __global__ void __launch_bounds__(256) gate_kernel(const uint8_t* x, const uint8_t* z, float* u,
                                                    int64_t vecs) {
+  __shared__ double exp2_tab[64];
+  fill_exp2_tab(exp2_tab);
+  __syncthreads();
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (v >= vecs) return;
-  float xf[8], zf[8];
+  float xf[8], zf[8], o[8];
   unpack8<DT>(ld16(x + (size_t)v * 16), xf);
   unpack8<DT>(ld16(z + (size_t)v * 16), zf);
-  float4 a, b;
-  a.x = silu_gate(xf[0], zf[0]);
-  a.y = silu_gate(xf[1], zf[1]);
-  a.z = silu_gate(xf[2], zf[2]);
-  a.w = silu_gate(xf[3], zf[3]);
-  b.x = silu_gate(xf[4], zf[4]);
-  b.y = silu_gate(xf[5], zf[5]);
-  b.z = silu_gate(xf[6], zf[6]);
-  b.w = silu_gate(xf[7], zf[7]);
-  float4* o = reinterpret_cast<float4*>(u + (size_t)v * 8);
-  o[0] = a;
-  o[1] = b;
+  silu_gate8(xf, zf, exp2_tab, o);
+  float4* dst = reinterpret_cast<float4*>(u + (size_t)v * 8);
+  dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_float4(o[4], o[5], o[6], o[7]);
 }
 
 hipError_t launch_gate(int dtype, const void* x, const void* z, float* u, int64_t vecs,

@@ -137,6 +137,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 ? 256 : 1024
 tail_kernel(TailParams p) {
   __shared__ double lds[64];
   __shared__ float mult_tab[128];  // NVFP4: G / value(sf) for every block-scale code
+  __shared__ double exp2_tab[64];  // gated: the table of the gate's exp
   const int32_t V = p.vec;
   int lane, L;
   int64_t group;
@@ -187,6 +188,7 @@ tail_kernel(TailParams p) {
   constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz || kGated;
   if constexpr (kNvfp4) {
     fill_mult_tab(mult_tab, sc);
+    if constexpr (kGated) fill_exp2_tab(exp2_tab);
     __syncthreads();
   }
   // gamma stays packed in registers (4 per vector) and is unpacked per row:
@@ -214,8 +216,7 @@ tail_kernel(TailParams p) {
       unpack8<DT>(xv[k], xf);
       unpack8<DT>(rv[k], rf);
       if constexpr (kGated) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[k][i] = silu_gate(xf[i], rf[i]);  // binary32 u
+        silu_gate8(xf, rf, exp2_tab, h[k]);  // binary32 u
       } else {
         float s[8];
 #pragma unroll
@@ -248,7 +249,7 @@ tail_kernel(TailParams p) {
         float xf, zf, unused;
         unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(xrow + voff[k] + 2 * i), xf, unused);
         unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + voff[k] + 2 * i), zf, unused);
-        return silu_gate(xf, zf);
+        return silu_gate(xf, zf, exp2_tab);
       });
     } else {  // the fallback re-reads the lane's own just-stored residual elements
       ss = row_sum_squares<K>(acc, p.hidden, parity, vok, red, [&](int k, int i) {

@@ -319,3 +319,18 @@ def test_separated_tail_validation(L):
         assert op(L, tokens=4, scale=addr(4, 4)) == ALIAS
     assert qnv(L, tokens=4, sf=None) == NULL
     assert qnv(L, tokens=4, sf=addr(4, 32)) == ALIAS         # scales over the codes
+
+
+def test_gate_exp2_table_is_correctly_rounded():
+    """The binary64 literals of the gate's exp table are 2^(j/64), j < 64, each
+    the nearest binary64 (checked with 60-digit decimal arithmetic)."""
+    from decimal import Decimal, localcontext
+    src = open(os.path.join(ROOT, "nvfp4_quantization_place_amd", "csrc", "anq_device.h")).read()
+    body = src[src.index("kExp2Tab[64] = {"):].split("}", 1)[0]
+    vals = [float.fromhex(t) for t in re.findall(r"0x[0-9a-f.]+p[+-]\d+", body)]
+    assert len(vals) == 64
+    with localcontext() as ctx:
+        ctx.prec = 60
+        for j, v in enumerate(vals):
+            exact = Decimal(2) ** (Decimal(j) / 64)
+            assert float(exact) == v, j                      # float(Decimal) rounds to nearest
