@@ -300,13 +300,18 @@ __device__ __forceinline__ float f32_next_down(float f) {
   return f > 0.0f ? __uint_as_float(__float_as_uint(f) - 1u) : 0.0f;
 }
 
-// The binary32 rounding of S (>= 0, a float64 sum of exact squares) is in
-// doubt when S lies within `bound` of a midpoint between two binary32 values.
-__device__ __forceinline__ bool near_f32_midpoint(double S, float f, double bound) {
-  const double fd = (double)f;
-  const double mid_hi = 0.5 * (fd + (double)f32_next_up(f));
-  const double mid_lo = 0.5 * (fd + (double)f32_next_down(f));
-  return __builtin_fabs(S - mid_hi) <= bound || (f > 0.0f && __builtin_fabs(S - mid_lo) <= bound);
+// The binary32 rounding of the exact sum is in doubt when S (>= 0, the
+// float64 sum of `width` exact squares, within width * 2^-53 * S of it) lies
+// within that bound of a midpoint between two binary32 values. In S's binade
+// the bound is below 2 * width float64 ulps, and a binary32 midpoint is a
+// float64 whose low 29 significand bits are 2^28 (midpoints of other binades
+// are at least 2^27 ulps away); so the test is on those bits alone. Nonzero S
+// below the binary32 normal range is always settled exactly; S = 0 is exact.
+__device__ __forceinline__ bool near_f32_midpoint(double S, int32_t width) {
+  if (!(S >= 0x1p-126)) return S != 0.0;
+  const uint32_t low29 = (uint32_t)__builtin_bit_cast(uint64_t, S) & 0x1FFFFFFFu;
+  const uint32_t w2 = 2u * (uint32_t)width;
+  return low29 - (0x10000000u - w2) <= 2u * w2;
 }
 
 // Round hi + lo (a double-double with |lo| <= ulp(hi)/2) to binary32, nearest

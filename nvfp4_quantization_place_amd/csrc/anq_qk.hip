@@ -105,7 +105,7 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
       }
       const double S = lanes_sum<LPH>(acc);
       float ss = (float)S;
-      if (near_f32_midpoint(S, ss, S * (double)D * 0x1p-52)) {
+      if (near_f32_midpoint(S, D)) {
         double hi = 0.0, lo = 0.0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
         lanes_sum_dd<LPH>(hi, lo);
         ss = dd_to_f32(hi, lo);
       }
-      const float r = 1.0f / sqrtf(ss / (float)D + p.eps);
+      const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);  // D = 2^k: exact, as ss / D
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float na = (a[i] * r) * ga[i];

@@ -115,7 +115,7 @@ __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int 
   const double S = red.sum(acc, parity);
   const float ss = (float)S;
   // float64 error of a sum of `width` non-negative terms is below width * 2^-53 * S
-  if (near_f32_midpoint(S, ss, S * (double)width * 0x1p-52))  // uniform over the row
+  if (near_f32_midpoint(S, width))  // uniform over the row
     return row_sum_squares_dd<K>(vok, red, elem);
   return ss;
 }
