@@ -205,9 +205,14 @@ __device__ __forceinline__ float div_rn(float a, float b, float y) {
 // DPP lane moves inside a 16-lane row (VALU, no LDS round trip):
 //   0xB1 quad_perm [1,0,3,2] (lane ^ 1), 0x4E quad_perm [2,3,0,1] (lane ^ 2),
 //   0x141 row_half_mirror (lane i <-> 7 - i within 8), 0x140 row_mirror (i <-> 15 - i).
+// Every lane has a valid source under these patterns and all lanes are active
+// where they are used, so no "old" value is needed (bound_ctrl set): the move
+// needs no register seeded beforehand.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  static_assert(CTRL == 0xB1 || CTRL == 0x4E || CTRL == 0x141 || CTRL == 0x140,
+                "only patterns with a source lane for every lane");
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
