@@ -200,6 +200,19 @@ __device__ __forceinline__ float div_rn(float a, float b, float y) {
   return __builtin_isfinite(q0) ? __builtin_copysignf(q1, q0) : q0;
 }
 
+// a / b rounded once, for a code decision that saturates past 448: a is first
+// clamped to +-c with c = 512 b (exact), so the quotient stays finite and every
+// clamped value still lands past 448, where the E4M3 code of a / b already
+// saturates. The residual is negated after the FMA (-(q0 b - a) = a - q0 b,
+// exact), which keeps the sign of a zero quotient without a copysign; the
+// result is the same Markstein-corrected quotient as div_rn. 4 operations.
+__device__ __forceinline__ float div_rn_sat(float a, float b, float y, float c) {
+  const float ac = __builtin_amdgcn_fmed3f(a, c, -c);
+  const float q0 = ac * y;
+  const float t = __builtin_fmaf(q0, b, -ac);
+  return __builtin_fmaf(-t, y, q0);
+}
+
 // ------------------------------------------------------ cross-lane sums
 
 // DPP lane moves inside a 16-lane row (VALU, no LDS round trip):
@@ -343,8 +356,9 @@ constexpr float kInv6 = 0x1.555556p-3f;  // RN(1/6)
 __device__ __forceinline__ void fp8_codes8(const float (&n)[8], float s, float inv_s, uint32_t& lo,
                                            uint32_t& hi) {
   float t[8];
+  const float c = s * 512.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) t[i] = div_rn(n[i], s, inv_s);
+  for (int i = 0; i < 8; ++i) t[i] = div_rn_sat(n[i], s, inv_s, c);
   lo = e4m3x4(t[0], t[1], t[2], t[3]);
   hi = e4m3x4(t[4], t[5], t[6], t[7]);
 }

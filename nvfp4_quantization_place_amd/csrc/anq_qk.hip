@@ -40,6 +40,7 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
   const int qk_heads = p.nq + p.nk;
   const float sc = *p.scale;
   const float inv_sc = 1.0f / sc;
+  const float sat = sc * 512.0f;  // |o| past this saturates the code: the clamp of div_rn_sat
   const size_t row_elems = (size_t)heads * D;
   const uint8_t* row = static_cast<const uint8_t*>(p.qkv) + (size_t)t * row_elems * 2;
   uint8_t* orow = p.out + (size_t)t * (STORE ? (size_t)p.nq * D : row_elems);
@@ -132,8 +133,8 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      oa[i] = div_rn(oa[i], sc, inv_sc);
-      ob[i] = div_rn(ob[i], sc, inv_sc);
+      oa[i] = div_rn_sat(oa[i], sc, inv_sc, sat);
+      ob[i] = div_rn_sat(ob[i], sc, inv_sc, sat);
     }
     // Lanes 2m and 2m+1 swap one 8-byte half so that each stores 16 contiguous
     // codes: the even lane elements [16m, 16m+16), the odd lane the same range

@@ -179,6 +179,8 @@ tail_kernel(TailParams p) {
       rv[k] = ld16s<NT>(res + rb + voff[k]);
     }
   }
+  const float width_f = (float)p.hidden;  // row width (exact: <= 65536)
+  const float inv_w = 1.0f / width_f;     // RN(1 / width)
   float sc = 0.0f, inv_sc = 0.0f;  // FP8: s and RN(1/s); NVFP4: G
   if constexpr (EPI != kEpiNone) {
     sc = *p.scale;
@@ -258,7 +260,19 @@ tail_kernel(TailParams p) {
         return f;
       });
     }
-    const float r = 1.0f / sqrtf(ss / (float)p.hidden + p.eps);
+    // ss / width rounded once: the Markstein-corrected quotient with RN(1/width)
+    // (three operations) inside the range where it holds with margin, the IEEE
+    // division outside it (sums near underflow or overflow; rare, and uniform
+    // over the row)
+    float mean;
+    if (ss >= 0x1p-100f && ss <= 0x1p120f) {
+      const float q0 = ss * inv_w;
+      const float t = __builtin_fmaf(q0, width_f, -ss);
+      mean = __builtin_fmaf(-t, inv_w, q0);
+    } else {
+      mean = ss / width_f;
+    }
+    const float r = 1.0f / sqrtf(mean + p.eps);
 
     // Codes and block scales are stored without the streaming hint: their 8-,
     // 4- and 1-byte stores only fill whole lines once merged in the L2, and
