@@ -71,7 +71,8 @@
  *    qkv/out/cos_sin/q_out/kv_cache; 4 bytes for scalars and swizzled sf; 8 for
  *    positions and slot_mapping; linear sf has none.
  *  - Left to the caller (not checked): finite inputs, a positive normal
- *    binary32 scale (s or G, so that 1/s is finite), 0 <= positions[t] < max_pos,
+ *    binary32 scale (s or G, so that 1/s is finite; an FP8 s also at most
+ *    2^119, so that 448 s is finite), 0 <= positions[t] < max_pos,
  *    distinct KV slots. Breaking them gives unspecified codes, never an
  *    out-of-bounds access: a position outside [0, max_pos) is clamped into it
  *    and a slot outside [0, num_slots) stores nothing.

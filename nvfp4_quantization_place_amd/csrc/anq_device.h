@@ -138,17 +138,15 @@ __device__ __forceinline__ U4 pack8(const float (&f)[8]) {
 // definition of the op (checked against definition-based encoders over every
 // rounding interval, exact ties included, on the target):
 //  * v_cvt_pk_fp8_f32 converts to OCP E4M3FN, nearest even, signed zeros kept,
-//    subnormals kept; it returns NaN beyond +-448, so inputs are first clamped
-//    with v_med3_f32 (saturation to +-448 is the nearest-even result there).
+//    subnormals kept; it returns NaN beyond +-448, so its inputs are either
+//    bounded by construction (div_rn_sat) or first clamped with v_med3_f32
+//    (saturation to +-448 is the nearest-even result there).
 //  * v_cvt_scalef32_pk_fp4_f32 with scale 1.0 converts to E2M1, nearest even,
 //    saturating at +-6, sign copied; the first operand goes to the low nibble.
 
-// Four binary32 values -> four E4M3FN codes, element i in byte i.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  a = __builtin_amdgcn_fmed3f(a, 448.0f, -448.0f);
-  b = __builtin_amdgcn_fmed3f(b, 448.0f, -448.0f);
-  c = __builtin_amdgcn_fmed3f(c, 448.0f, -448.0f);
-  d = __builtin_amdgcn_fmed3f(d, 448.0f, -448.0f);
+// Four binary32 values within +-448 (the quotients of div_rn_sat) -> four
+// E4M3FN codes, element i in byte i.
+__device__ __forceinline__ uint32_t e4m3x4_in_range(float a, float b, float c, float d) {
   uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
@@ -200,12 +198,19 @@ __device__ __forceinline__ float div_rn(float a, float b, float y) {
   return __builtin_isfinite(q0) ? __builtin_copysignf(q1, q0) : q0;
 }
 
-// a / b rounded once, for a code decision that saturates past 448: a is first
-// clamped to +-c with c = 512 b (exact), so the quotient stays finite and every
-// clamped value still lands past 448, where the E4M3 code of a / b already
-// saturates. The residual is negated after the FMA (-(q0 b - a) = a - q0 b,
-// exact), which keeps the sign of a zero quotient without a copysign; the
-// result is the same Markstein-corrected quotient as div_rn. 4 operations.
+// a / b rounded once, for an E4M3 code decision: a is first clamped to +-c
+// with c = the largest binary32 <= 448 b (sat_bound), so the quotient is at
+// most 448 in magnitude (the converter needs no clamp of its own) and a
+// clamped quotient lies in [432, 448], which has the saturated code 448 that
+// every |a / b| >= 448 has. The residual is negated after the FMA
+// (-(q0 b - a) = a - q0 b, exact), which keeps the sign of a zero quotient
+// without a copysign; the result is otherwise div_rn's Markstein-corrected
+// quotient. 4 operations. Requires 448 b finite.
+__device__ __forceinline__ float sat_bound(float b) {
+  float c = 448.0f * b;                                        // RN(448 b)
+  if (__builtin_fmaf(-448.0f, b, c) > 0.0f) c = __uint_as_float(__float_as_uint(c) - 1u);
+  return c;                                                    // the largest binary32 <= 448 b
+}
 __device__ __forceinline__ float div_rn_sat(float a, float b, float y, float c) {
   const float ac = __builtin_amdgcn_fmed3f(a, c, -c);
   const float q0 = ac * y;
@@ -356,11 +361,11 @@ constexpr float kInv6 = 0x1.555556p-3f;  // RN(1/6)
 __device__ __forceinline__ void fp8_codes8(const float (&n)[8], float s, float inv_s, uint32_t& lo,
                                            uint32_t& hi) {
   float t[8];
-  const float c = s * 512.0f;
+  const float c = sat_bound(s);
 #pragma unroll
   for (int i = 0; i < 8; ++i) t[i] = div_rn_sat(n[i], s, inv_s, c);
-  lo = e4m3x4(t[0], t[1], t[2], t[3]);
-  hi = e4m3x4(t[4], t[5], t[6], t[7]);
+  lo = e4m3x4_in_range(t[0], t[1], t[2], t[3]);
+  hi = e4m3x4_in_range(t[4], t[5], t[6], t[7]);
 }
 
 // NVFP4 multipliers G / value(c) for the 127 non-negative E4M3 codes (0 for c = 0

@@ -40,7 +40,7 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
   const int qk_heads = p.nq + p.nk;
   const float sc = *p.scale;
   const float inv_sc = 1.0f / sc;
-  const float sat = sc * 512.0f;  // |o| past this saturates the code: the clamp of div_rn_sat
+  const float sat = sat_bound(sc);  // the numerator clamp of div_rn_sat
   const size_t row_elems = (size_t)heads * D;
   const uint8_t* row = static_cast<const uint8_t*>(p.qkv) + (size_t)t * row_elems * 2;
   uint8_t* orow = p.out + (size_t)t * (STORE ? (size_t)p.nq * D : row_elems);
@@ -139,8 +139,10 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
     // Lanes 2m and 2m+1 swap one 8-byte half so that each stores 16 contiguous
     // codes: the even lane elements [16m, 16m+16), the odd lane the same range
     // of the second half. Every head's output then leaves as whole lines.
-    const uint32_t a0 = e4m3x4(oa[0], oa[1], oa[2], oa[3]), a1 = e4m3x4(oa[4], oa[5], oa[6], oa[7]);
-    const uint32_t b0 = e4m3x4(ob[0], ob[1], ob[2], ob[3]), b1 = e4m3x4(ob[4], ob[5], ob[6], ob[7]);
+    const uint32_t a0 = e4m3x4_in_range(oa[0], oa[1], oa[2], oa[3]);
+    const uint32_t a1 = e4m3x4_in_range(oa[4], oa[5], oa[6], oa[7]);
+    const uint32_t b0 = e4m3x4_in_range(ob[0], ob[1], ob[2], ob[3]);
+    const uint32_t b1 = e4m3x4_in_range(ob[4], ob[5], ob[6], ob[7]);
     const bool odd = (j & 1) != 0;
     const uint32_t r0 = dpp_u32<0xB1>(odd ? a0 : b0), r1 = dpp_u32<0xB1>(odd ? a1 : b1);
     uint8_t* dst = orow + (size_t)h * D;
