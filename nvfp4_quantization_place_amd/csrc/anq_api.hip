@@ -2,6 +2,7 @@
 // tiling choice and launch. The contract of every entry point is stated in
 // include/addnormq.h.
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 
 #include "../../include/addnormq.h"
@@ -187,10 +188,17 @@ extern "C" int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const voi
   p.hidden = (int32_t)group;
   p.vec = (int32_t)(group / 8);
   p.gamma_period = (int32_t)(hidden / group);
-  const anq::Tiling t = anq::pick_tail_tiling(p.vec, p.tokens);
+  // bf16 z, groups of at most 1024 and enough rows to share a workgroup's
+  // table: the gate from the lookup table (ANQ_GATE_LUT=0/1 overrides, for A/B runs)
+  bool lut = dtype == ANQ_BF16 && group <= 1024 && p.tokens >= 16384;
+  if (const char* e = getenv("ANQ_GATE_LUT")) {
+    if (*e) lut = atoi(e) != 0 && dtype == ANQ_BF16 && group <= 1024;
+  }
+  const anq::Tiling t = lut ? anq::pick_gate_lut_tiling(p.vec, p.tokens)
+                            : anq::pick_tail_tiling(p.vec, p.tokens);
   p.rows_per_group = t.rows;
-  return launch_status(anq::launch_tail(dtype, anq::kEpiGatedNvfp4, false, p, t,
-                                        static_cast<hipStream_t>(stream)));
+  return launch_status(anq::launch_tail(dtype, lut ? anq::kEpiGatedNvfp4Lut : anq::kEpiGatedNvfp4,
+                                        false, p, t, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int silu_gate_f32(const void* x, const void* z, int64_t n, int dtype, float* u,

@@ -485,6 +485,49 @@ __device__ __forceinline__ void silu_gate8(const float (&x)[8], const float (&z)
   for (int i = 0; i < 8; ++i) u[i] = x[i] * (z[i] * sigma[i]);
 }
 
+// ------------------------------------------------ bf16 gate lookup table
+//
+// For bf16 z the gate value s(z) = z * sigma(z) (the silu_gate steps with x = 1)
+// depends on z's 16 bits only. With |z| < 2^-25, exp(-z) rounds to 1, so
+// s = z / 2; with |z| >= 128 it rounds to 0 (z > 0, s = z) or overflows
+// (z < 0, s = -0). Between, there are 32 binades x 128 significands per sign:
+// an 8192-entry binary32 table, index (bf16 bits & 0x7FFF) - (102 << 7) plus
+// 4096 for negative z. A workgroup fills it from silu_gate itself, so a looked
+// up value is bit-identical to the computed one; values outside the table take
+// the computed path.
+constexpr int kGateTab = 8192;
+constexpr uint32_t kGateTabLo = 102u << 7;  // bf16 exponent field 102: 2^-25
+
+__device__ __forceinline__ void fill_gate_tab(float* tab, const double* exp2_tab) {
+  for (int j = threadIdx.x; j < kGateTab; j += blockDim.x) {
+    const uint32_t b = ((uint32_t)(j & 4095) + kGateTabLo) | ((uint32_t)(j >> 12) << 15);
+    tab[j] = silu_gate(1.0f, __uint_as_float(b << 16), exp2_tab);
+  }
+}
+
+// u_i = x_i * s(z_i) for the eight bf16 z of zv (the silu_gate8 result).
+__device__ __forceinline__ void gate_lut8(const float (&x)[8], const U4& zv, const float* tab,
+                                          const double* exp2_tab, float (&u)[8]) {
+  float s[8];
+  bool outside = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = (i & 1) ? (zv.w[i >> 1] >> 16) : (zv.w[i >> 1] & 0xFFFFu);
+    const uint32_t t = (b & 0x7FFFu) - kGateTabLo;  // wraps below the table
+    outside |= t >= 4096u;
+    s[i] = tab[(t & 4095u) | ((b >> 3) & 4096u)];
+  }
+  if (outside) {  // rare for activations: |z| < 2^-25 or |z| >= 128 somewhere in the vector
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = (i & 1) ? (zv.w[i >> 1] >> 16) : (zv.w[i >> 1] & 0xFFFFu);
+      if ((b & 0x7FFFu) - kGateTabLo >= 4096u) s[i] = silu_gate(1.0f, __uint_as_float(b << 16), exp2_tab);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = x[i] * s[i];
+}
+
 // Byte offset of the block scale of row r, block column c in the 128x4-tiled
 // scale layout of block-scaled GEMM operands: rows padded to 128, scale
 // columns to 4; tile (r / 128, c / 4) is 512 contiguous bytes, tiles row-major

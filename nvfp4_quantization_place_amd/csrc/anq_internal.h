@@ -10,7 +10,12 @@ namespace anq {
 // (its own instantiation, so the linear-layout kernel carries none of its code).
 // kEpiGatedNvfp4: the gated variant, n = RMSNorm(x * SiLU(z)) * gamma per row
 // of `hidden` (a group), NVFP4 codes; `residual` then holds z (read only).
-enum Epilogue { kEpiFp8 = 0, kEpiNvfp4 = 1, kEpiNone = 2, kEpiNvfp4Swz = 3, kEpiGatedNvfp4 = 4 };
+// kEpiGatedNvfp4Lut: the same with bf16 z and the gate from an 8192-entry LDS
+// table (32 KiB of dynamic shared memory), for calls with many rows.
+enum Epilogue {
+  kEpiFp8 = 0, kEpiNvfp4 = 1, kEpiNone = 2, kEpiNvfp4Swz = 3, kEpiGatedNvfp4 = 4,
+  kEpiGatedNvfp4Lut = 5
+};
 
 struct TailParams {
   const void* x;
@@ -44,6 +49,7 @@ struct Tiling {
 };
 
 Tiling pick_tail_tiling(int32_t vec, int64_t tokens);
+Tiling pick_gate_lut_tiling(int32_t vec, int64_t rows);
 
 hipError_t launch_tail(int dtype, int epi, bool norm_out, const TailParams& p, const Tiling& t,
                        hipStream_t stream);

@@ -133,7 +133,8 @@ __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int 
 // for the gated variant (its binary64 exp needs the registers).
 template <int DT, int EPI, bool NORM, int K, int G, bool NT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 ? 256 : 1024),
-                               amdgpu_waves_per_eu(K == 1 && EPI != kEpiGatedNvfp4 ? 7 : 4)))
+                               amdgpu_waves_per_eu(K == 1 && EPI != kEpiGatedNvfp4 &&
+                                                           EPI != kEpiGatedNvfp4Lut ? 7 : 4)))
 tail_kernel(TailParams p) {
   __shared__ double lds[64];
   __shared__ float mult_tab[128];  // NVFP4: G / value(sf) for every block-scale code
@@ -186,11 +187,18 @@ tail_kernel(TailParams p) {
     sc = *p.scale;
     inv_sc = 1.0f / sc;  // correctly rounded division
   }
-  constexpr bool kGated = EPI == kEpiGatedNvfp4;  // `res` is z: read only, never stored
+  constexpr bool kLut = EPI == kEpiGatedNvfp4Lut;  // bf16 z, gate from the LDS table
+  constexpr bool kGated = EPI == kEpiGatedNvfp4 || kLut;  // `res` is z: read only, never stored
   constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz || kGated;
   if constexpr (kNvfp4) {
     fill_mult_tab(mult_tab, sc);
     if constexpr (kGated) fill_exp2_tab(exp2_tab);
+    __syncthreads();
+  }
+  extern __shared__ float gate_tab[];  // kLut: kGateTab entries (dynamic shared memory)
+  if constexpr (kLut) {
+    static_assert(DT == kBF16, "the gate table covers bf16 z");
+    fill_gate_tab(gate_tab, exp2_tab);
     __syncthreads();
   }
   // gamma stays packed in registers (4 per vector) and is unpacked per row:
@@ -217,7 +225,9 @@ tail_kernel(TailParams p) {
       float xf[8], rf[8];
       unpack8<DT>(xv[k], xf);
       unpack8<DT>(rv[k], rf);
-      if constexpr (kGated) {
+      if constexpr (kLut) {
+        gate_lut8(xf, rv[k], gate_tab, exp2_tab, h[k]);  // binary32 u, looked up
+      } else if constexpr (kGated) {
         silu_gate8(xf, rf, exp2_tab, h[k]);  // binary32 u
       } else {
         float s[8];
@@ -375,6 +385,30 @@ Tiling pick_tail_tiling(int32_t vec, int64_t tokens) {
   return t;
 }
 
+// Tiling of the gated variant with the gate table (rows <= 1024 elements):
+// lane groups of 16/32/64 lanes, one or two vectors per lane, four to sixteen
+// lane groups per 256-lane workgroup, each walking enough consecutive rows that
+// about 1024 workgroups cover the call, so each workgroup fills its table once
+// for many rows. ANQ_ROWS_PER_GROUP and ANQ_STREAM override, as above.
+Tiling pick_gate_lut_tiling(int32_t vec, int64_t rows) {
+  Tiling t{};
+  t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
+  t.vec_per_lane = vec <= 64 ? 1 : 2;
+  t.block = 256;
+  const int64_t groups_per_block = 256 / t.group;
+  int64_t r = rows / (groups_per_block * 1024);
+  t.rows = (int)(r < 1 ? 1 : (r > 64 ? 64 : r));
+  const int env_rows = env_int("ANQ_ROWS_PER_GROUP", 0);
+  if (env_rows > 0) t.rows = env_rows;
+  t.stream = (int64_t)vec * 16 * rows >= ((int64_t)32 << 20);
+  const int env_stream = env_int("ANQ_STREAM", -1);
+  if (env_stream >= 0) t.stream = env_stream != 0;
+  const int64_t kMaxGrid = 0x7FFFFFFF;
+  while ((rows + groups_per_block * t.rows - 1) / (groups_per_block * t.rows) > kMaxGrid) t.rows *= 2;
+  t.grid = (rows + groups_per_block * t.rows - 1) / (groups_per_block * t.rows);
+  return t;
+}
+
 template <int DT, int EPI, bool NORM, bool NT>
 static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
   void* args[] = {const_cast<TailParams*>(&p)};
@@ -388,7 +422,8 @@ static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
   else if (t.group == 0 && t.vec_per_lane == 4) fn = (const void*)&tail_kernel<DT, EPI, NORM, 4, 0, NT>;
   else if (t.group == 0 && t.vec_per_lane == 8) fn = (const void*)&tail_kernel<DT, EPI, NORM, 8, 0, NT>;
   if (!fn) return hipErrorInvalidConfiguration;
-  return hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3((unsigned)t.block), args, 0, s);
+  const size_t dyn_lds = EPI == kEpiGatedNvfp4Lut ? kGateTab * sizeof(float) : 0;
+  return hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3((unsigned)t.block), args, dyn_lds, s);
 }
 
 template <int DT, int EPI, bool NORM>
@@ -406,6 +441,10 @@ static hipError_t launch1(int epi, bool norm, const TailParams& p, const Tiling&
   if (epi == kEpiNone) return launch3<DT, kEpiNone, true>(p, t, s);  // add + RMSNorm only
   if (epi == kEpiNvfp4Swz) return launch2<DT, kEpiNvfp4Swz>(norm, p, t, s);
   if (epi == kEpiGatedNvfp4) return launch3<DT, kEpiGatedNvfp4, false>(p, t, s);  // no norm out
+  if constexpr (DT == kBF16) {
+    if (epi == kEpiGatedNvfp4Lut) return launch3<DT, kEpiGatedNvfp4Lut, false>(p, t, s);
+  }
+  if (epi == kEpiGatedNvfp4Lut) return hipErrorInvalidValue;  // the table covers bf16 z only
   return epi == kEpiFp8 ? launch2<DT, kEpiFp8>(norm, p, t, s) : launch2<DT, kEpiNvfp4>(norm, p, t, s);
 }
 

@@ -162,3 +162,43 @@ def test_gated_workload_size():
     np.testing.assert_array_equal(sf[rows], ref["sf"])
     np.testing.assert_array_equal(q[rows], ref["q"])
     assert not np.any((sf & 0x7F) == 0x7F) and not np.any(sf & 0x80)
+
+
+@pytest.mark.parametrize("tokens,hidden,group", [(5, 64, 16), (37, 1024, 1024), (37, 1024, 128),
+                                                 (64, 8192, 1024), (9, 2048, 64), (130, 4096, 512)])
+@pytest.mark.parametrize("rows", ["", "1", "3"])
+def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, monkeypatch):
+    """The bf16 gate read from the workgroup's LDS table (forced on small
+    calls), with several rows per lane group, gives the oracle's codes."""
+    monkeypatch.setenv("ANQ_GATE_LUT", "1")
+    monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
+    inp = W.make_gated(hidden + 7 * group + tokens, "bf16", tokens, hidden, group,
+                       z=("normal", 3.0), eps=1e-5)
+    G = float(O.nvfp4_global_scale(_oracle(inp, 1.0)["n"]))
+    q, sf = _run(inp, G)
+    ref = _oracle(inp, G)
+    np.testing.assert_array_equal(sf, ref["sf"])
+    np.testing.assert_array_equal(q, ref["q"])
+
+
+def test_gated_table_path_edge_rows(monkeypatch):
+    """Gates outside the table (|z| < 2^-25, |z| >= 128, z = 0) next to table
+    entries in one vector, and every bf16 z in the table's range once."""
+    monkeypatch.setenv("ANQ_GATE_LUT", "1")
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    z = O.t_decode(b, "bf16")
+    b = b[np.isfinite(z) & (np.abs(z) < 1e4)]
+    rng = np.random.default_rng(12)
+    rng.shuffle(b)
+    H = 256
+    b = np.concatenate([b, np.zeros((-len(b)) % H, np.uint16)]).reshape(-1, H)
+    x = O.t_encode((1 + 0.5 * rng.standard_normal(b.shape)).astype(np.float32), "bf16")
+    tdt = torch.bfloat16
+    inp = W.TailInputs(name="edge", op="gated", dtype="bf16", tokens=b.shape[0], hidden=H,
+                       x=_from_bits(x, "bf16"), residual=_from_bits(b, "bf16"),
+                       gamma=torch.ones(H, dtype=tdt), eps=1e-6, scale=None, norm_out=False,
+                       meta={"group": 64})
+    q, sf = _run(inp, 300.0)
+    ref = _oracle(inp, 300.0)
+    np.testing.assert_array_equal(sf, ref["sf"])
+    np.testing.assert_array_equal(q, ref["q"])
