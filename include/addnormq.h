@@ -79,6 +79,9 @@
  *  - Intermediate binary32 results that overflow (n, n / s, G * amax / 6,
  *    n * mult, reachable with bf16 gamma near its maximum) are infinities, and
  *    the encoders saturate them like any value past the top code.
+ *  - With eps = 0, a row (or group) whose mean square is 0 has r = inf, and its
+ *    zero elements give n = 0 * inf = NaN; the codes of such blocks are
+ *    unspecified. Any eps > 0 keeps r finite.
  *  - Calls that share output buffers and overlap in time on different streams
  *    race; calls on one stream are ordered.
  */

@@ -142,7 +142,9 @@ __device__ __forceinline__ U4 pack8(const float (&f)[8]) {
 //    bounded by construction (div_rn_sat) or first clamped with v_med3_f32
 //    (saturation to +-448 is the nearest-even result there).
 //  * v_cvt_scalef32_pk_fp4_f32 with scale 1.0 converts to E2M1, nearest even,
-//    saturating at +-6, sign copied; the first operand goes to the low nibble.
+//    sign copied, and saturates every value past +-6 (infinities included) to
+//    the signed top code, which is the nearest-even result there; the first
+//    operand goes to the low nibble.
 
 // Four binary32 values within +-448 (the quotients of div_rn_sat) -> four
 // E4M3FN codes, element i in byte i.
@@ -165,17 +167,14 @@ __device__ __forceinline__ float e4m3_value_pos(uint32_t c) {
 }
 
 // Eight binary32 values -> eight E2M1 codes, element i in bits 4i..4i+3. The
-// clamp to +-6 (the nearest-even result beyond 6) keeps infinities, which a
-// block's n * mult can reach, out of the converter.
+// converter's own saturation covers the infinities a block's n * mult can
+// reach, so no clamp precedes it.
 __device__ __forceinline__ uint32_t e2m1x8(const float (&v)[8]) {
-  float c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(v[i], 6.0f, -6.0f);
   uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[0], c[1], 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[2], c[3], 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[4], c[5], 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[6], c[7], 1.0f, 3);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
   return w;
 }
 
