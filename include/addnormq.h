@@ -72,7 +72,9 @@
  *    positions and slot_mapping; linear sf has none.
  *  - Left to the caller (not checked): finite inputs, a positive normal
  *    binary32 scale (s or G, so that 1/s is finite; an FP8 s also at most
- *    2^119, so that 448 s is finite), 0 <= positions[t] < max_pos,
+ *    2^119, so that 448 s is finite; an NVFP4 G below 2^119, so that every
+ *    multiplier G / value(sf) is finite and no zero element meets an infinite
+ *    one), 0 <= positions[t] < max_pos,
  *    distinct KV slots. Breaking them gives unspecified codes, never an
  *    out-of-bounds access: a position outside [0, max_pos) is clamped into it
  *    and a slot outside [0, num_slots) stores nothing.

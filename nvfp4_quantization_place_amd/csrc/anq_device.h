@@ -181,30 +181,63 @@ __device__ __forceinline__ uint32_t e2m1x8(const float (&v)[8]) {
 // ---------------------------------------------------------------- division
 
 
-// Correctly rounded a / b from y = RN(1/b): q0 = RN(a*y) is within an ulp of
-// a/b, the remainder a - b*q0 is exact in one FMA, and q0 + rem*y rounded once
-// is RN(a/b) (Markstein's correction theorem). Where a/b is below the normal
-// binary32 range the result may be an ulp off, but every encoder here maps all
-// such values to a zero of the quotient's sign. The sign of q0 is carried over
-// so that a = -0 keeps its sign like IEEE division.
-__device__ __forceinline__ float div_rn(float a, float b, float y) {
-  const float q0 = a * y;
-  const float rem = __builtin_fmaf(-q0, b, a);
-  const float q1 = __builtin_fmaf(rem, y, q0);
-  // q0 = +-inf (a infinite, or a/b at the top of the range): the correction
-  // would be inf - inf; the quotient is then at least the largest finite value
-  // in magnitude, which every encoder here saturates, so q0 stands.
-  return __builtin_isfinite(q0) ? __builtin_copysignf(q1, q0) : q0;
+// 1 / b rounded once, for a normal b < 2^126: the hardware reciprocal estimate
+// y and one residual correction, y + y (1 - b y), the residual exact in one
+// FMA. An exhaustive GPU check over every normal binary32 b below 2^120 gave
+// the IEEE quotient bit for bit. From 2^126 up the quotient is subnormal and
+// the estimate flushes it to zero, so callers stay below that.
+__device__ __forceinline__ float recip_rn(float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  const float e = __builtin_fmaf(-d, y, 1.0f);
+  return __builtin_fmaf(e, y, y);
 }
 
-// a / b rounded once, for an E4M3 code decision: a is first clamped to +-c
-// with c = the largest binary32 <= 448 b (sat_bound), so the quotient is at
-// most 448 in magnitude (the converter needs no clamp of its own) and a
-// clamped quotient lies in [432, 448], which has the saturated code 448 that
-// every |a / b| >= 448 has. The residual is negated after the FMA
-// (-(q0 b - a) = a - q0 b, exact), which keeps the sign of a zero quotient
-// without a copysign; the result is otherwise div_rn's Markstein-corrected
-// quotient. 4 operations. Requires 448 b finite.
+// recip_rn extended to d = +0 and d = +inf (r = 1 / sqrt(mean + eps) with eps = 0
+// or an overflowing mean): there the correction is NaN, and the estimate alone
+// is already the IEEE result (+inf, +0).
+__device__ __forceinline__ float recip_rn_ext(float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  const float y1 = __builtin_fmaf(__builtin_fmaf(-d, y, 1.0f), y, y);
+  return __builtin_isfinite(y1) ? y1 : y;
+}
+
+// amax / 6 rounded once, for amax >= +0 (the NVFP4 block scale's quotient):
+// q0 = RN(amax RN(1/6)), the remainder amax - 6 q0 exact in one FMA, and
+// q0 + rem RN(1/6) rounded once (Markstein's correction). An exhaustive GPU
+// check over every non-negative binary32 found it exact for amax >= 2^-125 and
+// an ulp off for some smaller amax, where the quotient is subnormal; a large G
+// (>= 2^120 in the same check) carries that ulp into the scale code. Those
+// blocks, whose every |n| is below 2^-125, take a branch: amax = k 2^-149 with
+// k < 2^24 is scaled by 2^48 (exact), divided in the normal range and scaled
+// back. k/6 has at most 22 integer bits, so the first rounding keeps at least
+// two fraction bits; a fraction of 1/6, 1/3, 2/3 or 5/6 then cannot round
+// across one half, and a half stays exact, so the second rounding gives
+// RN(amax / 6). amax = +inf makes the correction NaN; q0 = inf stands and the
+// code saturates.
+__device__ __forceinline__ float amax_div6(float am) {
+  constexpr float kInv6 = 0x1.555556p-3f;  // RN(1/6)
+  const float q0 = am * kInv6;
+  float q = q0 < __builtin_inff() ? __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, am), kInv6, q0) : q0;
+  if (__float_as_uint(am) - 1u < 0x00FFFFFFu) {  // 0 < amax < 2^-125
+    asm volatile("");  // keeps this a branch: it is almost never taken
+    const float a = am * 0x1p48f;
+    const float p0 = a * kInv6;
+    q = __builtin_fmaf(__builtin_fmaf(-p0, 6.0f, a), kInv6, p0) * 0x1p-48f;
+  }
+  return q;
+}
+
+// a / b rounded once, for an E4M3 code decision, from y = RN(1/b): q0 = RN(a y)
+// is within an ulp of a/b, the remainder a - b q0 is exact in one FMA, and
+// q0 + rem y rounded once is RN(a/b) while the quotient is normal (Markstein's
+// correction). a is first clamped to +-c with c = the largest binary32
+// <= 448 b (sat_bound), so the quotient is at most 448 in magnitude (the
+// converter needs no clamp of its own) and a clamped quotient lies in
+// [432, 448], which has the saturated code 448 that every |a / b| >= 448 has.
+// The residual is negated after the FMA (-(q0 b - a) = a - q0 b, exact), which
+// keeps the sign of a zero quotient without a copysign. 4 operations. Requires 448 b finite. Checked exhaustively at the
+// code level: for every binary32 a (subnormal quotients included) and 13
+// scales from 2^-126 to 2^119, the E4M3 code equals that of the IEEE quotient.
 __device__ __forceinline__ float sat_bound(float b) {
   float c = 448.0f * b;                                        // RN(448 b)
   if (__builtin_fmaf(-448.0f, b, c) > 0.0f) c = __uint_as_float(__float_as_uint(c) - 1u);
@@ -354,8 +387,6 @@ __device__ __forceinline__ float dd_to_f32(double hi, double lo) {
 // Shared by the fused tail and the standalone quantisers, so both encode with
 // the same instructions.
 
-constexpr float kInv6 = 0x1.555556p-3f;  // RN(1/6)
-
 // FP8: codes of n_i / s for eight values (s = dequant scale, inv_s = RN(1/s)).
 __device__ __forceinline__ void fp8_codes8(const float (&n)[8], float s, float inv_s, uint32_t& lo,
                                            uint32_t& hi) {
@@ -384,8 +415,11 @@ __device__ __forceinline__ void nvfp4_half_block(const float (&n)[8], float G, c
   float am = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(n[i]));
-  am = fmaxf(am, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(am))));  // other half
-  sfc = e4m3_pos(G * div_rn(am, 6.0f, kInv6));
+  // the other half's amax; both are non-negative (fmaxf drops NaN), and such
+  // binary32 values order as their bit patterns
+  const uint32_t ab = __float_as_uint(am);
+  am = __uint_as_float(max(ab, dpp_u32<0xB1>(ab)));
+  sfc = e4m3_pos(G * amax_div6(am));
   const float mult = mult_tab[sfc & 0x7Fu];  // in the table whatever the input (NaN gives 0x7F)
   float t[8];
 #pragma unroll
@@ -442,15 +476,8 @@ __device__ __forceinline__ float exp_neg_rn(float z, const double* exp2_tab) {
   return (float)__builtin_ldexp(exp2_tab[ni & 63] * p, ni >> 6);
 }
 
-// 1 / d rounded once, for 1 <= d < 2^126: the hardware reciprocal estimate
-// and one residual correction. Below 2^-126 the estimate flushes to zero, so
-// d >= 2^126 (and d = inf) goes through recip_big instead. Checked, with the
-// exp above, over every d that an fp16 or bf16 z produces.
-__device__ __forceinline__ float recip_rn(float d) {
-  const float y = __builtin_amdgcn_rcpf(d);
-  const float e = __builtin_fmaf(-d, y, 1.0f);
-  return __builtin_fmaf(e, y, y);
-}
+// The gate's sigma = 1 / d uses recip_rn for d < 2^126 and binary64 division
+// (recip_big) above, where the estimate would flush the subnormal quotient.
 constexpr float kRecipBig = 0x1p126f;
 __device__ __forceinline__ float recip_big(float d) { return (float)(1.0 / (double)d); }
 

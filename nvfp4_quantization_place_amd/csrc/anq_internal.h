@@ -26,6 +26,7 @@ struct TailParams {
   uint8_t* q;
   uint8_t* sf;         // NVFP4 only
   float eps;
+  float inv_w;         // RN(1 / hidden), set by launch_tail
   int64_t tokens;
   int32_t hidden;
   int32_t vec;         // hidden / 8: 16-byte vectors per row

@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
   const int heads = p.nq + p.nk + p.nv;
   const int qk_heads = p.nq + p.nk;
   const float sc = *p.scale;
-  const float inv_sc = 1.0f / sc;
+  const float inv_sc = recip_rn(sc);  // s is a positive normal <= 2^119
   const float sat = sat_bound(sc);  // the numerator clamp of div_rn_sat
   const size_t row_elems = (size_t)heads * D;
   const uint8_t* row = static_cast<const uint8_t*>(p.qkv) + (size_t)t * row_elems * 2;
@@ -116,7 +116,7 @@ __global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
         lanes_sum_dd<LPH>(hi, lo);
         ss = dd_to_f32(hi, lo);
       }
-      const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);  // D = 2^k: exact, as ss / D
+      const float r = recip_rn_ext(sqrtf(ss * (1.0f / D) + p.eps));  // D = 2^k: exact, as ss / D
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float na = (a[i] * r) * ga[i];

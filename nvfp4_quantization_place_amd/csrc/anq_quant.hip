@@ -24,7 +24,7 @@ __global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
   __shared__ float mult_tab[128];
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const float sc = *p.scale;  // FP8: s, NVFP4: G
-  const float inv_sc = 1.0f / sc;
+  const float inv_sc = recip_rn(sc);  // s is a positive normal <= 2^119
   if constexpr (kNvfp4) {
     fill_mult_tab(mult_tab, sc);
     __syncthreads();

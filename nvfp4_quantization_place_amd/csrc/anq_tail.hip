@@ -181,11 +181,11 @@ tail_kernel(TailParams p) {
     }
   }
   const float width_f = (float)p.hidden;  // row width (exact: <= 65536)
-  const float inv_w = 1.0f / width_f;     // RN(1 / width)
+  const float inv_w = p.inv_w;            // RN(1 / width)
   float sc = 0.0f, inv_sc = 0.0f;  // FP8: s and RN(1/s); NVFP4: G
   if constexpr (EPI != kEpiNone) {
     sc = *p.scale;
-    inv_sc = 1.0f / sc;  // correctly rounded division
+    if constexpr (EPI == kEpiFp8) inv_sc = recip_rn(sc);  // s is a positive normal <= 2^119
   }
   constexpr bool kLut = EPI == kEpiGatedNvfp4Lut;  // bf16 z, gate from the LDS table
   constexpr bool kGated = EPI == kEpiGatedNvfp4 || kLut;  // `res` is z: read only, never stored
@@ -282,7 +282,7 @@ tail_kernel(TailParams p) {
     } else {
       mean = ss / width_f;
     }
-    const float r = 1.0f / sqrtf(mean + p.eps);
+    const float r = recip_rn_ext(sqrtf(mean + p.eps));
 
     // Codes and block scales are stored without the streaming hint: their 8-,
     // 4- and 1-byte stores only fill whole lines once merged in the L2, and
@@ -448,8 +448,10 @@ static hipError_t launch1(int epi, bool norm, const TailParams& p, const Tiling&
   return epi == kEpiFp8 ? launch2<DT, kEpiFp8>(norm, p, t, s) : launch2<DT, kEpiNvfp4>(norm, p, t, s);
 }
 
-hipError_t launch_tail(int dtype, int epi, bool norm, const TailParams& p, const Tiling& t,
+hipError_t launch_tail(int dtype, int epi, bool norm, const TailParams& p_in, const Tiling& t,
                        hipStream_t s) {
+  TailParams p = p_in;
+  p.inv_w = 1.0f / (float)p.hidden;  // IEEE binary32 division on the host
   return dtype == kBF16 ? launch1<kBF16>(epi, norm, p, t, s) : launch1<kF16>(epi, norm, p, t, s);
 }
 

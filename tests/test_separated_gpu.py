@@ -110,6 +110,58 @@ def test_quant_nvfp4_every_finite_input(dtype, gscale):
     np.testing.assert_array_equal(_np(q), rq)
 
 
+@pytest.mark.parametrize("gscale", [2.0 ** 118, 1.5 * 2.0 ** 118, 1.1875 * 2.0 ** 118,
+                                    float.fromhex("0x1.fffffep118")])
+def test_quant_nvfp4_tiny_blocks_huge_global_scale(gscale):
+    """Blocks whose every |value| is below 2^-125 (bf16 subnormals and the
+    lowest normal binade), under global scales large enough that the last ulp
+    of amax / 6, a subnormal binary32, decides the block-scale code (G stays
+    below 2^119, so every multiplier G / value(sf) is finite). Each such
+    value is the amax of one block of zeros and of one block of smaller tiny
+    values, so every subnormal quotient the input can give is met."""
+    b = _finite_patterns("bf16")
+    mag = np.abs(O.t_decode(b, "bf16"))
+    tiny = b[(mag > 0) & (mag < 2.0 ** -125)]
+    tmag = np.abs(O.t_decode(tiny, "bf16"))
+    rng = np.random.default_rng(29)
+    blocks = []
+    for lead, m in zip(tiny, tmag):
+        blocks.append(np.concatenate([[lead], np.zeros(15, np.uint16)]))
+        pool = tiny[tmag <= m]
+        blk = rng.choice(pool, 16)
+        blk[rng.integers(16)] = lead
+        blocks.append(blk)
+    hidden = 256
+    flat = np.concatenate(blocks).astype(np.uint16)
+    flat = np.concatenate([flat, np.zeros((-len(flat)) % hidden, np.uint16)]).reshape(-1, hidden)
+    q, sf = _A().quant_nvfp4(_from_bits(flat, "bf16").cuda(), _dev_scalar(gscale))
+    rq, rsf = O.quant_nvfp4(O.t_decode(flat, "bf16"), gscale)
+    np.testing.assert_array_equal(_np(sf), rsf)
+    np.testing.assert_array_equal(_np(q), rq)
+    assert np.any(rsf != 0)                       # the scale codes are not all zero
+
+
+def test_fused_nvfp4_tiny_norm_huge_global_scale():
+    """The fused op with gamma in bf16's subnormal range: every n is below
+    2^-125, and the largest allowed G (just below 2^119) makes the subnormal
+    amax / 6 decide the scale code."""
+    A = _A()
+    rng = np.random.default_rng(31)
+    H = 1024
+    x = W.to_dtype(rng.standard_normal((9, H)), "bf16")
+    res = W.to_dtype(rng.standard_normal((9, H)), "bf16")
+    g = W.to_dtype(rng.uniform(2.0 ** -133, 2.0 ** -127, H), "bf16")
+    G = float.fromhex("0x1.fffffep118")
+    rc = res.cuda()
+    q, sf, _ = A.add_rmsnorm_quant_nvfp4(x.cuda(), rc, g.cuda(), _dev_scalar(G), 1e-6)
+    torch.cuda.synchronize()
+    ref = O.add_rmsnorm_quant_nvfp4(W.bits(x), W.bits(res), W.bits(g), "bf16", G, 1e-6, False)
+    assert np.all(np.abs(ref["n"]) < 2.0 ** -125) and np.any(ref["sf"] != 0)
+    np.testing.assert_array_equal(_np(rc), ref["residual"])
+    np.testing.assert_array_equal(_np(sf), ref["sf"])
+    np.testing.assert_array_equal(_np(q), ref["q"])
+
+
 @pytest.mark.parametrize("op", ["fp8", "nvfp4"])
 @pytest.mark.parametrize("tokens,hidden", [(0, 128), (1, 16), (3, 48), (37, 1040), (513, 7168)])
 @pytest.mark.parametrize("stream_hint", ["0", "1"])
