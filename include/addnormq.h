@@ -293,6 +293,29 @@ int anq_nvfp4_shape(int64_t tokens, int64_t hidden, int64_t* q_cols, int64_t* sf
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* anq_status_string(int status);
 
+/*
+ * Self-check of the device arithmetic that the exact results above rest on,
+ * run on the current device. The kernels replace four IEEE operations by
+ * cheaper forms; each count is the number of inputs where the form the
+ * kernels use differs from the operation it stands for (all four are 0 where
+ * the kernels are exact):
+ *   counts[0] the reciprocal (hardware estimate + one FMA correction) against
+ *             1 / b, every normal binary32 b below 2^120, and b = +0, +inf
+ *   counts[1] the NVFP4 block-scale quotient against amax / 6, every
+ *             non-negative binary32 amax (+inf included)
+ *   counts[2] the E4M3 code of the FP8 quotient a / s against the code of the
+ *             IEEE quotient, every binary32 a at seven scales s from 2^-126
+ *             to 2^119
+ *   counts[3] the E2M1 code of every binary32 at or beyond +-6 (infinities
+ *             included) against the signed top code
+ * counts: device memory, ANQ_SELFCHECK_COUNTS uint64 values, 8-byte aligned;
+ * zeroed, then counted, on `stream` (read it after the stream completes).
+ * About 3.4e10 comparisons. Returns ANQ_OK, ANQ_ERR_NULL, ANQ_ERR_ALIGN or
+ * ANQ_ERR_LAUNCH.
+ */
+#define ANQ_SELFCHECK_COUNTS 4
+int anq_selfcheck_arith(uint64_t* counts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

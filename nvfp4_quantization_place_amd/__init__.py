@@ -18,7 +18,7 @@ __all__ = ["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4", "qk_norm_rope_fp8
            "qk_norm_rope_fp8_kv_store", "add_rmsnorm_quant_nvfp4_swizzled",
            "gated_rmsnorm_quant_nvfp4", "silu_gate_f32",
            "quant_nvfp4_swizzled", "nvfp4_swizzled_sf_shape", "add_rmsnorm", "quant_fp8", "quant_nvfp4",
-           "nvfp4_shape", "status_string", "lib", "AnqError", "LIB_PATH",
+           "nvfp4_shape", "status_string", "selfcheck_arith", "lib", "AnqError", "LIB_PATH",
            "ANQ_F16", "ANQ_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddnormq.so")
@@ -47,6 +47,7 @@ _SIGS = {
     "quant_nvfp4_swizzled": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P],
     "gated_rmsnorm_quant_nvfp4": [_P, _P, _P, _P, _F, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P],
     "silu_gate_f32": [_P, _P, _I64, ctypes.c_int, _P, _P],
+    "anq_selfcheck_arith": [_P, _P],
     "anq_nvfp4_swizzled_sf_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "anq_nvfp4_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "anq_status_string": [ctypes.c_int],
@@ -377,6 +378,19 @@ def gated_rmsnorm_quant_nvfp4(x, z, gamma, global_scale, eps: float, group: int 
     if st:
         raise AnqError("gated_rmsnorm_quant_nvfp4", st)
     return q, sf
+
+
+def selfcheck_arith(device=None, stream=None) -> list[int]:
+    """Mismatch counts of the device arithmetic self-check (anq_selfcheck_arith):
+    [reciprocal, block-scale quotient, FP8 quotient codes, E2M1 saturation];
+    all zero where the kernels are exact. Waits for the check to finish."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    counts = torch.empty(4, dtype=torch.int64, device=dev)
+    st = lib().anq_selfcheck_arith(_ptr(counts), _stream(dev, stream))
+    if st:
+        raise AnqError("anq_selfcheck_arith", st)
+    torch.cuda.synchronize(dev)
+    return [int(v) for v in counts.cpu()]
 
 
 def silu_gate_f32(x, z, u=None, stream=None):

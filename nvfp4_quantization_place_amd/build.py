@@ -21,7 +21,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libaddnormq.so")
-SOURCES = ["anq_api.hip", "anq_tail.hip", "anq_qk.hip", "anq_quant.hip"]
+SOURCES = ["anq_api.hip", "anq_tail.hip", "anq_qk.hip", "anq_quant.hip", "anq_selfcheck.hip"]
 ARCH = "gfx950"
 
 

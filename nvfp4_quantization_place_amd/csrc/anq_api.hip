@@ -214,6 +214,14 @@ extern "C" int silu_gate_f32(const void* x, const void* z, int64_t n, int dtype,
   return launch_status(anq::launch_gate(dtype, x, z, u, n / 8, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int anq_selfcheck_arith(uint64_t* counts, void* stream) {
+  if (!counts) return ANQ_ERR_NULL;
+  if (!aligned(counts, 8)) return ANQ_ERR_ALIGN;
+  static_assert(anq::kSelfcheckCounts == ANQ_SELFCHECK_COUNTS, "count array length");
+  return launch_status(anq::launch_selfcheck(reinterpret_cast<unsigned long long*>(counts),
+                                             static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 // Checks shared by the two Q/K entry points. q_cols is the width of `out` in

@@ -96,4 +96,8 @@ hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t st
 hipError_t launch_gate(int dtype, const void* x, const void* z, float* u, int64_t vecs,
                        hipStream_t stream);
 
+// Self-check of the device arithmetic: kSelfcheckCounts mismatch counts.
+constexpr int kSelfcheckCounts = 4;
+hipError_t launch_selfcheck(unsigned long long* counts, hipStream_t stream);
+
 }  // namespace anq

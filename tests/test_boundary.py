@@ -45,7 +45,7 @@ def test_header_declares_the_entry_points():
                                            "quant_nvfp4", "add_rmsnorm_quant_nvfp4_swizzled",
                                            "quant_nvfp4_swizzled", "anq_nvfp4_swizzled_sf_shape",
                                            "gated_rmsnorm_quant_nvfp4", "silu_gate_f32",
-                                           "anq_nvfp4_shape",
+                                           "anq_nvfp4_shape", "anq_selfcheck_arith",
                                            "anq_status_string"])
 
 
@@ -148,6 +148,13 @@ def test_gated_validation(L):
     assert gate(addr(0), addr(1), 8, 1, addr(2, 4), None) == ALIGN
     assert gate(addr(0), addr(1), 8, 1, addr(1), None) == ALIAS
     assert g(tokens=4, sf=addr(4, 16)) == ALIAS              # scales over the codes
+
+
+def test_selfcheck_validation(L):
+    """The arithmetic self-check rejects a missing or misaligned count array
+    before any device work."""
+    assert L.anq_selfcheck_arith(None, None) == NULL
+    assert L.anq_selfcheck_arith(addr(0, 4), None) == ALIGN
 
 
 def fp8(L, **kw):
