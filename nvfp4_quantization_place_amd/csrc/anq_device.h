@@ -518,32 +518,33 @@ __device__ __forceinline__ void silu_gate8(const float (&x)[8], const float (&z)
 // s = z / 2; with |z| >= 128 it rounds to 0 (z > 0, s = z) or overflows
 // (z < 0, s = -0). Between, there are 32 binades x 128 significands per sign:
 // an 8192-entry binary32 table, index (bf16 bits & 0x7FFF) - (102 << 7) plus
-// 4096 for negative z. A workgroup fills it from silu_gate itself, so a looked
-// up value is bit-identical to the computed one; values outside the table take
-// the computed path.
+// 4096 for negative z. The library holds it as constants (anq_gate_table.h,
+// written by gen_gate_table.py from the same binary32 steps; a CPU test pins
+// every entry to the oracle's gate and the GPU tests run every in-range z
+// through it); each workgroup copies it into LDS. Values outside the table
+// take the computed path.
 constexpr int kGateTab = 8192;
 constexpr uint32_t kGateTabLo = 102u << 7;  // bf16 exponent field 102: 2^-25
 
-__device__ __forceinline__ void fill_gate_tab(float* tab, const double* exp2_tab) {
-  for (int j = threadIdx.x; j < kGateTab; j += blockDim.x) {
-    const uint32_t b = ((uint32_t)(j & 4095) + kGateTabLo) | ((uint32_t)(j >> 12) << 15);
-    tab[j] = silu_gate(1.0f, __uint_as_float(b << 16), exp2_tab);
-  }
-}
-
 // u_i = x_i * s(z_i) for the eight bf16 z of zv (the silu_gate8 result).
+// With b a bf16 pattern and t = b - (102 << 7) (32-bit, wrapping below the
+// table), b is in the table iff bits 12..14 of t are clear: positive z in
+// range give t < 4096, negative ones 0x8000 <= t < 0x9000, and every other b
+// sets one of those bits. The entry is (t & 4095) | (b's sign at bit 12), one
+// bitfield insert of b >> 3 (b has 16 bits, so b >> 3 has nothing above bit 12).
 __device__ __forceinline__ void gate_lut8(const float (&x)[8], const U4& zv, const float* tab,
                                           const double* exp2_tab, float (&u)[8]) {
   float s[8];
-  bool outside = false;
+  uint32_t any = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t b = (i & 1) ? (zv.w[i >> 1] >> 16) : (zv.w[i >> 1] & 0xFFFFu);
-    const uint32_t t = (b & 0x7FFFu) - kGateTabLo;  // wraps below the table
-    outside |= t >= 4096u;
-    s[i] = tab[(t & 4095u) | ((b >> 3) & 4096u)];
+    const uint32_t w = zv.w[i >> 1];
+    const uint32_t b = (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+    const uint32_t t = b - kGateTabLo;
+    any |= t;
+    s[i] = tab[(t & 4095u) | ((b >> 3) & ~4095u)];
   }
-  if (outside) {  // rare for activations: |z| < 2^-25 or |z| >= 128 somewhere in the vector
+  if (any & 0x7000u) {  // rare for activations: |z| < 2^-25 or |z| >= 128 somewhere in the vector
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t b = (i & 1) ? (zv.w[i >> 1] >> 16) : (zv.w[i >> 1] & 0xFFFFu);

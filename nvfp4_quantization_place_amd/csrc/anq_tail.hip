@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "anq_device.h"
+#include "anq_gate_table.h"
 #include "anq_internal.h"
 
 namespace anq {
@@ -75,6 +76,13 @@ struct BlockReduce {
     GroupReduce<16>().sum_dd(hi, lo);
   }
 };
+
+// The bf16 gate table into the workgroup's LDS: 32 KiB copied from the
+// library's constant table in 16-byte pieces.
+__device__ __forceinline__ void fill_gate_tab(uint4* tab) {
+  const uint4* src = reinterpret_cast<const uint4*>(kGateTabBits);
+  for (int j = threadIdx.x; j < kGateTab / 4; j += blockDim.x) tab[j] = src[j];
+}
 
 // ---------------------------------------------------------------- the kernel
 
@@ -190,15 +198,13 @@ tail_kernel(TailParams p) {
   constexpr bool kLut = EPI == kEpiGatedNvfp4Lut;  // bf16 z, gate from the LDS table
   constexpr bool kGated = EPI == kEpiGatedNvfp4 || kLut;  // `res` is z: read only, never stored
   constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz || kGated;
+  extern __shared__ uint4 gate_tab4[];  // kLut: kGateTab entries (dynamic shared memory)
+  const float* gate_tab = reinterpret_cast<const float*>(gate_tab4);
+  static_assert(!kLut || DT == kBF16, "the gate table covers bf16 z");
   if constexpr (kNvfp4) {
     fill_mult_tab(mult_tab, sc);
     if constexpr (kGated) fill_exp2_tab(exp2_tab);
-    __syncthreads();
-  }
-  extern __shared__ float gate_tab[];  // kLut: kGateTab entries (dynamic shared memory)
-  if constexpr (kLut) {
-    static_assert(DT == kBF16, "the gate table covers bf16 z");
-    fill_gate_tab(gate_tab, exp2_tab);
+    if constexpr (kLut) fill_gate_tab(gate_tab4);
     __syncthreads();
   }
   // gamma stays packed in registers (4 per vector) and is unpacked per row:

@@ -172,3 +172,26 @@ def test_gated_pins_catch_planted_mistakes(monkeypatch):
                   lambda h, r, g: orig_norm(h, r, g) * real(np.ones_like(h), np.full_like(h, 20.0)))
         with pytest.raises(AssertionError):
             test_gated_norm_follows_the_gate()
+
+
+def test_library_gate_table_is_the_oracle_gate():
+    """The constant bf16 gate table compiled into the library
+    (csrc/anq_gate_table.h) holds, for every bf16 z with 2^-25 <= |z| < 128,
+    the bit pattern of the oracle's gate s(z) = silu_gate(1, z); its layout is
+    positive z in entries 0..4095, negative z in 4096..8191, exponent field
+    102 upward."""
+    import os
+    import re
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "nvfp4_quantization_place_amd", "csrc", "anq_gate_table.h")
+    src = open(path).read()
+    body = src[src.index("kGateTabBits[8192] = {"):].split("}", 1)[0]
+    vals = np.array([int(v, 16) for v in re.findall(r"0x([0-9a-f]{8})u", body)], np.uint32)
+    assert len(vals) == 8192
+    j = np.arange(8192, dtype=np.uint32)
+    b = (((j & 4095) + (102 << 7)) | ((j >> 12) << 15)).astype(np.uint16)
+    z = O.t_decode(b, "bf16")
+    assert np.all((np.abs(z) >= 2.0 ** -25) & (np.abs(z) < 128))
+    with np.errstate(over="ignore"):
+        ref = O.silu_gate(np.ones(8192, F32), z)
+    np.testing.assert_array_equal(vals, ref.view(np.uint32))
