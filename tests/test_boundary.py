@@ -341,3 +341,19 @@ def test_gate_exp2_table_is_correctly_rounded():
         for j, v in enumerate(vals):
             exact = Decimal(2) ** (Decimal(j) / 64)
             assert float(exact) == v, j                      # float(Decimal) rounds to nearest
+
+
+def test_product_fails_loudly_without_library_or_gpu(monkeypatch):
+    """There is no CPU path: a missing library raises, and CPU tensors are
+    refused before any library call."""
+    import torch
+    monkeypatch.setattr(A, "_lib", None)
+    monkeypatch.setattr(A, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libaddnormq.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        A.lib()
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        A.add_rmsnorm_quant_nvfp4(x, x.clone(), torch.ones(64, dtype=torch.bfloat16),
+                                  torch.ones(1), 1e-6)
+    with pytest.raises(ValueError, match="GPU"):
+        A.quant_fp8(x, torch.ones(1))
