@@ -172,7 +172,11 @@ class Workload:
             raise ValueError(f"no call for workload kind {self.kind!r}")
 
 
-def time_workload(w: Workload, steps: int, warmup: int, eager: bool = True) -> dict:
+SPREAD_REPLAYS = 10
+
+
+def time_workload(w: Workload, steps: int, warmup: int, eager: bool = True,
+                  spread: bool = True) -> dict:
     import torch
     for i in range(warmup):
         w.call(i)
@@ -209,10 +213,38 @@ def time_workload(w: Workload, steps: int, warmup: int, eager: bool = True) -> d
     wall_s = time.perf_counter() - t0
     dev_us = ev0.elapsed_time(ev1) * 1e3 / steps
     gbs = w.bytes / (dev_us * 1e-6) / 1e9
-    return dict(workload=w.name, io_dtype=w.dtype, bytes_per_call=w.bytes, rotating_sets=w.sets,
-                us_per_call=round(dev_us, 3), eager_us_per_call=eager_us,
-                wall_ms_timed=round(wall_s * 1e3, 3), gbs=round(gbs, 1),
-                frac_of_peak=round(gbs / PEAK_GBS, 4))
+    r = dict(workload=w.name, io_dtype=w.dtype, bytes_per_call=w.bytes, rotating_sets=w.sets,
+             us_per_call=round(dev_us, 3), eager_us_per_call=eager_us,
+             wall_ms_timed=round(wall_s * 1e3, 3), gbs=round(gbs, 1),
+             frac_of_peak=round(gbs / PEAK_GBS, 4))
+    if not spread:
+        return r
+    # spread: the per-call average of SPREAD_REPLAYS further replays of the same graph
+    per = []
+    for _ in range(SPREAD_REPLAYS):
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        per.append(ev0.elapsed_time(ev1) * 1e3 / steps)
+    per.sort()
+    pick = lambda q: round(per[int(round(q * (len(per) - 1)))], 3)
+    # hot: the same calls on one buffer set, so inputs that fit stay in the last-level cache
+    gh = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gh):
+        for _ in range(steps):
+            w.call(0)
+    gh.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    gh.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    hot_us = ev0.elapsed_time(ev1) * 1e3 / steps
+    del g, gh
+    r["spread_us"] = {"replays": SPREAD_REPLAYS, "p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+    r["hot_us_per_call"] = round(hot_us, 3)
+    return r
 
 
 def cpu_baseline(k: int, scalars: dict, budget_s: float = 10.0) -> dict:
@@ -307,6 +339,9 @@ def main():
                     help="skip the fused vs separated (two-kernel) comparison and the KV-store timing")
     ap.add_argument("--no-eager", action="store_true",
                     help="skip the eager timing (so a kernel trace holds graph launches only)")
+    ap.add_argument("--no-spread", action="store_true",
+                    help="skip the spread replays and the hot (same buffers) graph, so a kernel "
+                    "trace holds only the timed graph's launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 1 GiB instead (practical "
                     "streaming ceiling; the same copy calibrates the HBM byte counters)")
@@ -334,10 +369,16 @@ def main():
     results = {}
     for k in todo:
         w = Workload(k, scalars, args.steps)
-        r = time_workload(w, args.steps, args.warmup, eager=not args.no_eager)
+        r = time_workload(w, args.steps, args.warmup, eager=not args.no_eager,
+                          spread=not args.no_spread)
         r["traffic_bytes_per_call"] = load_traffic(k, w.bytes)
         results[k] = r
-        print(f"# workload {k} {r['workload']}: {r['us_per_call']} us/call (graph), "
+        extra = ""
+        if "spread_us" in r:
+            sp = r["spread_us"]
+            extra = (f"; p10/p50/p90 {sp['p10']}/{sp['p50']}/{sp['p90']}; hot, same buffers "
+                     f"{r['hot_us_per_call']}")
+        print(f"# workload {k} {r['workload']}: {r['us_per_call']} us/call (graph{extra}), "
               f"{r['eager_us_per_call']} us/call (eager), {r['gbs']} GB/s", file=sys.stderr, flush=True)
         del w
         torch.cuda.empty_cache()
@@ -404,8 +445,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": head["workload"], "io_dtype": inp_dtype,
                    "us_per_call": head["us_per_call"], "eager_us_per_call": head["eager_us_per_call"],
-                   "bytes_per_call": head["bytes_per_call"], "timing": "HIP graph of steps calls, "
-                   "HIP events on the launch stream; inputs rotate over >= 1 GiB of buffers"},
+                   "bytes_per_call": head["bytes_per_call"], "spread_us": head.get("spread_us"),
+                   "hot_us_per_call": head.get("hot_us_per_call"), "timing": "HIP graph of steps calls, "
+                   "HIP events on the launch stream; inputs rotate over >= 1 GiB of buffers; "
+                   "spread_us over further replays of that graph; hot_us_per_call on one buffer set"},
         "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": head["frac_of_peak"],
                      "traffic": (round(traffic / (head["us_per_call"] * 1e-6) / 1e9, 1)
