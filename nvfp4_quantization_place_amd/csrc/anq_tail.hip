@@ -140,7 +140,7 @@ __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int 
 // lane, which then needs no spills; 4 (<= 128) for rows wider than 8192 and
 // for the gated variant (its binary64 exp needs the registers).
 template <int DT, int EPI, bool NORM, int K, int G, bool NT>
-__global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 ? 256 : 1024),
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 && EPI != kEpiGatedNvfp4Lut ? 256 : 1024),
                                amdgpu_waves_per_eu(K == 1 && EPI != kEpiGatedNvfp4 &&
                                                            EPI != kEpiGatedNvfp4Lut ? 7 : 4)))
 tail_kernel(TailParams p) {
@@ -392,17 +392,23 @@ Tiling pick_tail_tiling(int32_t vec, int64_t tokens) {
 }
 
 // Tiling of the gated variant with the gate table (rows <= 1024 elements):
-// lane groups of 16/32/64 lanes, one or two vectors per lane, four to sixteen
-// lane groups per 256-lane workgroup, each walking enough consecutive rows that
-// about 1024 workgroups cover the call, so each workgroup fills its table once
-// for many rows. ANQ_ROWS_PER_GROUP and ANQ_STREAM override, as above.
+// lane groups of 16/32/64 lanes, one or two vectors per lane, in 512-lane
+// workgroups (one 32 KiB table per 8 wavefronts), each lane group walking
+// enough consecutive rows that about 512 workgroups cover the call, so each
+// workgroup copies its table once for many rows. On the gated workload
+// (bf16 [8192, 8192], groups of 1024) 512-lane workgroups with 16 rows per
+// group measured 66.8 us against 67.8 with 256 lanes (320 and 384 lanes:
+// 74-85). ANQ_GATE_BLOCK (a multiple of 64, at most 1024), ANQ_ROWS_PER_GROUP
+// and ANQ_STREAM override, for sweeps.
 Tiling pick_gate_lut_tiling(int32_t vec, int64_t rows) {
   Tiling t{};
   t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
   t.vec_per_lane = vec <= 64 ? 1 : 2;
-  t.block = 256;
-  const int64_t groups_per_block = 256 / t.group;
-  int64_t r = rows / (groups_per_block * 1024);
+  t.block = 512;
+  const int env_block = env_int("ANQ_GATE_BLOCK", 0);
+  if (env_block > 0 && env_block <= 1024 && env_block % 64 == 0) t.block = env_block;
+  const int64_t groups_per_block = t.block / t.group;
+  int64_t r = rows / (groups_per_block * 512);
   t.rows = (int)(r < 1 ? 1 : (r > 64 ? 64 : r));
   const int env_rows = env_int("ANQ_ROWS_PER_GROUP", 0);
   if (env_rows > 0) t.rows = env_rows;

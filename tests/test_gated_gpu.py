@@ -167,11 +167,14 @@ def test_gated_workload_size():
 @pytest.mark.parametrize("tokens,hidden,group", [(5, 64, 16), (37, 1024, 1024), (37, 1024, 128),
                                                  (64, 8192, 1024), (9, 2048, 64), (130, 4096, 512)])
 @pytest.mark.parametrize("rows", ["", "1", "3"])
-def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, monkeypatch):
+@pytest.mark.parametrize("block", ["", "256"])
+def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, block, monkeypatch):
     """The bf16 gate read from the workgroup's LDS table (forced on small
-    calls), with several rows per lane group, gives the oracle's codes."""
+    calls), with several rows per lane group and both workgroup sizes, gives
+    the oracle's codes."""
     monkeypatch.setenv("ANQ_GATE_LUT", "1")
     monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
+    monkeypatch.setenv("ANQ_GATE_BLOCK", block)
     inp = W.make_gated(hidden + 7 * group + tokens, "bf16", tokens, hidden, group,
                        z=("normal", 3.0), eps=1e-5)
     G = float(O.nvfp4_global_scale(_oracle(inp, 1.0)["n"]))
