@@ -25,7 +25,7 @@
 namespace anq {
 
 template <int DT, int LPH, bool NT, bool STORE>
-__global__ void __launch_bounds__(256) qk_kernel(QKParams p) {
+__global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
   constexpr int D = LPH * 16;
   constexpr int HALF = D / 2;
   constexpr int HPP = 64 / LPH;  // heads per pass of a wavefront
@@ -173,8 +173,13 @@ static hipError_t launch_qk_nt(const QKParams& p, hipStream_t s) {
     case 32: fn = (const void*)&qk_kernel<DT, 32, NT, STORE>; break;
     default: return hipErrorInvalidConfiguration;
   }
-  const int block = 256;  // four wavefronts
-  const int64_t grid = (p.tokens * p.waves_per_token + 3) / 4;
+  int block = 256;  // four wavefronts
+  if (const char* e = getenv("ANQ_QK_BLOCK")) {
+    const int b = atoi(e);
+    if (b >= 64 && b <= 1024 && b % 64 == 0) block = b;
+  }
+  const int64_t wpb = block / 64;
+  const int64_t grid = (p.tokens * p.waves_per_token + wpb - 1) / wpb;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(block), args, 0, s);
 }
@@ -182,10 +187,15 @@ static hipError_t launch_qk_nt(const QKParams& p, hipStream_t s) {
 // Streaming hints (see ld16s) once qkv alone is >= 32 MiB; ANQ_STREAM=0/1 overrides.
 template <int DT, bool STORE>
 static hipError_t launch_qk_dt(QKParams p, hipStream_t s) {
-  // wavefronts per token: enough head groups in flight at once that the
-  // per-token chain of loads stays short (ANQ_QK_WAVES overrides, for sweeps)
+  // wavefronts per token: one, walking all of the token's head groups, once
+  // the call has enough tokens to fill the GPU (~2048 wavefronts); more, up to
+  // one per head group, for fewer tokens. At 4096 tokens x 32 heads of 128
+  // (bf16) one wavefront per token measured 11.8 us against 12.8 with two.
+  // ANQ_QK_WAVES and ANQ_QK_BLOCK override, for sweeps.
   const int passes = (p.nq + p.nk + p.nv + 64 / (p.head_dim / 16) - 1) / (64 / (p.head_dim / 16));
-  int W = passes < 2 ? 1 : 2;
+  const int64_t want = p.tokens > 0 ? (2048 + p.tokens - 1) / p.tokens : 1;
+  int W = (int)(want < passes ? want : passes);
+  if (W < 1) W = 1;
   if (const char* e = getenv("ANQ_QK_WAVES")) {
     if (*e && atoi(e) > 0) W = atoi(e);
   }

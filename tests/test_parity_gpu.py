@@ -266,9 +266,12 @@ def test_every_tiling_matches_the_oracle(hidden, tilings, op, monkeypatch):
 
 @pytest.mark.parametrize("waves", ["1", "2", "3", "5"])
 @pytest.mark.parametrize("head_dim", [64, 128])
-def test_qk_waves_per_token_agree(head_dim, waves, monkeypatch):
-    """Splitting a token's heads over several wavefronts changes nothing."""
+@pytest.mark.parametrize("block", ["", "64", "1024"])
+def test_qk_waves_per_token_agree(head_dim, waves, block, monkeypatch):
+    """Splitting a token's heads over several wavefronts, and packing
+    wavefronts into workgroups of other sizes, changes nothing."""
     monkeypatch.setenv("ANQ_QK_WAVES", waves)
+    monkeypatch.setenv("ANQ_QK_BLOCK", block)
     pos = np.random.default_rng(3).integers(0, 64, 23)
     inp = W.make_qk(31, "bf16", 23, 9, 5, 3, head_dim, positions=pos, max_pos=64, scale=0.04)
     got = gpu_qk(inp)
