@@ -104,7 +104,7 @@ typedef enum { ANQ_F16 = 0, ANQ_BF16 = 1 } anq_dtype;
 enum {
   ANQ_OK = 0,
   ANQ_ERR_NULL = 1,        /* a required pointer is NULL */
-  ANQ_ERR_SHAPE = 2,       /* tokens < 0, hidden <= 0, hidden % 16 != 0, bad group, size overflow */
+  ANQ_ERR_SHAPE = 2,       /* tokens < 0, hidden <= 0, hidden % 16 != 0, bad group, bad head count, size overflow */
   ANQ_ERR_DTYPE = 3,       /* dtype is not ANQ_F16 / ANQ_BF16 */
   ANQ_ERR_ALIGN = 4,       /* a pointer breaks the alignment rule above */
   ANQ_ERR_ALIAS = 5,       /* buffers overlap where they must not */
@@ -166,6 +166,8 @@ int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
  *   scale      device pointer to one binary32 s
  *   rotary_dim must equal head_dim (partial rotation is not fused: ANQ_ERR_UNSUPPORTED)
  *   head_dim   one of 32, 64, 128, 256, 512
+ *   nq, nk, nv >= 0, at least one head and at most 2^20 in all (ANQ_ERR_VALUE
+ *              for a negative count, ANQ_ERR_SHAPE otherwise)
  *   out        [tokens, (nq+nk+nv)*D] uint8 E4M3 codes (output)
  */
 int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
@@ -213,8 +215,9 @@ int add_rmsnorm(const void* x, void* residual, const void* gamma, float eps, int
                 int64_t hidden, int dtype, void* norm_out, void* stream);
 
 /*
- * quant_fp8: q_i = E4M3(in_i / s) for in [tokens, hidden] T (hidden % 16 == 0),
- *   s = *scale; q [tokens, hidden] uint8.
+ * quant_fp8: q_i = E4M3(in_i / s) for in [tokens, hidden] T (hidden % 16 == 0,
+ *   hidden < 2^34: no ANQ_MAX_HIDDEN limit, the quantisers keep no row in
+ *   registers), s = *scale; q [tokens, hidden] uint8.
  */
 int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden, int dtype,
               uint8_t* q, void* stream);

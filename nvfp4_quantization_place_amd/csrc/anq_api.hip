@@ -233,7 +233,7 @@ int check_qk(const void* qkv, const void* gamma_q, const void* gamma_k, const in
              const uint8_t* out, bool kv_store, const int64_t* slots, int64_t num_slots,
              const uint8_t* kv) {
   const bool need_out = !kv_store || nq > 0;
-  const bool need_kv = kv_store && nk + nv > 0;
+  const bool need_kv = kv_store && (int64_t)nk + nv > 0;
   if (!cos_sin || !scale ||
       (tokens != 0 && (!qkv || !positions || (need_out && !out) || (need_kv && (!slots || !kv)))))
     return ANQ_ERR_NULL;
@@ -242,12 +242,13 @@ int check_qk(const void* qkv, const void* gamma_q, const void* gamma_k, const in
   if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
   if (nq < 0 || nk < 0 || nv < 0 || max_pos < 1 || (kv_store && num_slots < 0))
     return ANQ_ERR_VALUE;
-  if (tokens < 0 || head_dim <= 0 || nq + nk + nv == 0) return ANQ_ERR_SHAPE;
+  const int64_t heads = (int64_t)nq + nk + nv;  // in 64 bits: int32 counts may not sum in 32
+  if (tokens < 0 || head_dim <= 0 || heads == 0 || heads > (1 << 20)) return ANQ_ERR_SHAPE;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
     return ANQ_ERR_UNSUPPORTED;
   if (rotary_dim != head_dim) return ANQ_ERR_UNSUPPORTED;
   if (!valid_eps(eps)) return ANQ_ERR_VALUE;
-  const int64_t cols = (int64_t)(nq + nk + nv) * head_dim;
+  const int64_t cols = heads * head_dim;
   if (tokens > INT64_MAX / (2 * cols) || max_pos > INT64_MAX / (4 * (int64_t)head_dim) ||
       (kv_store && num_slots > INT64_MAX / cols))
     return ANQ_ERR_SHAPE;
@@ -256,7 +257,7 @@ int check_qk(const void* qkv, const void* gamma_q, const void* gamma_k, const in
       (kv_store && (!aligned(kv, 16) || !aligned(slots, 8))))
     return ANQ_ERR_ALIGN;
   const int64_t out_cols = kv_store ? (int64_t)nq * head_dim : cols;
-  const int64_t kv_bytes = need_kv ? num_slots * (int64_t)(nk + nv) * head_dim : 0;
+  const int64_t kv_bytes = need_kv ? num_slots * ((int64_t)nk + nv) * head_dim : 0;
   const Span outs[2] = {span(out, tokens * out_cols), span(kv, kv_bytes)};
   const Span ins[7] = {span(qkv, tokens * cols * 2), span(nq ? gamma_q : nullptr, nq ? head_dim * 2 : 0),
                        span(nk ? gamma_k : nullptr, nk ? head_dim * 2 : 0), span(positions, tokens * 8),
@@ -364,7 +365,7 @@ int quant_common(const void* in, const float* scale, int64_t tokens, int64_t hid
   if (!scale || (tokens != 0 && (!in || !q || (nvfp4 && !sf)))) return ANQ_ERR_NULL;
   if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
   if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
-  if (tokens > INT64_MAX / (2 * hidden)) return ANQ_ERR_SHAPE;
+  if (tokens > INT64_MAX / (2 * hidden) || hidden / 8 > INT32_MAX) return ANQ_ERR_SHAPE;
   if (!aligned(in, 16) || !aligned(q, 16) || !aligned(scale, 4) || (swizzled && !aligned(sf, 4)))
     return ANQ_ERR_ALIGN;
   const int64_t n = tokens * hidden;

@@ -240,6 +240,10 @@ def test_qk_validation(L):
     assert qk(L, nq=-1) == VALUE
     assert qk(L, max_pos=0) == VALUE
     assert qk(L, nq=0, nk=0, nv=0) == SHAPE
+    big = 2 ** 31 - 1                                    # head counts summed in 64 bits
+    assert qk(L, tokens=4, nq=big, nk=big, nv=big) == SHAPE
+    assert qk(L, tokens=4, nq=(1 << 20) + 1, nk=0, nv=0) == SHAPE
+    assert qks(L, tokens=4, nq=0, nk=big, nv=big) == SHAPE
     assert qk(L, tokens=-2) == SHAPE
     assert qk(L, eps=-1.0) == VALUE
     assert qk(L, qkv=addr(0, 8)) == ALIGN
@@ -318,7 +322,8 @@ def test_separated_tail_validation(L):
         assert op(L, tokens=0, t=None, q=None) == OK
         assert op(L, scale=None) == NULL
         assert op(L, hidden=40) == SHAPE
-        assert op(L, hidden=1 << 20) == OK                  # no row-width limit
+        assert op(L, hidden=1 << 20) == OK                  # no row-width limit below 2^34
+        assert op(L, hidden=1 << 35) == SHAPE               # 16-byte vectors per row beyond int32
         assert op(L, dtype=9) == DTYPE
         assert op(L, t=addr(0, 8)) == ALIGN
         assert op(L, scale=addr(3, 2)) == ALIGN
