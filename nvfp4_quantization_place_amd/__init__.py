@@ -110,8 +110,9 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
-def _check_gpu(*ts):
-    dev = None
+def _check_gpu(*ts) -> int:
+    """The one GPU (ordinal) all given tensors live on; they must be contiguous."""
+    dev = -1
     for t in ts:
         if t is None:
             continue
@@ -119,16 +120,25 @@ def _check_gpu(*ts):
             raise ValueError("all tensors must live on the GPU (there is no CPU path)")
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
-        if dev is None:
-            dev = t.device
-        elif t.device != dev:
+        d = t.get_device()
+        if dev < 0:
+            dev = d
+        elif d != dev:
             raise ValueError("all tensors must be on one device")
     return dev
 
 
-def _stream(dev, stream) -> int:
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
-    return s.cuda_stream
+# the current stream's raw handle without building a Stream object (torch's own
+# launchers read it this way); the public API where this build lacks it
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(dev: int, stream) -> int:
+    if stream is not None:
+        return stream.cuda_stream
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _ptr(t):
@@ -175,7 +185,7 @@ def add_rmsnorm_quant_nvfp4(x, residual, gamma, global_scale, eps: float, norm_o
     _scalar(global_scale, "global_scale")
     tokens, hidden = _rows(x)
     if hidden % 16 == 0 and hidden > 0:
-        qc, sc = nvfp4_shape(tokens, hidden)
+        qc, sc = hidden // 2, hidden // 16
     else:
         qc, sc = max(hidden // 2, 1), max(hidden // 16, 1)
     if q is None:
@@ -384,7 +394,9 @@ def selfcheck_arith(device=None, stream=None) -> list[int]:
     """Mismatch counts of the device arithmetic self-check (anq_selfcheck_arith):
     [reciprocal, block-scale quotient, FP8 quotient codes, E2M1 saturation];
     all zero where the kernels are exact. Waits for the check to finish."""
-    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    dev = torch.cuda.current_device() if device is None else torch.device(device).index
+    if dev is None:
+        dev = torch.cuda.current_device()
     counts = torch.empty(4, dtype=torch.int64, device=dev)
     st = lib().anq_selfcheck_arith(_ptr(counts), _stream(dev, stream))
     if st:
