@@ -1,10 +1,12 @@
 // Device building blocks of the fused tail kernels (gfx950 / CDNA4).
 //
 // Every helper here is exact or correctly rounded: the kernels must reproduce
-// the binary32 definition of the op bit for bit, so nothing is approximated
+// the binary32 definition of the op bit for bit, so no result is approximated
 // and nothing is contracted (the library is built with -ffp-contract=off; the
 // only fused multiply-adds are the explicit ones below, where they are exact
-// or part of a proven correction step).
+// or part of a correction step). Where a correction rests on a property of the
+// hardware estimate or conversion instructions rather than on a proof, the
+// property is checked over every input on the GPU by anq_selfcheck_arith.
 #pragma once
 
 #include <hip/hip_runtime.h>
