@@ -173,6 +173,7 @@ class Workload:
 
 
 SPREAD_REPLAYS = 10
+GRAPH_WARM_S = 0.025
 
 
 def time_workload(w: Workload, steps: int, warmup: int, eager: bool = True,
@@ -201,9 +202,16 @@ def time_workload(w: Workload, steps: int, warmup: int, eager: bool = True,
     with torch.cuda.graph(g):
         for i in range(steps):
             w.call(i)
-    for _ in range(2):
+    # warm the graph until the GPU has run it for >= GRAPH_WARM_S (at least 2
+    # replays), so the timed replay runs at settled clocks; profiler runs
+    # (spread off) keep to 2 replays so their traces stay small
+    warm_s = GRAPH_WARM_S if spread else 0.0
+    t_w = time.perf_counter()
+    reps = 0
+    while reps < 2 or time.perf_counter() - t_w < warm_s:
         g.replay()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        reps += 1
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
