@@ -90,3 +90,29 @@ def test_extreme_qk(i):
                     scale=float(np.float32(2.0 ** rng.uniform(-20, 20))))
     inp.qkv = _tensor(_finite_bits(rng, dtype, tuple(inp.qkv.shape)), dtype)
     np.testing.assert_array_equal(gpu_qk(inp), oracle_qk(inp))
+
+
+@pytest.mark.parametrize("op", ["fp8", "nvfp4"])
+def test_wide_span_midpoint_rows(op):
+    """bf16 rows whose large squares sum exactly to a binary32 midpoint
+    (2^120 + 2^96) next to tiny ones (2^-10, 2^-30, 2^-60) far below float64's reach
+    of the large part: the exact sum is just above the midpoint and rounds up,
+    and the double-double fallback keeps the tiny part in its low word. A row
+    without the tiny element is the exact tie (to even, down)."""
+    H = 64
+    rows = []
+    for tiny in (2.0 ** -10, 2.0 ** -30, 2.0 ** -60, 0.0):
+        r = np.zeros(H, np.float32)
+        r[0], r[1], r[2] = 2.0 ** 60, 2.0 ** 48, tiny
+        rows.append(r)
+    xb = O.t_encode(np.stack(rows), "bf16")
+    gb = O.t_encode(np.ones(H, np.float32), "bf16")
+    scale = 0.01 if op == "fp8" else 300.0
+    inp = W.TailInputs(name="span", op=op, dtype="bf16", tokens=len(rows), hidden=H,
+                       x=_tensor(xb, "bf16"), residual=_tensor(np.zeros_like(xb), "bf16"),
+                       gamma=_tensor(gb, "bf16"), eps=1e-30, scale=scale if op == "fp8" else None,
+                       norm_out=True, meta={})
+    got, ref = gpu_tail(inp, scale), oracle_tail(inp, scale)
+    assert [float(v) for v in ref["ss"]] == [2.0 ** 120 * (1 + 2.0 ** -23)] * 3 + [2.0 ** 120]
+    for k in ["residual", "norm_out", "q"] + (["sf"] if op == "nvfp4" else []):
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
