@@ -355,8 +355,9 @@ def main():
                     "streaming ceiling; the same copy calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the fused tail is row-parallel and this build runs "
-              "on a single MI355X; rerun with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the fused tail is row-parallel (a split of the "
+              "tokens needs no exchange), so one GPU's share is the whole measurement; "
+              "rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -129,7 +129,7 @@ def _check_gpu(*ts) -> int:
 
 
 # the current stream's raw handle without building a Stream object (torch's own
-# launchers read it this way); the public API where this build lacks it
+# launchers read it this way); the public API where the installed torch lacks it
 _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
