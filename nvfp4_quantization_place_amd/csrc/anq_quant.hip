@@ -23,6 +23,10 @@ __global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
   constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz;
   __shared__ float mult_tab[128];
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool ok = v < p.vecs;
+  const int64_t vv = ok ? v : p.vecs - 1;  // past the end: a clamped load, no store
+  // the vector's load goes out first; it lands while the multiplier table fills
+  const U4 in = ld16s<NT>(static_cast<const uint8_t*>(p.in) + (size_t)vv * 16);
   const float sc = *p.scale;  // FP8: s, NVFP4: G
   const float inv_sc = recip_rn(sc);  // s is a positive normal <= 2^119
   if constexpr (kNvfp4) {
@@ -38,10 +42,8 @@ __global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
                                                                p.sf_tiles)) = 0u;
     }
   }
-  const bool ok = v < p.vecs;
-  const int64_t vv = ok ? v : p.vecs - 1;  // past the end: a clamped load, no store
   float f[8];
-  unpack8<DT>(ld16s<NT>(static_cast<const uint8_t*>(p.in) + (size_t)vv * 16), f);
+  unpack8<DT>(in, f);
   if constexpr (EPI == kEpiFp8) {
     uint32_t lo, hi;
     fp8_codes8(f, sc, inv_sc, lo, hi);
