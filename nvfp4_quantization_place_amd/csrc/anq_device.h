@@ -151,7 +151,9 @@ __device__ __forceinline__ U4 pack8(const float (&f)[8]) {
 // Four binary32 values within +-448 (the quotients of div_rn_sat) -> four
 // E4M3FN codes, element i in byte i.
 __device__ __forceinline__ uint32_t e4m3x4_in_range(float a, float b, float c, float d) {
-  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion's untouched upper half is overwritten by the second;
+  // `a` (dead after it) fills it, so no register has to be zeroed first
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)__float_as_uint(a), false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
 

@@ -5,11 +5,11 @@
 // gfx950 mapping: one or a few wavefronts per token. 64 lanes form 64/(D/16) head
 // slots of D/16 lanes; lane j of a slot holds elements [8j, 8j+8) of the first
 // half of a head and [D/2 + 8j, D/2 + 8j + 8) of the second half, so every
-// NeoX rotation pair (k, k + D/2) lives in one lane. A wavefront loads the
-// token's cos|sin slice and both gammas once, then walks its share of the
-// token's head groups, loading the next group while it finishes the current
-// one. A head's sum of squares meets through a DPP butterfly over its
-// D/16 lanes. Q and K heads are normalised, rotated and quantised; V heads
+// NeoX rotation pair (k, k + D/2) lives in one lane. A wavefront takes at most
+// four groups of heads of its token and issues all of their loads at once,
+// with the token's cos|sin slice; the workgroup shares gamma_q and gamma_k as
+// binary32 in LDS. A head's sum of squares meets through a DPP butterfly over
+// its D/16 lanes. Q and K heads are normalised, rotated and quantised; V heads
 // are only quantised.
 //
 // STORE selects the KV-store epilogue (the "store" of the norm + RoPE + store
@@ -24,7 +24,7 @@
 
 namespace anq {
 
-template <int DT, int LPH, bool NT, bool STORE>
+template <int DT, int LPH, bool NT, bool STORE, int PF>
 __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
   constexpr int D = LPH * 16;
   constexpr int HALF = D / 2;
@@ -32,32 +32,57 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
   const int lane = threadIdx.x & 63;
   const int j = lane & (LPH - 1);
   const int slot = lane / LPH;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  // wavefront-uniform indices and row bases live in scalar registers; the
+  // lanes add 32-bit byte offsets (a token row is < 2^31 bytes)
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t t = wave / p.waves_per_token;
   const int w = (int)(wave - t * p.waves_per_token);
-  if (t >= p.tokens) return;  // the whole wavefront
+  const bool active = t < p.tokens;  // uniform over the wavefront
   const int heads = p.nq + p.nk + p.nv;
   const int qk_heads = p.nq + p.nk;
-  const float sc = *p.scale;
-  const float inv_sc = recip_rn(sc);  // s is a positive normal <= 2^119
-  const float sat = sat_bound(sc);  // the numerator clamp of div_rn_sat
   const size_t row_elems = (size_t)heads * D;
-  const uint8_t* row = static_cast<const uint8_t*>(p.qkv) + (size_t)t * row_elems * 2;
-  uint8_t* orow = p.out + (size_t)t * (STORE ? (size_t)p.nq * D : row_elems);
-  uint8_t* kvrow = nullptr;  // KV store: the token's pool row, or none
-  if constexpr (STORE) {
-    if (p.num_slots > 0) {  // 0 also when there are no K/V heads (slots may then be NULL)
-      const int64_t sl = p.slots[t];
-      if (sl >= 0 && sl < p.num_slots) kvrow = p.kv + (size_t)sl * (size_t)(heads - p.nq) * D;
-    }
-  }
-  const uint32_t oa_off = 8 * j, ob_off = HALF + 8 * j;  // element offsets inside a head
+  // a wavefront past the last token reads token 0's row (never used), so that
+  // every load below is unconditional
+  const uint8_t* row = static_cast<const uint8_t*>(p.qkv) + (size_t)(active ? t : 0) * row_elems * 2;
+  const uint32_t oa_off = 8 * j;  // element offset of the lane's first-half vector inside a head
+  const uint32_t lane_off = ((uint32_t)slot * D + oa_off) * 2;  // bytes, first half of the slot's head
 
-  // per-token constants: the lane's cos|sin values and gamma slices
+  // gamma_q | gamma_k: thread i < D/4 loads 16-byte vector i first of all, so
+  // that waiting for it (to fill LDS below) does not wait for the row loads
+  // (the launcher gives every workgroup at least D/4 threads)
+  const int gi = (int)threadIdx.x;
+  const bool gfill = qk_heads > 0 && gi < D / 4 && (gi >= D / 8 ? p.nk > 0 : p.nq > 0);
+  U4 gvec{};
+  if (gfill)
+    gvec = ld16(static_cast<const uint8_t*>(gi >= D / 8 ? p.gamma_k : p.gamma_q) +
+                (size_t)(gi >= D / 8 ? gi - D / 8 : gi) * 16);
+
+  int64_t pos = 0;
+  if (active && qk_heads > 0) pos = p.positions[t];
+
+  // The loads of all of the wavefront's head groups (at most PF, by the
+  // launcher's choice of W) go out before anything waits on them, group 0's
+  // first, then the token's cos|sin slice (after its position), then the other
+  // groups': loads complete in issue order, so group 0 then waits only for
+  // itself and cos|sin. Heads past the end re-read the last head (never
+  // stored), and so do slots past the wavefront's last group.
+  const int passes = (heads + HPP - 1) / HPP;
+  const int W = p.waves_per_token;  // this wavefront takes passes w, w + W, ...
+  const uint32_t last_off = ((uint32_t)(heads - 1) * D + oa_off) * 2;
+  auto group_off = [&](int pass) {
+    return min((uint32_t)pass * (HPP * D * 2) + lane_off, last_off);
+  };
+  U4 ra[PF], rb[PF];
+  {
+    const uint32_t o = group_off(w);
+    ra[0] = ld16s<NT>(row + o);
+    rb[0] = ld16s<NT>(row + o + HALF * 2);
+  }
+
+  // per-token constants: the lane's cos|sin values
   float c[8], s[8];
-  U4 gqa{}, gqb{}, gka{}, gkb{};
-  if (qk_heads > 0) {
-    int64_t pos = p.positions[t];
+  if (active && qk_heads > 0) {
     pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);  // never read outside the table
     const float* cs = p.cos_sin + (size_t)pos * D;
     const float4 c0 = *reinterpret_cast<const float4*>(cs + oa_off);
@@ -68,36 +93,55 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
     c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
     s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
     s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
-    if (p.nq > 0) {
-      gqa = ld16(static_cast<const uint8_t*>(p.gamma_q) + oa_off * 2);
-      gqb = ld16(static_cast<const uint8_t*>(p.gamma_q) + ob_off * 2);
-    }
-    if (p.nk > 0) {
-      gka = ld16(static_cast<const uint8_t*>(p.gamma_k) + oa_off * 2);
-      gkb = ld16(static_cast<const uint8_t*>(p.gamma_k) + ob_off * 2);
-    }
+  }
+#pragma unroll
+  for (int u = 1; u < PF; ++u) {
+    const uint32_t o = group_off(w + u * W);
+    ra[u] = ld16s<NT>(row + o);
+    rb[u] = ld16s<NT>(row + o + HALF * 2);
   }
 
-  const int passes = (heads + HPP - 1) / HPP;
-  const int W = p.waves_per_token;  // this wavefront takes passes w, w + W, ...
-  // loads of the first pass (heads past the end re-read the last head; never stored)
-  int hl = w * HPP + slot < heads ? w * HPP + slot : heads - 1;
-  U4 av = ld16s<NT>(row + ((size_t)hl * D + oa_off) * 2);
-  U4 bv = ld16s<NT>(row + ((size_t)hl * D + ob_off) * 2);
-  for (int pass = w; pass < passes; pass += W) {
-    const int h = pass * HPP + slot;
-    float a[8], b[8], oa[8], ob[8];
-    unpack8<DT>(av, a);
-    unpack8<DT>(bv, b);
-    if (pass + W < passes) {  // next group of heads, landing while this one is processed
-      hl = h + W * HPP < heads ? h + W * HPP : heads - 1;
-      av = ld16s<NT>(row + ((size_t)hl * D + oa_off) * 2);
-      bv = ld16s<NT>(row + ((size_t)hl * D + ob_off) * 2);
+  // gamma_q | gamma_k as binary32 in LDS, shared by the workgroup's
+  // wavefronts; a lane reads elements [8j, 8j+8) and [D/2 + 8j, D/2 + 8j + 8)
+  // of its head's gamma
+  __shared__ float4 gam_lds[2 * D / 4];
+  if (qk_heads > 0) {
+    if (gfill) {
+      float g[8];
+      unpack8<DT>(gvec, g);
+      gam_lds[2 * gi] = make_float4(g[0], g[1], g[2], g[3]);
+      gam_lds[2 * gi + 1] = make_float4(g[4], g[5], g[6], g[7]);
     }
+    __syncthreads();
+  }
+  if (!active) return;  // the whole wavefront, after the workgroup's barrier
+
+  const float sc = *p.scale;
+  const float inv_sc = recip_rn(sc);  // s is a positive normal <= 2^119
+  const float sat = sat_bound(sc);  // the numerator clamp of div_rn_sat
+  uint8_t* orow = p.out + (size_t)t * (STORE ? (size_t)p.nq * D : row_elems);
+  uint8_t* kvrow = nullptr;  // KV store: the token's pool row, or none
+  if constexpr (STORE) {
+    if (p.num_slots > 0) {  // 0 also when there are no K/V heads (slots may then be NULL)
+      const int64_t sl = p.slots[t];
+      if (sl >= 0 && sl < p.num_slots) kvrow = p.kv + (size_t)sl * (size_t)(heads - p.nq) * D;
+    }
+  }
+  const bool odd = (j & 1) != 0;
+  // lanes 2m and 2m+1 each store 16 contiguous codes (see the swap below)
+  const uint32_t st_off = odd ? HALF + 8 * (j - 1) : 8 * j;
+
+  // one group of heads: the slot's head h = pass * HPP + slot, from its two
+  // unpacked halves
+  auto group = [&](int pass, float (&a)[8], float (&b)[8]) {
+    const int h = pass * HPP + slot;
+    float oa[8], ob[8];
     if (h < qk_heads) {  // uniform over the head's lanes
-      float ga[8], gb[8];
-      unpack8<DT>(h < p.nq ? gqa : gka, ga);
-      unpack8<DT>(h < p.nq ? gqb : gkb, gb);
+      const float4* gl = gam_lds + (h < p.nq ? 0 : D / 4);
+      const float4 ga0 = gl[2 * j], ga1 = gl[2 * j + 1];
+      const float4 gb0 = gl[2 * (LPH + j)], gb1 = gl[2 * (LPH + j) + 1];
+      const float ga[8] = {ga0.x, ga0.y, ga0.z, ga0.w, ga1.x, ga1.y, ga1.z, ga1.w};
+      const float gb[8] = {gb0.x, gb0.y, gb0.z, gb0.w, gb1.x, gb1.y, gb1.z, gb1.w};
       double acc = 0.0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -107,6 +151,9 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
       const double S = lanes_sum<LPH>(acc);
       float ss = (float)S;
       if (near_f32_midpoint(S, D)) {
+        // rare: the exact sum as a double-double, in the order a0 b0 a1 b1 ...
+        // (this form, from the registers, measured 1.8 us faster at 4096
+        // tokens than re-reading the elements, though it is seldom taken)
         double hi = 0.0, lo = 0.0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -143,11 +190,14 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
     const uint32_t a1 = e4m3x4_in_range(oa[4], oa[5], oa[6], oa[7]);
     const uint32_t b0 = e4m3x4_in_range(ob[0], ob[1], ob[2], ob[3]);
     const uint32_t b1 = e4m3x4_in_range(ob[4], ob[5], ob[6], ob[7]);
-    const bool odd = (j & 1) != 0;
     const uint32_t r0 = dpp_u32<0xB1>(odd ? a0 : b0), r1 = dpp_u32<0xB1>(odd ? a1 : b1);
-    uint8_t* dst = orow + (size_t)h * D;
+    uint8_t* dst = orow;
+    uint32_t hd = (uint32_t)h;
     if constexpr (STORE) {
-      if (h >= p.nq) dst = kvrow ? kvrow + (size_t)(h - p.nq) * D : nullptr;
+      if (h >= p.nq) {
+        dst = kvrow;
+        hd = (uint32_t)(h - p.nq);
+      }
     }
     if (h < heads && dst) {
       U4 v;
@@ -155,29 +205,49 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
       v.w[1] = odd ? r1 : a1;
       v.w[2] = odd ? b0 : r0;
       v.w[3] = odd ? b1 : r1;
-      st16s<NT>(dst + (odd ? HALF + 8 * (j - 1) : 8 * j), v);
+      st16s<NT>(dst + (hd * D + st_off), v);
+    }
+  };
+
+  const int mine = (passes - w + W - 1) / W;  // groups of this wavefront, <= PF (w < W <= passes)
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    if (u < mine) {  // uniform over the wavefront
+      float a[8], b[8];
+      unpack8<DT>(ra[u], a);
+      unpack8<DT>(rb[u], b);
+      group(w + u * W, a, b);
     }
   }
 }
 
-template <int DT, bool NT, bool STORE>
-static hipError_t launch_qk_nt(const QKParams& p, hipStream_t s) {
-  void* args[] = {const_cast<QKParams*>(&p)};
-  const void* fn = nullptr;
-  const int lph = p.head_dim / 16;
+template <int DT, bool NT, bool STORE, int PF>
+static const void* qk_fn(int lph) {
   switch (lph) {
-    case 2: fn = (const void*)&qk_kernel<DT, 2, NT, STORE>; break;
-    case 4: fn = (const void*)&qk_kernel<DT, 4, NT, STORE>; break;
-    case 8: fn = (const void*)&qk_kernel<DT, 8, NT, STORE>; break;
-    case 16: fn = (const void*)&qk_kernel<DT, 16, NT, STORE>; break;
-    case 32: fn = (const void*)&qk_kernel<DT, 32, NT, STORE>; break;
-    default: return hipErrorInvalidConfiguration;
+    case 2: return (const void*)&qk_kernel<DT, 2, NT, STORE, PF>;
+    case 4: return (const void*)&qk_kernel<DT, 4, NT, STORE, PF>;
+    case 8: return (const void*)&qk_kernel<DT, 8, NT, STORE, PF>;
+    case 16: return (const void*)&qk_kernel<DT, 16, NT, STORE, PF>;
+    case 32: return (const void*)&qk_kernel<DT, 32, NT, STORE, PF>;
+    default: return nullptr;
   }
+}
+
+template <int DT, bool NT, bool STORE>
+static hipError_t launch_qk_nt(const QKParams& p, int groups, hipStream_t s) {
+  void* args[] = {const_cast<QKParams*>(&p)};
+  const int lph = p.head_dim / 16;
+  const void* fn = groups == 4 ? qk_fn<DT, NT, STORE, 4>(lph)
+                 : groups == 3 ? qk_fn<DT, NT, STORE, 3>(lph)
+                 : groups == 2 ? qk_fn<DT, NT, STORE, 2>(lph)
+                               : qk_fn<DT, NT, STORE, 1>(lph);
+  if (!fn || groups < 1 || groups > 4) return hipErrorInvalidConfiguration;
   int block = 256;  // four wavefronts
   if (const char* e = getenv("ANQ_QK_BLOCK")) {
     const int b = atoi(e);
     if (b >= 64 && b <= 1024 && b % 64 == 0) block = b;
   }
+  if (block < p.head_dim / 4) block = p.head_dim / 4;  // one gamma vector per thread (D <= 512)
   const int64_t wpb = block / 64;
   const int64_t grid = (p.tokens * p.waves_per_token + wpb - 1) / wpb;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
@@ -187,24 +257,36 @@ static hipError_t launch_qk_nt(const QKParams& p, hipStream_t s) {
 // Streaming hints (see ld16s) once qkv alone is >= 32 MiB; ANQ_STREAM=0/1 overrides.
 template <int DT, bool STORE>
 static hipError_t launch_qk_dt(QKParams p, hipStream_t s) {
-  // wavefronts per token: one, walking all of the token's head groups, once
-  // the call has enough tokens to fill the GPU (~2048 wavefronts); more, up to
-  // one per head group, for fewer tokens. At 4096 tokens x 32 heads of 128
-  // (bf16) one wavefront per token measured 11.8 us against 12.8 with two.
-  // ANQ_QK_WAVES and ANQ_QK_BLOCK override, for sweeps.
+  // Wavefronts per token W: one once the call has enough tokens to fill the
+  // GPU (~2048 wavefronts), more for fewer tokens; and at least enough that no
+  // wavefront takes more than 4 head groups, all of whose loads it issues at
+  // once. Measured on MI355X (graph of 200 calls, bf16, 4096 tokens): 16+8+8
+  // heads of 128 (4 groups) 11.0 us with one wavefront per token, 12.4 with
+  // the cap at 3 or 2 (two wavefronts); 64+8+8 heads (10 groups) 25.3, 25.0
+  // and 26.1 us with the cap at 4, 3 and 2. 256-lane workgroups: 512 lanes
+  // measured 11.4 us. ANQ_QK_WAVES, ANQ_QK_GROUPS (the cap, 1-4) and
+  // ANQ_QK_BLOCK override, for sweeps.
   const int passes = (p.nq + p.nk + p.nv + 64 / (p.head_dim / 16) - 1) / (64 / (p.head_dim / 16));
   const int64_t want = p.tokens > 0 ? (2048 + p.tokens - 1) / p.tokens : 1;
   int W = (int)(want < passes ? want : passes);
-  if (W < 1) W = 1;
   if (const char* e = getenv("ANQ_QK_WAVES")) {
     if (*e && atoi(e) > 0) W = atoi(e);
   }
-  p.waves_per_token = W < passes ? W : passes;
+  int cap = 4;
+  if (const char* e = getenv("ANQ_QK_GROUPS")) {
+    if (*e && atoi(e) >= 1 && atoi(e) <= 4) cap = atoi(e);
+  }
+  if (W < (passes + cap - 1) / cap) W = (passes + cap - 1) / cap;
+  if (W > passes) W = passes;
+  if (W < 1) W = 1;
+  p.waves_per_token = W;
+  const int groups = (passes + W - 1) / W;  // the most any wavefront takes (<= cap)
   bool stream = p.pairs * (int64_t)p.head_dim * 2 >= ((int64_t)32 << 20);
   if (const char* e = getenv("ANQ_STREAM")) {
     if (*e) stream = atoi(e) != 0;
   }
-  return stream ? launch_qk_nt<DT, true, STORE>(p, s) : launch_qk_nt<DT, false, STORE>(p, s);
+  return stream ? launch_qk_nt<DT, true, STORE>(p, groups, s)
+                : launch_qk_nt<DT, false, STORE>(p, groups, s);
 }
 
 hipError_t launch_qk(int dtype, bool kv_store, const QKParams& p, hipStream_t s) {

@@ -116,3 +116,34 @@ def test_wide_span_midpoint_rows(op):
     assert [float(v) for v in ref["ss"]] == [2.0 ** 120 * (1 + 2.0 ** -23)] * 3 + [2.0 ** 120]
     for k in ["residual", "norm_out", "q"] + (["sf"] if op == "nvfp4" else []):
         np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+
+
+@pytest.mark.parametrize("cap", ["1", "2", "3", "4"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_qk_midpoint_heads(head_dim, dtype, cap, monkeypatch):
+    """Q and K heads whose squares sum exactly to a binary32 midpoint
+    (2^30 + 64, from 32768 and 8), with or without a tiny element whose square
+    float64 cannot hold beside 2^30: the tie rounds to even (down), the rest up
+    through the double-double path. The planted elements sit in both halves of
+    a head, in heads of every pass (17 heads: a ragged last pass), and the op
+    runs with one wavefront per token where the cap on the head groups a
+    wavefront loads at once allows it (so 1-3 groups per wavefront)."""
+    monkeypatch.setenv("ANQ_QK_WAVES", "1")
+    monkeypatch.setenv("ANQ_QK_GROUPS", cap)
+    nq, nk, nv, D = 9, 5, 3, head_dim
+    tokens = 6
+    rng = np.random.default_rng(4711 + D)
+    inp = W.make_qk(40_000 + D, dtype, tokens, nq, nk, nv, D,
+                    positions=rng.integers(0, 32, tokens), max_pos=32, scale=0.05)
+    q = inp.qkv.float().numpy().reshape(tokens, nq + nk + nv, D).copy()
+    tiny = 2.0 ** -24 if dtype == "f16" else 2.0 ** -40
+    for t in range(tokens):
+        for h in (t, nq + (t % nk), (3 * t + 7) % (nq + nk)):
+            q[t, h] = 0.0
+            q[t, h, D // 2 + 3] = 32768.0
+            q[t, h, 1 + t] = 8.0
+            if (t + h) % 3:
+                q[t, h, D - 1 - t] = tiny
+    inp.qkv = _tensor(O.t_encode(q.reshape(tokens, -1).astype(np.float32), dtype), dtype)
+    np.testing.assert_array_equal(gpu_qk(inp), oracle_qk(inp))

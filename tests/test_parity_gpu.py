@@ -264,16 +264,32 @@ def test_every_tiling_matches_the_oracle(hidden, tilings, op, monkeypatch):
             compare_tail(inp, scale, got, ref)
 
 
+@pytest.mark.parametrize("groups", ["", "2", "3"])
 @pytest.mark.parametrize("waves", ["1", "2", "3", "5"])
 @pytest.mark.parametrize("head_dim", [64, 128])
 @pytest.mark.parametrize("block", ["", "64", "1024"])
-def test_qk_waves_per_token_agree(head_dim, waves, block, monkeypatch):
-    """Splitting a token's heads over several wavefronts, and packing
-    wavefronts into workgroups of other sizes, changes nothing."""
+def test_qk_waves_per_token_agree(head_dim, waves, block, groups, monkeypatch):
+    """Splitting a token's heads over several wavefronts (also unevenly: the
+    cap on head groups per wavefront raises the count), and packing wavefronts
+    into workgroups of other sizes, changes nothing."""
     monkeypatch.setenv("ANQ_QK_WAVES", waves)
     monkeypatch.setenv("ANQ_QK_BLOCK", block)
+    monkeypatch.setenv("ANQ_QK_GROUPS", groups)
     pos = np.random.default_rng(3).integers(0, 64, 23)
     inp = W.make_qk(31, "bf16", 23, 9, 5, 3, head_dim, positions=pos, max_pos=64, scale=0.04)
     got = gpu_qk(inp)
     cs = code_stats(got, oracle_qk(inp), e4m3_rank)
     assert cs["bit_exact"], cs
+
+
+@pytest.mark.parametrize("groups", ["", "1", "4"])
+def test_qk_wide_heads_small_workgroups(groups, monkeypatch):
+    """Heads of 512 with 64-lane workgroups asked for: the launcher widens the
+    workgroup to 128 lanes, one gamma vector per lane, and the op still
+    matches (9 groups of 2 heads per token, one wavefront per token)."""
+    monkeypatch.setenv("ANQ_QK_BLOCK", "64")
+    monkeypatch.setenv("ANQ_QK_WAVES", "1")
+    monkeypatch.setenv("ANQ_QK_GROUPS", groups)
+    pos = np.random.default_rng(5).integers(0, 16, 5)
+    inp = W.make_qk(37, "f16", 5, 9, 5, 3, 512, positions=pos, max_pos=16, scale=0.04)
+    np.testing.assert_array_equal(gpu_qk(inp), oracle_qk(inp))
