@@ -380,9 +380,11 @@ Tiling pick_tail_tiling(int32_t vec, int64_t tokens) {
   t.rows = (t.group == 0 && t.block >= 512 && tokens >= 4096) ? 2 : 1;
   const int env_rows = env_int("ANQ_ROWS_PER_GROUP", 0);
   if (env_rows > 0) t.rows = env_rows;
-  // streaming hints once the call is large next to the 256 MB last-level cache
-  // (x alone >= 32 MiB, so >= ~128 MiB of traffic); ANQ_STREAM=0/1 overrides
-  t.stream = (int64_t)vec * 16 * tokens >= ((int64_t)32 << 20);
+  // streaming hints from 1 MiB of x. With inputs coming from HBM they measured
+  // 10-15% faster from 1 to 32 MiB of x on MI355X (fp16 [256, 8192] NVFP4 5.25
+  // -> 4.65 us, [64, 8192] 4.08 -> 3.88) and 3% slower at 256 KiB; with inputs
+  // already in cache, 0-5% slower. ANQ_STREAM=0/1 overrides.
+  t.stream = (int64_t)vec * 16 * tokens >= ((int64_t)1 << 20);
   const int env_stream = env_int("ANQ_STREAM", -1);
   if (env_stream >= 0) t.stream = env_stream != 0;
   const int64_t kMaxGrid = 0x7FFFFFFF;
@@ -412,7 +414,10 @@ Tiling pick_gate_lut_tiling(int32_t vec, int64_t rows) {
   t.rows = (int)(r < 1 ? 1 : (r > 64 ? 64 : r));
   const int env_rows = env_int("ANQ_ROWS_PER_GROUP", 0);
   if (env_rows > 0) t.rows = env_rows;
-  t.stream = (int64_t)vec * 16 * rows >= ((int64_t)32 << 20);
+  // streaming hints from 1 MiB of x, as in the tail tiling (bf16 groups of
+  // 1024, inputs from HBM: [2048, 1024] 6.33 -> 6.04 us, [2048, 8192] 25.6 ->
+  // 24.1, [1024, 8192] 16.4 -> 16.9)
+  t.stream = (int64_t)vec * 16 * rows >= ((int64_t)1 << 20);
   const int env_stream = env_int("ANQ_STREAM", -1);
   if (env_stream >= 0) t.stream = env_stream != 0;
   const int64_t kMaxGrid = 0x7FFFFFFF;
