@@ -140,3 +140,26 @@ def test_random_swizzled_shapes(case):
     np.testing.assert_array_equal(_np(res), ref["residual"])
     np.testing.assert_array_equal(_np(q), ref["q"])
     np.testing.assert_array_equal(_np(sf), O.swizzle_block_scales(ref["sf"]))
+
+
+def _qk_many_token_cases(n=4):
+    rng = np.random.default_rng(909)
+    out = []
+    for i in range(n):
+        head_dim = int(rng.choice([64, 128, 256]))
+        nq, nk, nv = int(rng.integers(1, 40)), int(rng.integers(0, 9)), int(rng.integers(0, 9))
+        out.append((i, ("bf16", "f16")[i % 2], int(rng.integers(2048, 4097)), nq, nk, nv, head_dim))
+    return out
+
+
+@pytest.mark.parametrize("case", _qk_many_token_cases(),
+                         ids=lambda c: f"{c[1]}-t{c[2]}-q{c[3]}k{c[4]}v{c[5]}-d{c[6]}")
+def test_random_qk_many_tokens(case):
+    """Enough tokens for one wavefront per token, so each wavefront loads
+    several head groups at once (the launcher's default path at scale), with
+    random head layouts and positions across an 8192-entry table."""
+    i, dtype, tokens, nq, nk, nv, head_dim = case
+    rng = np.random.default_rng(300 + i)
+    inp = W.make_qk(700 + i, dtype, tokens, nq, nk, nv, head_dim,
+                    positions=rng.integers(0, 8192, tokens), max_pos=8192, scale=0.05)
+    np.testing.assert_array_equal(gpu_qk(inp), oracle_qk(inp))
