@@ -284,7 +284,6 @@ anq::QKParams qk_params(const void* qkv, const void* gamma_q, const void* gamma_
   p.out = out;
   p.eps = eps;
   p.tokens = tokens;
-  p.pairs = tokens * (int64_t)(nq + nk + nv);
   p.nq = nq;
   p.nk = nk;
   p.nv = nv;

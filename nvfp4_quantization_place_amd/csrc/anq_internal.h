@@ -69,7 +69,6 @@ struct QKParams {
   int64_t max_pos;
   float eps;
   int64_t tokens;
-  int64_t pairs;  // tokens * (nq + nk + nv)
   int32_t nq, nk, nv, head_dim;
   int32_t waves_per_token;  // set by the launcher
 };
