@@ -155,19 +155,45 @@ def _scalar(s: torch.Tensor, name: str):
         raise ValueError(f"{name} must be a one-element float32 device tensor")
 
 
+def _need(t, numel: int, dtype, name: str):
+    """t (if given) holds exactly numel elements of dtype. The library takes
+    pointers and sizes and trusts the sizes, so every tensor is checked here,
+    before any launch."""
+    if t is not None and (t.dtype != dtype or t.numel() != numel):
+        raise ValueError(f"{name} must hold {numel} elements of {dtype}, "
+                         f"got {t.numel()} of {t.dtype}")
+
+
+def _tail_shapes(x, residual, gamma, norm, other: str = "residual"):
+    """x and `other` share dtype and shape; gamma [hidden] and norm like x."""
+    tokens, hidden = _rows(x)
+    if residual.dtype != x.dtype or gamma.dtype != x.dtype or residual.shape != x.shape:
+        raise ValueError(f"x, {other} and gamma must share the dtype; x and {other} the shape")
+    _need(gamma, hidden, x.dtype, "gamma")
+    _need(norm, x.numel(), x.dtype, "norm")
+    return tokens, hidden
+
+
+def _nvfp4_outs(q, sf, tokens: int, hidden: int):
+    """q [tokens, hidden/2] and sf [tokens, hidden/16] uint8 (sizes the library
+    accepts: other hidden sizes are rejected there, with ANQ_ERR_SHAPE)."""
+    if hidden > 0 and hidden % 16 == 0:
+        _need(q, tokens * (hidden // 2), torch.uint8, "q")
+        _need(sf, tokens * (hidden // 16), torch.uint8, "sf")
+
+
 def add_rmsnorm_quant_fp8(x, residual, gamma, scale, eps: float, norm_out: bool = False,
                           q=None, norm=None, stream=None):
     """residual += x (in place, rounded to T); n = RMSNorm(residual) * gamma;
     returns (q, norm_out): q uint8 E4M3 codes of n / scale, norm_out n in T or None."""
     dev = _check_gpu(x, residual, gamma, scale, q, norm)
     _scalar(scale, "scale")
-    tokens, hidden = _rows(x)
+    tokens, hidden = _tail_shapes(x, residual, gamma, norm)
+    _need(q, x.numel(), torch.uint8, "q")
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=dev)
     if norm_out and norm is None:
         norm = torch.empty_like(x)
-    if residual.dtype != x.dtype or gamma.dtype != x.dtype or residual.shape != x.shape:
-        raise ValueError("x, residual and gamma must share the dtype; x and residual the shape")
     st = lib().add_rmsnorm_quant_fp8(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(scale), eps,
                                      tokens, hidden, _dtype_code(x), _ptr(q), _ptr(norm),
                                      _stream(dev, stream))
@@ -183,7 +209,8 @@ def add_rmsnorm_quant_nvfp4(x, residual, gamma, global_scale, eps: float, norm_o
     the global scale G, norm_out n in T or None."""
     dev = _check_gpu(x, residual, gamma, global_scale, q, sf, norm)
     _scalar(global_scale, "global_scale")
-    tokens, hidden = _rows(x)
+    tokens, hidden = _tail_shapes(x, residual, gamma, norm)
+    _nvfp4_outs(q, sf, tokens, hidden)
     if hidden % 16 == 0 and hidden > 0:
         qc, sc = hidden // 2, hidden // 16
     else:
@@ -194,14 +221,24 @@ def add_rmsnorm_quant_nvfp4(x, residual, gamma, global_scale, eps: float, norm_o
         sf = torch.empty(*x.shape[:-1], sc, dtype=torch.uint8, device=dev)
     if norm_out and norm is None:
         norm = torch.empty_like(x)
-    if residual.dtype != x.dtype or gamma.dtype != x.dtype or residual.shape != x.shape:
-        raise ValueError("x, residual and gamma must share the dtype; x and residual the shape")
     st = lib().add_rmsnorm_quant_nvfp4(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(global_scale),
                                        eps, tokens, hidden, _dtype_code(x), _ptr(q), _ptr(sf),
                                        _ptr(norm), _stream(dev, stream))
     if st:
         raise AnqError("add_rmsnorm_quant_nvfp4", st)
     return q, sf, norm
+
+
+def _qk_inputs(qkv, gamma_q, gamma_k, positions, cos_sin, nq, nk, head_dim, tokens):
+    """gamma_q / gamma_k [head_dim] in the dtype of qkv where there are Q / K
+    heads, one position per token, and a [max_pos, head_dim] cos|sin table."""
+    if nq > 0:
+        _need(gamma_q, head_dim, qkv.dtype, "gamma_q")
+    if nk > 0:
+        _need(gamma_k, head_dim, qkv.dtype, "gamma_k")
+    _need(positions, tokens, torch.int64, "positions")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != head_dim:
+        raise ValueError(f"cos_sin must be [max_pos, head_dim={head_dim}] float32")
 
 
 def qk_norm_rope_fp8(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: float, nq: int,
@@ -217,6 +254,8 @@ def qk_norm_rope_fp8(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: floa
     if qkv.shape[-1] != cols:
         raise ValueError(f"qkv last dim {qkv.shape[-1]} != (nq+nk+nv)*head_dim = {cols}")
     tokens = qkv.numel() // cols if cols else 0
+    _qk_inputs(qkv, gamma_q, gamma_k, positions, cos_sin, nq, nk, head_dim, tokens)
+    _need(out, qkv.numel(), torch.uint8, "out")
     if out is None:
         out = torch.empty(qkv.shape, dtype=torch.uint8, device=dev)
     max_pos = cos_sin.shape[0]
@@ -253,6 +292,8 @@ def qk_norm_rope_fp8_kv_store(qkv, gamma_q, gamma_k, positions, cos_sin, scale, 
     tokens = qkv.numel() // cols if cols else 0
     if slot_mapping.numel() != tokens:
         raise ValueError("slot_mapping must hold one slot per token")
+    _qk_inputs(qkv, gamma_q, gamma_k, positions, cos_sin, nq, nk, head_dim, tokens)
+    _need(q_out, tokens * nq * head_dim, torch.uint8, "q_out")
     if q_out is None:
         q_out = torch.empty(*qkv.shape[:-1], nq * head_dim, dtype=torch.uint8, device=dev)
     st = lib().qk_norm_rope_fp8_kv_store(
@@ -273,9 +314,7 @@ def add_rmsnorm(x, residual, gamma, eps: float, norm=None, stream=None):
     """residual += x (in place, rounded to T); returns norm_out = RMSNorm(residual) * gamma in T.
     The first kernel of the separated (unfused) tail."""
     dev = _check_gpu(x, residual, gamma, norm)
-    tokens, hidden = _rows(x)
-    if residual.dtype != x.dtype or gamma.dtype != x.dtype or residual.shape != x.shape:
-        raise ValueError("x, residual and gamma must share the dtype; x and residual the shape")
+    tokens, hidden = _tail_shapes(x, residual, gamma, norm)
     if norm is None:
         norm = torch.empty_like(x)
     st = lib().add_rmsnorm(_ptr(x), _ptr(residual), _ptr(gamma), eps, tokens, hidden,
@@ -290,6 +329,7 @@ def quant_fp8(t, scale, q=None, stream=None):
     dev = _check_gpu(t, scale, q)
     _scalar(scale, "scale")
     tokens, hidden = _rows(t)
+    _need(q, t.numel(), torch.uint8, "q")
     if q is None:
         q = torch.empty(t.shape, dtype=torch.uint8, device=dev)
     st = lib().quant_fp8(_ptr(t), _ptr(scale), tokens, hidden, _dtype_code(t), _ptr(q),
@@ -304,6 +344,7 @@ def quant_nvfp4(t, global_scale, q=None, sf=None, stream=None):
     dev = _check_gpu(t, global_scale, q, sf)
     _scalar(global_scale, "global_scale")
     tokens, hidden = _rows(t)
+    _nvfp4_outs(q, sf, tokens, hidden)
     qc, sc = (hidden // 2, hidden // 16) if hidden % 16 == 0 and hidden > 0 else (1, 1)
     if q is None:
         q = torch.empty(*t.shape[:-1], qc, dtype=torch.uint8, device=dev)
@@ -320,6 +361,9 @@ def quant_nvfp4(t, global_scale, q=None, sf=None, stream=None):
 
 
 def _swizzled_sf(t, dev, sf, tokens, hidden):
+    if sf is not None and hidden > 0 and hidden % 16 == 0:
+        r, c = nvfp4_swizzled_sf_shape(tokens, hidden)
+        _need(sf, r * c, torch.uint8, "sf (swizzled)")
     if sf is None and hidden > 0 and hidden % 16 == 0:
         r, c = nvfp4_swizzled_sf_shape(tokens, hidden)
         sf = torch.empty(r, c, dtype=torch.uint8, device=dev)
@@ -333,9 +377,9 @@ def add_rmsnorm_quant_nvfp4_swizzled(x, residual, gamma, global_scale, eps: floa
     layout: sf [roundup(tokens,128), roundup(hidden/16,4)] uint8, padding zeroed."""
     dev = _check_gpu(x, residual, gamma, global_scale, q, sf, norm)
     _scalar(global_scale, "global_scale")
-    tokens, hidden = _rows(x)
-    if residual.dtype != x.dtype or gamma.dtype != x.dtype or residual.shape != x.shape:
-        raise ValueError("x, residual and gamma must share the dtype; x and residual the shape")
+    tokens, hidden = _tail_shapes(x, residual, gamma, norm)
+    if hidden > 0 and hidden % 16 == 0:
+        _need(q, tokens * (hidden // 2), torch.uint8, "q")
     if q is None:
         q = torch.empty(*x.shape[:-1], max(hidden // 2, 1), dtype=torch.uint8, device=dev)
     sf = _swizzled_sf(x, dev, sf, tokens, hidden)
@@ -354,6 +398,8 @@ def quant_nvfp4_swizzled(t, global_scale, q=None, sf=None, stream=None):
     dev = _check_gpu(t, global_scale, q, sf)
     _scalar(global_scale, "global_scale")
     tokens, hidden = _rows(t)
+    if hidden > 0 and hidden % 16 == 0:
+        _need(q, tokens * (hidden // 2), torch.uint8, "q")
     if q is None:
         q = torch.empty(*t.shape[:-1], max(hidden // 2, 1), dtype=torch.uint8, device=dev)
     sf = _swizzled_sf(t, dev, sf, tokens, hidden)
@@ -373,9 +419,8 @@ def gated_rmsnorm_quant_nvfp4(x, z, gamma, global_scale, eps: float, group: int 
     the whole row), then NVFP4: returns (q [.., hidden/2], sf [.., hidden/16])."""
     dev = _check_gpu(x, z, gamma, global_scale, q, sf)
     _scalar(global_scale, "global_scale")
-    tokens, hidden = _rows(x)
-    if z.dtype != x.dtype or gamma.dtype != x.dtype or z.shape != x.shape:
-        raise ValueError("x, z and gamma must share the dtype; x and z the shape")
+    tokens, hidden = _tail_shapes(x, z, gamma, None, other="z")
+    _nvfp4_outs(q, sf, tokens, hidden)
     group = hidden if group is None else group
     qc, sc = (hidden // 2, hidden // 16) if hidden % 16 == 0 and hidden > 0 else (1, 1)
     if q is None:
@@ -410,6 +455,7 @@ def silu_gate_f32(x, z, u=None, stream=None):
     dev = _check_gpu(x, z, u)
     if z.dtype != x.dtype or z.shape != x.shape:
         raise ValueError("x and z must share dtype and shape")
+    _need(u, x.numel(), torch.float32, "u")
     if u is None:
         u = torch.empty(x.shape, dtype=torch.float32, device=dev)
     st = lib().silu_gate_f32(_ptr(x), _ptr(z), x.numel(), _dtype_code(x), _ptr(u),
