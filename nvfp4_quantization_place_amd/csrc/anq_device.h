@@ -29,12 +29,12 @@ __device__ __forceinline__ void st16(void* p, const U4& v) {
   *reinterpret_cast<U4*>(p) = v;
 }
 
-// Row streams of a call much larger than the last-level cache are read once and
-// written once: with NT they carry the non-temporal hint (the `nt` bit of
-// gfx950 global loads and stores), which keeps them from displacing each other
-// in the L2 and the Infinity Cache. Measured on MI355X at 8192 x 7168 and
-// 65536 x 1024, the 16-byte row loads and stores hinted together cut the
-// kernel time by ~10%; either hint alone does little.
+// Row streams are read once and written once: with NT they carry the
+// non-temporal hint (the `nt` bit of gfx950 global loads and stores). Measured
+// on MI355X: at 8192 x 7168 and 65536 x 1024 the 16-byte row loads and stores
+// hinted together cut the kernel time by ~10% (either alone does little); from
+// 1 to 32 MiB of input, with inputs coming from HBM, the hinted loads alone cut
+// it by 5-15%. The launchers choose NT by call size.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
