@@ -92,13 +92,17 @@ def test_extreme_qk(i):
     np.testing.assert_array_equal(gpu_qk(inp), oracle_qk(inp))
 
 
+@pytest.mark.parametrize("stream", ["", "1"])
 @pytest.mark.parametrize("op", ["fp8", "nvfp4"])
-def test_wide_span_midpoint_rows(op):
+def test_wide_span_midpoint_rows(op, stream, monkeypatch):
     """bf16 rows whose large squares sum exactly to a binary32 midpoint
     (2^120 + 2^96) next to tiny ones (2^-10, 2^-30, 2^-60) far below float64's reach
     of the large part: the exact sum is just above the midpoint and rounds up,
     and the double-double fallback keeps the tiny part in its low word. A row
-    without the tiny element is the exact tie (to even, down)."""
+    without the tiny element is the exact tie (to even, down). With streaming
+    hints forced on, the fallback re-reads residual elements the same lanes
+    have just written with non-temporal stores."""
+    monkeypatch.setenv("ANQ_STREAM", stream)
     H = 64
     rows = []
     for tiny in (2.0 ** -10, 2.0 ** -30, 2.0 ** -60, 0.0):

@@ -130,15 +130,18 @@ def _tail_from_arrays(op, dtype, x, res, gamma, eps=1e-6, scale=0.02, norm=True)
                         scale=scale if op == "fp8" else None, norm_out=norm)
 
 
+@pytest.mark.parametrize("stream", ["", "1"])
 @pytest.mark.parametrize("op", ["fp8", "nvfp4"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("hidden", [64, 1024, 7168])
-def test_edge_rows(op, dtype, hidden):
+def test_edge_rows(op, dtype, hidden, stream, monkeypatch):
     """All-zero rows (with a negative gamma: signed zeros), a one-hot row,
     x = -residual (exact cancellation), x50 and x1000 outliers (E4M3 and E2M1
     saturation), tiny values (E4M3 subnormals), and rows whose exact sum of
     squares sits on or just past a binary32 rounding midpoint that float64
-    cannot resolve (the double-double path)."""
+    cannot resolve (the double-double path, which re-reads the residual the
+    lanes just stored: with and without streaming hints)."""
+    monkeypatch.setenv("ANQ_STREAM", stream)
     rng = np.random.default_rng(hidden)
     H = hidden
     rows = []
