@@ -116,11 +116,11 @@ def _check_gpu(*ts) -> int:
     for t in ts:
         if t is None:
             continue
-        if not t.is_cuda:
+        d = t.get_device()  # -1 for a CPU tensor
+        if d < 0:
             raise ValueError("all tensors must live on the GPU (there is no CPU path)")
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
-        d = t.get_device()
         if dev < 0:
             dev = d
         elif d != dev:
