@@ -178,8 +178,19 @@ tail_kernel(TailParams p) {
     voff[k] = (uint32_t)(vok[k] ? v : V - 1) * 16u;
   }
 
+  constexpr bool kLut = EPI == kEpiGatedNvfp4Lut;  // bf16 z, gate from the LDS table
+  constexpr bool kGated = EPI == kEpiGatedNvfp4 || kLut;  // `res` is z: read only, never stored
+  constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz || kGated;
+  // Wide rows (4 or 8 vectors per lane) keep only what the next step needs in
+  // registers: the row's vectors are loaded at the top of each row (no
+  // prefetch of the next one), the residual is held packed in T (it is the
+  // stored value, so unpacking it again is exact), and gamma is loaded after
+  // the sum of squares. Holding all of it at once spilled: at bf16 [2048,
+  // 32768] and [1024, 65536] the kernel streamed at 4.0 and 1.1 TB/s.
+  constexpr bool kWide = K >= 4 && !kGated;
+
   U4 gv[K], xv[K], rv[K];
-  {
+  if constexpr (!kWide) {
     const size_t rb = (size_t)(row < last ? row : last) * row_bytes;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -195,9 +206,6 @@ tail_kernel(TailParams p) {
     sc = *p.scale;
     if constexpr (EPI == kEpiFp8) inv_sc = recip_rn(sc);  // s is a positive normal <= 2^119
   }
-  constexpr bool kLut = EPI == kEpiGatedNvfp4Lut;  // bf16 z, gate from the LDS table
-  constexpr bool kGated = EPI == kEpiGatedNvfp4 || kLut;  // `res` is z: read only, never stored
-  constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz || kGated;
   extern __shared__ uint4 gate_tab4[];  // kLut: kGateTab entries (dynamic shared memory)
   const float* gate_tab = reinterpret_cast<const float*>(gate_tab4);
   static_assert(!kLut || DT == kBF16, "the gate table covers bf16 z");
@@ -214,9 +222,102 @@ tail_kernel(TailParams p) {
   typename std::conditional<(G > 0), GroupReduce<(G > 0 ? G : 64)>, BlockReduce>::type red;
   if constexpr (G == 0) red.lds = lds;
 
+  // ss / width rounded once, then r = RN(1 / RN(sqrt(mean + eps))): the
+  // Markstein-corrected quotient with RN(1/width) (three operations) inside the
+  // range where it holds with margin, the IEEE division outside it (sums near
+  // underflow or overflow; rare, and uniform over the row)
+  auto row_r = [&](float ss) {
+    float mean;
+    if (ss >= 0x1p-100f && ss <= 0x1p120f) {
+      const float q0 = ss * inv_w;
+      const float t = __builtin_fmaf(q0, width_f, -ss);
+      mean = __builtin_fmaf(-t, inv_w, q0);
+    } else {
+      mean = ss / width_f;
+    }
+    return recip_rn_ext(sqrtf(mean + p.eps));
+  };
+
+  // The epilogue of the lane's vector k of `row`: the norm output and the codes.
+  // Codes and block scales are stored without the streaming hint: their 8-,
+  // 4- and 1-byte stores only fill whole lines once merged in the L2, and
+  // hinting them measured ~5% slower on MI355X.
+  auto emit = [&](int64_t row_, int k, const float (&n)[8]) {
+    if constexpr (NORM) {
+      if (vok[k]) st16s<NT>(row_ptr<G>(nout, (size_t)row_ * row_bytes) + voff[k], pack8<DT>(n));
+    }
+    if constexpr (EPI == kEpiFp8) {
+      uint32_t lo, hi;
+      fp8_codes8(n, sc, inv_sc, lo, hi);
+      if (vok[k]) st8s<false>(row_ptr<G>(p.q, (size_t)row_ * p.hidden) + voff[k] / 2, lo, hi);
+    } else if constexpr (kNvfp4) {
+      uint32_t w, sfc;
+      nvfp4_half_block(n, sc, mult_tab, w, sfc);
+      if (vok[k]) {
+        st4s<false>(row_ptr<G>(p.q, (size_t)row_ * (p.hidden / 2)) + voff[k] / 4, w);
+        if ((lane & 1) == 0) {
+          if constexpr (EPI == kEpiNvfp4Swz)
+            store_block_scale_swizzled(p.sf, row_, (int32_t)(voff[k] / 32), p.hidden / 16,
+                                       p.sf_tiles, (uint8_t)sfc);
+          else  // linear [rows, width/16] (the plain and the gated variants)
+            st1s<false>(row_ptr<G>(p.sf, (size_t)row_ * (p.hidden / 16)) + voff[k] / 32,
+                        (uint8_t)sfc);
+        }
+      }
+    }
+  };
+
   int parity = 0;
   for (; row < row_end; ++row, parity ^= 1) {
     uint8_t* rrow = row_ptr<G>(res, (size_t)row * row_bytes);
+    // the rare double-double pass re-reads the lane's own just-stored residual
+    // elements (the gated variant recomputes u from x and z below)
+    auto stored_h = [&](int k, int i) {
+      float f, unused;
+      unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + voff[k] + 2 * i), f, unused);
+      return f;
+    };
+    if constexpr (kWide) {
+      const uint8_t* xrow = row_ptr<G>(x, (size_t)row * row_bytes);
+      U4 hv[K];
+      double acc = 0.0;
+      {
+        U4 xw[K], rw[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          xw[k] = ld16s<NT>(xrow + voff[k]);
+          rw[k] = ld16s<NT>(rrow + voff[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          float xf[8], rf[8], s[8], h[8];
+          unpack8<DT>(xw[k], xf);
+          unpack8<DT>(rw[k], rf);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s[i] = xf[i] + rf[i];
+          hv[k] = pack8<DT>(s);
+          if (vok[k]) st16s<NT>(rrow + voff[k], hv[k]);
+          unpack8<DT>(hv[k], h);
+          double a = 0.0;  // vectors past the row end hold a clamped copy: not counted
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = __builtin_fma((double)h[i], (double)h[i], a);
+          acc += vok[k] ? a : 0.0;
+        }
+      }
+      U4 gw[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) gw[k] = ld16(gam + voff[k]);  // lands during the reduction
+      const float r = row_r(row_sum_squares<K>(acc, p.hidden, parity, vok, red, stored_h));
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        float h[8], g[8], n[8];
+        unpack8<DT>(hv[k], h);
+        unpack8<DT>(gw[k], g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) n[i] = (h[i] * r) * g[i];
+        emit(row, k, n);
+      }
+    } else {
     if constexpr (kGated) {  // each group of a token has its own gamma slice
       if (p.gamma_period > 1) {
         const uint8_t* grow = gam + (size_t)(row % p.gamma_period) * row_bytes;
@@ -269,58 +370,18 @@ tail_kernel(TailParams p) {
         unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + voff[k] + 2 * i), zf, unused);
         return silu_gate(xf, zf, exp2_tab);
       });
-    } else {  // the fallback re-reads the lane's own just-stored residual elements
-      ss = row_sum_squares<K>(acc, p.hidden, parity, vok, red, [&](int k, int i) {
-        float f, unused;
-        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + voff[k] + 2 * i), f, unused);
-        return f;
-      });
-    }
-    // ss / width rounded once: the Markstein-corrected quotient with RN(1/width)
-    // (three operations) inside the range where it holds with margin, the IEEE
-    // division outside it (sums near underflow or overflow; rare, and uniform
-    // over the row)
-    float mean;
-    if (ss >= 0x1p-100f && ss <= 0x1p120f) {
-      const float q0 = ss * inv_w;
-      const float t = __builtin_fmaf(q0, width_f, -ss);
-      mean = __builtin_fmaf(-t, inv_w, q0);
     } else {
-      mean = ss / width_f;
+      ss = row_sum_squares<K>(acc, p.hidden, parity, vok, red, stored_h);
     }
-    const float r = recip_rn_ext(sqrtf(mean + p.eps));
-
-    // Codes and block scales are stored without the streaming hint: their 8-,
-    // 4- and 1-byte stores only fill whole lines once merged in the L2, and
-    // hinting them measured ~5% slower on MI355X.
+    const float r = row_r(ss);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       float g[8], n[8];
       unpack8<DT>(gv[k], g);
 #pragma unroll
       for (int i = 0; i < 8; ++i) n[i] = (h[k][i] * r) * g[i];
-      if constexpr (NORM) {
-        if (vok[k]) st16s<NT>(row_ptr<G>(nout, (size_t)row * row_bytes) + voff[k], pack8<DT>(n));
-      }
-      if constexpr (EPI == kEpiFp8) {
-        uint32_t lo, hi;
-        fp8_codes8(n, sc, inv_sc, lo, hi);
-        if (vok[k]) st8s<false>(row_ptr<G>(p.q, (size_t)row * p.hidden) + voff[k] / 2, lo, hi);
-      } else if constexpr (kNvfp4) {
-        uint32_t w, sfc;
-        nvfp4_half_block(n, sc, mult_tab, w, sfc);
-        if (vok[k]) {
-          st4s<false>(row_ptr<G>(p.q, (size_t)row * (p.hidden / 2)) + voff[k] / 4, w);
-          if ((lane & 1) == 0) {
-            if constexpr (EPI == kEpiNvfp4Swz)
-              store_block_scale_swizzled(p.sf, row, (int32_t)(voff[k] / 32), p.hidden / 16,
-                                         p.sf_tiles, (uint8_t)sfc);
-            else  // linear [rows, width/16] (the plain and the gated variants)
-              st1s<false>(row_ptr<G>(p.sf, (size_t)row * (p.hidden / 16)) + voff[k] / 32,
-                          (uint8_t)sfc);
-          }
-        }
-      }
+      emit(row, k, n);
+    }
     }
   }
   if constexpr (EPI == kEpiNvfp4Swz) {  // lane groups share the padded rows
