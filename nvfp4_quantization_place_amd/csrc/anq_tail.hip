@@ -139,7 +139,7 @@ __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int 
 // Register budget: 7 wavefronts per SIMD (<= 72 VGPRs) for one vector per
 // lane, which then needs no spills; 4 (<= 128) for rows wider than 8192 and
 // for the gated variant (its binary64 exp needs the registers).
-template <int DT, int EPI, bool NORM, int K, int G, bool NT>
+template <int DT, int EPI, bool NORM, int K, int G, bool NT, bool SL = (K >= 4)>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 && EPI != kEpiGatedNvfp4Lut ? 256 : 1024),
                                amdgpu_waves_per_eu(K == 1 && EPI != kEpiGatedNvfp4 &&
                                                            EPI != kEpiGatedNvfp4Lut ? 7 : 4)))
@@ -181,13 +181,14 @@ tail_kernel(TailParams p) {
   constexpr bool kLut = EPI == kEpiGatedNvfp4Lut;  // bf16 z, gate from the LDS table
   constexpr bool kGated = EPI == kEpiGatedNvfp4 || kLut;  // `res` is z: read only, never stored
   constexpr bool kNvfp4 = EPI == kEpiNvfp4 || EPI == kEpiNvfp4Swz || kGated;
-  // Wide rows (4 or 8 vectors per lane) keep only what the next step needs in
-  // registers: the row's vectors are loaded at the top of each row (no
-  // prefetch of the next one), the residual is held packed in T (it is the
-  // stored value, so unpacking it again is exact), and gamma is loaded after
-  // the sum of squares. Holding all of it at once spilled: at bf16 [2048,
-  // 32768] and [1024, 65536] the kernel streamed at 4.0 and 1.1 TB/s.
-  constexpr bool kWide = K >= 4 && !kGated;
+  // The streamlined row (SL: 4 or 8 vectors per lane, and 2 when a workgroup
+  // takes one row) keeps only what the next step needs in registers: the row's
+  // vectors are loaded at the top of each row (no prefetch of the next one),
+  // the residual is held packed in T (it is the stored value, so unpacking it
+  // again is exact), and gamma is loaded after the sum of squares. Holding all
+  // of it at once spilled: at bf16 [2048, 32768] and [1024, 65536] the kernel
+  // streamed at 4.0 and 1.1 TB/s.
+  constexpr bool kWide = SL && !kGated;
 
   U4 gv[K], xv[K], rv[K];
   if constexpr (!kWide) {
@@ -496,7 +497,17 @@ static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
   else if (t.group == 64 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 64, NT>;
   else if (t.group == 64 && t.vec_per_lane == 2) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 64, NT>;
   else if (t.group == 0 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 0, NT>;
-  else if (t.group == 0 && t.vec_per_lane == 2) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 0, NT>;
+  else if (t.group == 0 && t.vec_per_lane == 2) {
+    // one row per workgroup: the streamlined row (no prefetch to keep); bf16
+    // [1024, 12288] NVFP4 + norm 24.3 -> 21.9 us, [64, 16384] 6.2 -> 5.8. With
+    // two or more rows the prefetching row is faster ([4096, 16384] 99.7
+    // against 102.4 us).
+    constexpr bool kGatedEpi = EPI == kEpiGatedNvfp4 || EPI == kEpiGatedNvfp4Lut;
+    if constexpr (!kGatedEpi) {
+      if (t.rows == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 0, NT, true>;
+    }
+    if (!fn) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 0, NT>;
+  }
   else if (t.group == 0 && t.vec_per_lane == 4) fn = (const void*)&tail_kernel<DT, EPI, NORM, 4, 0, NT>;
   else if (t.group == 0 && t.vec_per_lane == 8) fn = (const void*)&tail_kernel<DT, EPI, NORM, 8, 0, NT>;
   if (!fn) return hipErrorInvalidConfiguration;
