@@ -100,12 +100,12 @@ __device__ __forceinline__ T* row_ptr(T* base, size_t off) {
 // time through `elem(k, i)` (re-reading memory, not registers), so it adds no
 // registers to the common path.
 template <int K, class Red, class Elem>
-__device__ __forceinline__ float row_sum_squares_dd(const bool* vok, const Red& red,
+__device__ __forceinline__ float row_sum_squares_dd(int lane, int L, int V, const Red& red,
                                                     const Elem& elem) {
   double hi = 0.0, lo = 0.0;
 #pragma unroll 1
   for (int k = 0; k < K; ++k) {
-    if (!vok[k]) continue;
+    if (lane + k * L >= V) continue;  // a clamped copy past the row end
 #pragma unroll 1
     for (int i = 0; i < 8; ++i) {
       const double d = (double)elem(k, i);
@@ -118,13 +118,13 @@ __device__ __forceinline__ float row_sum_squares_dd(const bool* vok, const Red& 
 
 template <int K, class Red, class Elem>
 __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int parity,
-                                                 const bool* vok, const Red& red,
+                                                 int lane, int L, int V, const Red& red,
                                                  const Elem& elem) {
   const double S = red.sum(acc, parity);
   const float ss = (float)S;
   // float64 error of a sum of `width` non-negative terms is below width * 2^-53 * S
   if (near_f32_midpoint(S, width))  // uniform over the row
-    return row_sum_squares_dd<K>(vok, red, elem);
+    return row_sum_squares_dd<K>(lane, L, V, red, elem);
   return ss;
 }
 
@@ -177,6 +177,9 @@ tail_kernel(TailParams p) {
     vok[k] = v < V;
     voff[k] = (uint32_t)(vok[k] ? v : V - 1) * 16u;
   }
+  // the same offset for a run-time k (the rare double-double pass loops over
+  // k without unrolling; indexing voff there would put the array in scratch)
+  auto vec_off = [&](int k) { return (uint32_t)min(lane + k * L, V - 1) * 16u; };
 
   constexpr bool kLut = EPI == kEpiGatedNvfp4Lut;  // bf16 z, gate from the LDS table
   constexpr bool kGated = EPI == kEpiGatedNvfp4 || kLut;  // `res` is z: read only, never stored
@@ -189,6 +192,7 @@ tail_kernel(TailParams p) {
   // of it at once spilled: at bf16 [2048, 32768] and [1024, 65536] the kernel
   // streamed at 4.0 and 1.1 TB/s.
   constexpr bool kWide = SL && !kGated;
+  constexpr bool kReload = kWide && K >= 8;
 
   U4 gv[K], xv[K], rv[K];
   if constexpr (!kWide) {
@@ -275,7 +279,7 @@ tail_kernel(TailParams p) {
     // elements (the gated variant recomputes u from x and z below)
     auto stored_h = [&](int k, int i) {
       float f, unused;
-      unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + voff[k] + 2 * i), f, unused);
+      unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + vec_off(k) + 2 * i), f, unused);
       return f;
     };
     if constexpr (kWide) {
@@ -308,11 +312,13 @@ tail_kernel(TailParams p) {
       U4 gw[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) gw[k] = ld16(gam + voff[k]);  // lands during the reduction
-      const float r = row_r(row_sum_squares<K>(acc, p.hidden, parity, vok, red, stored_h));
+      const float r = row_r(row_sum_squares<K>(acc, p.hidden, parity, lane, L, V, red, stored_h));
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         float h[8], g[8], n[8];
-        unpack8<DT>(hv[k], h);
+        // at 8 vectors per lane the residual is read back (the lane's own
+        // just-stored vector, from the cache) instead of held across the sum
+        unpack8<DT>(kReload ? ld16(rrow + voff[k]) : hv[k], h);
         unpack8<DT>(gw[k], g);
 #pragma unroll
         for (int i = 0; i < 8; ++i) n[i] = (h[i] * r) * g[i];
@@ -365,14 +371,14 @@ tail_kernel(TailParams p) {
     float ss;
     if constexpr (kGated) {  // the fallback recomputes u from x and z
       const uint8_t* xrow = row_ptr<G>(x, (size_t)row * row_bytes);
-      ss = row_sum_squares<K>(acc, p.hidden, parity, vok, red, [&](int k, int i) {
+      ss = row_sum_squares<K>(acc, p.hidden, parity, lane, L, V, red, [&](int k, int i) {
         float xf, zf, unused;
-        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(xrow + voff[k] + 2 * i), xf, unused);
-        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + voff[k] + 2 * i), zf, unused);
+        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(xrow + vec_off(k) + 2 * i), xf, unused);
+        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + vec_off(k) + 2 * i), zf, unused);
         return silu_gate(xf, zf, exp2_tab);
       });
     } else {
-      ss = row_sum_squares<K>(acc, p.hidden, parity, vok, red, stored_h);
+      ss = row_sum_squares<K>(acc, p.hidden, parity, lane, L, V, red, stored_h);
     }
     const float r = row_r(ss);
 #pragma unroll
