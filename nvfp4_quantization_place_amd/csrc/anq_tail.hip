@@ -283,6 +283,14 @@ tail_kernel(TailParams p) {
       return f;
     };
     if constexpr (kWide) {
+      // Opaque per row (4 and 8 vectors per lane): otherwise the compiler
+      // hoists a 64-bit address per vector and output stream (base + offset)
+      // out of the row loop, which at 8 vectors per lane costs more registers
+      // than the row itself. At 2 vectors the hoisted form measured faster.
+      if constexpr (K >= 4) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) asm volatile("" : "+v"(voff[k]));
+      }
       const uint8_t* xrow = row_ptr<G>(x, (size_t)row * row_bytes);
       U4 hv[K];
       double acc = 0.0;
