@@ -98,7 +98,8 @@ def test_workload_qk_full_compare():
 
 # ------------------------------------------------------------ shape grid ---
 
-GRID_H = [16, 48, 128, 256, 400, 512, 1024, 1040, 2048, 4112, 7168, 8192, 16400, 32768, 65536]
+GRID_H = [16, 48, 128, 256, 400, 512, 1024, 1040, 2048, 4112, 7168, 8192, 16400, 32768, 40976,
+          65520, 65536]  # 40976 and 65520: 8 vectors per lane, the last ones past the row end
 
 
 @pytest.mark.parametrize("hidden", GRID_H)
@@ -133,7 +134,7 @@ def _tail_from_arrays(op, dtype, x, res, gamma, eps=1e-6, scale=0.02, norm=True)
 @pytest.mark.parametrize("stream", ["", "1"])
 @pytest.mark.parametrize("op", ["fp8", "nvfp4"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("hidden", [64, 1024, 7168, 16384, 32768, 65536])
+@pytest.mark.parametrize("hidden", [64, 1024, 7168, 16384, 32768, 40976, 65536])
 def test_edge_rows(op, dtype, hidden, stream, monkeypatch):
     """All-zero rows (with a negative gamma: signed zeros), a one-hot row,
     x = -residual (exact cancellation), x50 and x1000 outliers (E4M3 and E2M1

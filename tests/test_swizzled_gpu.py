@@ -32,7 +32,7 @@ def _poisoned_sf(tokens, hidden):
 
 
 SHAPES = [(1, 16), (5, 48), (37, 1040), (128, 7168), (129, 1024), (300, 2048), (64, 8192),
-          (3, 16400)]
+          (3, 16400), (2, 40976), (3, 65520)]
 
 
 @pytest.mark.parametrize("tokens,hidden", SHAPES)
