@@ -258,13 +258,23 @@ tail_kernel(TailParams p) {
     } else if constexpr (kNvfp4) {
       uint32_t w, sfc;
       nvfp4_half_block(n, sc, mult_tab, w, sfc);
+      if constexpr (EPI == kEpiNvfp4Swz) {
+        // Four consecutive blocks of a row are one 32-bit word of the swizzled
+        // layout. Their codes sit in lanes 8j, 8j+2, 8j+4, 8j+6 (two lanes per
+        // block, lane groups a multiple of 8 wide), so lane 8j gathers them
+        // and stores the word; codes of vectors past the row end count as 0,
+        // which also writes the padded columns of the last word.
+        const uint32_t c8 = vok[k] ? (sfc & 0xffu) : 0u;
+        const uint32_t word = c8 | ((uint32_t)__shfl_down((int)c8, 2) << 8) |
+                              ((uint32_t)__shfl_down((int)c8, 4) << 16) |
+                              ((uint32_t)__shfl_down((int)c8, 6) << 24);
+        if (vok[k] && (lane & 7) == 0)
+          st4s<false>(p.sf + sf_swizzled_offset(row_, (int32_t)(voff[k] / 32), p.sf_tiles), word);
+      }
       if (vok[k]) {
         st4s<false>(row_ptr<G>(p.q, (size_t)row_ * (p.hidden / 2)) + voff[k] / 4, w);
-        if ((lane & 1) == 0) {
-          if constexpr (EPI == kEpiNvfp4Swz)
-            store_block_scale_swizzled(p.sf, row_, (int32_t)(voff[k] / 32), p.hidden / 16,
-                                       p.sf_tiles, (uint8_t)sfc);
-          else  // linear [rows, width/16] (the plain and the gated variants)
+        if constexpr (EPI != kEpiNvfp4Swz) {
+          if ((lane & 1) == 0)  // linear [rows, width/16] (the plain and the gated variants)
             st1s<false>(row_ptr<G>(p.sf, (size_t)row_ * (p.hidden / 16)) + voff[k] / 32,
                         (uint8_t)sfc);
         }
