@@ -16,6 +16,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -41,17 +42,21 @@ def flags() -> list[str]:
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library; returns its path."""
-    objs = []
     cc = hipcc()
     tmp = os.path.join(PKG, "_build")
     os.makedirs(tmp, exist_ok=True)
-    for src in SOURCES:
-        obj = os.path.join(tmp, src + ".o")
-        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    objs = [os.path.join(tmp, src + ".o") for src in SOURCES]
+
+    def compile_one(i: int) -> None:
+        cmd = [cc, *flags(), "-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        objs.append(obj)
+
+    # one compiler process per source, at most as many as there are cores (16 at most)
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(compile_one, range(len(SOURCES))))
     out_tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
     if verbose:

@@ -67,3 +67,76 @@ def oracle_qk(inp: W.QKInputs, tokens=None) -> np.ndarray:
     return O.qk_norm_rope_fp8(W.bits(inp.qkv)[sel], W.bits(inp.gamma_q), W.bits(inp.gamma_k),
                               inp.positions.numpy()[sel], inp.cos_sin, inp.scale, inp.eps, inp.nq,
                               inp.nk, inp.nv, inp.head_dim, inp.dtype)["out"]
+
+
+def gpu_full_workload(k: int, variant: str = "fused") -> dict:
+    """Outputs of one full-size launch of workload k on fresh inputs, as 2-D
+    numpy arrays named like the oracle digests in tests/golden/workload_digests.json.
+
+    variant: "fused" (the workload's own op), "separated" (add_rmsnorm, then the
+    standalone quantiser on its T norm output), "swizzled" (NVFP4 with the
+    128x4-tiled block scales) or "kv_store" (the Q/K op into a KV pool)."""
+    import json
+    import os
+
+    import nvfp4_quantization_place_amd as A
+    golden = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    with open(os.path.join(golden, "workload_scalars.json")) as fh:
+        scalars = json.load(fh)
+    inp = W.make_config(k)
+    dev = "cuda"
+    if isinstance(inp, W.QKInputs):
+        args = (inp.qkv.to(dev), inp.gamma_q.to(dev), inp.gamma_k.to(dev), inp.positions.to(dev),
+                torch.from_numpy(inp.cos_sin).to(dev),
+                torch.tensor([inp.scale], dtype=torch.float32, device=dev), inp.eps, inp.nq,
+                inp.nk, inp.nv, inp.head_dim)
+        if variant == "fused":
+            out = {"out": A.qk_norm_rope_fp8(*args)}
+        elif variant == "kv_store":
+            with open(os.path.join(golden, "workload_digests.json")) as fh:
+                kv = json.load(fh)[str(k)]["kv_store"]
+            slots = torch.from_numpy(W.kv_slots(k, inp.tokens, kv["num_slots"])).to(dev)
+            pool = torch.full((kv["num_slots"], (inp.nk + inp.nv) * inp.head_dim), kv["sentinel"],
+                              dtype=torch.uint8, device=dev)
+            q = A.qk_norm_rope_fp8_kv_store(*args, slots, pool)
+            out = {"kv_store_q": q, "kv_store_pool": pool}
+        else:
+            raise ValueError(variant)
+        torch.cuda.synchronize()
+        return {n: _np(v) for n, v in out.items()}
+    x, res, g = inp.x.to(dev), inp.residual.to(dev), inp.gamma.to(dev)
+    s = float(inp.scale) if inp.op == "fp8" else scalars[str(k)]["global_scale"]
+    st = torch.tensor([s], dtype=torch.float32, device=dev)
+    if inp.op == "gated":
+        q, sf = A.gated_rmsnorm_quant_nvfp4(x, res, g, st, inp.eps, group=inp.meta["group"])
+        out = {"q": q, "sf": sf}
+    elif variant == "separated":
+        norm = A.add_rmsnorm(x, res, g, inp.eps)
+        if inp.op == "fp8":
+            out = {"q_separated": A.quant_fp8(norm, st)}
+        else:
+            q, sf = A.quant_nvfp4(norm, st)
+            out = {"q_separated": q, "sf_separated": sf}
+        out["residual"] = res
+        if inp.norm_out:
+            out["norm_out"] = norm
+    elif variant == "swizzled":
+        q, sf, norm = A.add_rmsnorm_quant_nvfp4_swizzled(x, res, g, st, inp.eps,
+                                                         norm_out=inp.norm_out)
+        out = {"residual": res, "q": q, "sf_swizzled": sf}
+        if norm is not None:
+            out["norm_out"] = norm
+    elif variant == "fused":
+        if inp.op == "fp8":
+            q, norm = A.add_rmsnorm_quant_fp8(x, res, g, st, inp.eps, norm_out=inp.norm_out)
+            out = {"q": q}
+        else:
+            q, sf, norm = A.add_rmsnorm_quant_nvfp4(x, res, g, st, inp.eps, norm_out=inp.norm_out)
+            out = {"q": q, "sf": sf}
+        out["residual"] = res
+        if norm is not None:
+            out["norm_out"] = norm
+    else:
+        raise ValueError(variant)
+    torch.cuda.synchronize()
+    return {n: _np(v) for n, v in out.items()}

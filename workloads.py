@@ -16,7 +16,8 @@ Generator (stated once so any reader can re-derive every input):
     r = sqrt(-2 ln(1-u1)), z0 = r cos(2 pi u2), z1 = r sin(2 pi u2); both are used.
   * each float64 draw is converted to fp16 / bf16 by torch's CPU conversion.
 
-Tensor ids: x = 0, residual = 1, gamma (gamma_q) = 2, outlier mask = 3, qkv = 4, gamma_k = 5.
+Tensor ids: x = 0, residual = 1, gamma (gamma_q) = 2, outlier mask = 3, qkv = 4, gamma_k = 5,
+KV-cache slot order = 6.
 
 Workload shapes follow the fused NVFP4 tail of TensorRT-LLM issue #17900
 ("Performance result" and "Correctness" sections: FP16 [64, 8192]; hidden
@@ -38,7 +39,7 @@ _GOLDEN = 0x9E3779B97F4A7C15
 _M1 = 0xBF58476D1CE4E5B9
 _M2 = 0x94D049BB133111EB
 
-TID_X, TID_RES, TID_GAMMA, TID_MASK, TID_QKV, TID_GAMMA_K = 0, 1, 2, 3, 4, 5
+TID_X, TID_RES, TID_GAMMA, TID_MASK, TID_QKV, TID_GAMMA_K, TID_SLOTS = 0, 1, 2, 3, 4, 5, 6
 
 
 def _s64(v: int) -> int:
@@ -245,6 +246,46 @@ def make_config(k: int):
     return make_tail(k, c["op"], c["dtype"], c["tokens"], c["hidden"], x=c["x"], res=c["res"],
                      gamma=c["gamma"], eps=c["eps"], scale=c["scale"], norm_out=c["norm_out"],
                      outliers=c["outliers"], name=c["name"])
+
+
+def kv_slots(seed: int, tokens: int, num_slots: int, pad_every: int = 16) -> np.ndarray:
+    """Distinct KV-cache slots for `tokens` tokens in a pool of num_slots rows:
+    the first `tokens` entries of the permutation that sorts num_slots uniform
+    draws (stable sort), with every pad_every-th token (index % pad_every ==
+    pad_every - 1) set to -1, a padding token that stores nothing."""
+    order = np.argsort(uniform(seed, TID_SLOTS, num_slots), kind="stable")[:tokens]
+    s = order.astype(np.int64)
+    if pad_every > 0:
+        s[pad_every - 1::pad_every] = -1
+    return s
+
+
+MEMBERS_PER_DIGEST = 64
+
+
+def row_chunk_digests(a, chunk_rows: int) -> dict:
+    """SHA-256 of a 2-D array's bytes (whole, 64 hex digits) and of each run of
+    chunk_rows consecutive rows (16 hex digits each): a stored expected output
+    is compared without storing it, and a mismatch names the rows it is in."""
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().contiguous()
+        a = a.view(torch.uint8).numpy() if a.dtype != torch.uint8 else a.numpy()
+    a = np.ascontiguousarray(a)
+    if a.ndim != 2:
+        raise ValueError("row_chunk_digests takes a 2-D array")
+    raw = a.view(np.uint8).reshape(a.shape[0], -1)
+    whole = hashlib.sha256()
+    chunks = []
+    for r0 in range(0, raw.shape[0], chunk_rows):
+        b = raw[r0:r0 + chunk_rows].tobytes()
+        whole.update(b)
+        chunks.append(hashlib.sha256(b).hexdigest()[:16])
+    return {"sha256": whole.hexdigest(), "chunk_rows": chunk_rows, "chunks": chunks}
+
+
+def chunk_rows_for(rows: int) -> int:
+    """Rows per digest chunk: about MEMBERS_PER_DIGEST chunks per tensor."""
+    return max(1, -(-rows // MEMBERS_PER_DIGEST))
 
 
 def checksum(t) -> str:
