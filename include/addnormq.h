@@ -11,10 +11,11 @@
  *
  * Sources of the operations (the pages these ops are built from):
  *  - TensorRT-LLM issue #17900, "[Performance]: Fuse local NVFP4 tail after
- *    NCCL fallback", Proposal: residual + RMSNorm + NVFP4 in one launch, with or
- *    without a returned high-precision norm output; contiguous FP16/BF16 with
- *    matching dtypes; per-tensor scale a contiguous FP32 scalar; no bias;
- *    hidden divisible by 16; unsupported cases keep a separated path.
+ *    NCCL fallback", Proposal: the residual add, RMSNorm and NVFP4 quantisation
+ *    as one launch. The fused case it describes: the norm output is optional;
+ *    activations are fp16 or bf16, all of one type; the scale is one fp32
+ *    value; there is no bias; hidden is a multiple of 16. Anything else falls
+ *    back to the unfused kernels.
  *  - TensorRT-LLM PR #17288, "Add NanoJet backend for AutoDeploy prefill-only
  *    FP8 inference", Description: RMSNorm with FP8 quantisation in the kernel
  *    epilogue; FP8 projection with an in-place residual add; Q/K RMSNorm and
@@ -60,7 +61,12 @@
  *    runs asynchronously. Scales are read on the device when the kernel runs,
  *    so a producer kernel on the same stream may write them.
  *  - Arguments are validated on the host before any HIP call. A rejected call
- *    returns a nonzero status and enqueues nothing. tokens == 0 returns ANQ_OK
+ *    returns a nonzero status and enqueues nothing. The ANQ_* environment
+ *    variables (ANQ_TAIL_TILING, ANQ_ROWS_PER_GROUP, ANQ_STREAM, ANQ_GATE_LUT,
+ *    ANQ_GATE_BLOCK, ANQ_QK_WAVES, ANQ_QK_GROUPS, ANQ_QK_BLOCK) override the
+ *    tiling for sweeps; a value the library has no kernel for is refused with
+ *    ANQ_ERR_CONFIG, never replaced by a default. Every accepted tiling gives
+ *    bit-identical results. tokens == 0 returns ANQ_OK
  *    and enqueues nothing; the token-sized buffers (x, z, residual, q, sf,
  *    norm_out, qkv, positions, out, slot_mapping) may then be NULL, as empty
  *    tensors are.
@@ -110,7 +116,8 @@ enum {
   ANQ_ERR_ALIAS = 5,       /* buffers overlap where they must not */
   ANQ_ERR_UNSUPPORTED = 6, /* hidden > ANQ_MAX_HIDDEN, head_dim not supported, rotary_dim != head_dim */
   ANQ_ERR_LAUNCH = 7,      /* the HIP launch failed (message via anq_status_string) */
-  ANQ_ERR_VALUE = 8        /* eps negative or not finite, max_pos < 1, negative head counts or num_slots */
+  ANQ_ERR_VALUE = 8,       /* eps negative or not finite, max_pos < 1, negative head counts or num_slots */
+  ANQ_ERR_CONFIG = 9       /* an ANQ_* tuning variable in the environment names no kernel of the library */
 };
 
 /* Largest hidden size the fused row kernels take (a row is held in registers). */
@@ -118,8 +125,8 @@ enum {
 
 /*
  * Residual add + RMSNorm + per-tensor FP8 E4M3 quantisation.
- * (NanoJet "RMSNorm with FP8 quantization in the kernel epilogue" and the
- * in-place residual add, TensorRT-LLM PR #17288, Description.)
+ * (TensorRT-LLM PR #17288, Description: the NanoJet backend quantises to FP8
+ * in the epilogue of its RMSNorm and adds the residual in place.)
  *
  *   x        [tokens, hidden] T, read only
  *   residual [tokens, hidden] T, in/out: receives h = RNE_T(x + residual)
@@ -130,7 +137,7 @@ enum {
  *   norm_out [tokens, hidden] T (output) or NULL to skip it
  */
 int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* gamma, const float* scale,
-                          float eps, int64_t tokens, int64_t hidden, int dtype, uint8_t* q,
+                          float eps, int64_t tokens, int64_t hidden, anq_dtype dtype, uint8_t* q,
                           void* norm_out, void* stream);
 
 /*
@@ -146,7 +153,7 @@ int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* gamma, cons
  */
 int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
                             const float* global_scale, float eps, int64_t tokens, int64_t hidden,
-                            int dtype, uint8_t* q, uint8_t* sf, void* norm_out, void* stream);
+                            anq_dtype dtype, uint8_t* q, uint8_t* sf, void* norm_out, void* stream);
 
 /*
  * Q/K per-head RMSNorm + NeoX RoPE + uniform FP8 E4M3 store of a fused QKV
@@ -173,7 +180,7 @@ int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
 int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
                      const int64_t* positions, const float* cos_sin, int64_t max_pos,
                      const float* scale, float eps, int64_t tokens, int32_t nq, int32_t nk,
-                     int32_t nv, int32_t head_dim, int32_t rotary_dim, int dtype, uint8_t* out,
+                     int32_t nv, int32_t head_dim, int32_t rotary_dim, anq_dtype dtype, uint8_t* out,
                      void* stream);
 
 /*
@@ -197,7 +204,7 @@ int qk_norm_rope_fp8_kv_store(const void* qkv, const void* gamma_q, const void* 
                               const int64_t* positions, const float* cos_sin, int64_t max_pos,
                               const float* scale, float eps, int64_t tokens, int32_t nq,
                               int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
-                              int dtype, const int64_t* slot_mapping, int64_t num_slots,
+                              anq_dtype dtype, const int64_t* slot_mapping, int64_t num_slots,
                               uint8_t* q_out, uint8_t* kv_cache, void* stream);
 
 /*
@@ -212,14 +219,14 @@ int qk_norm_rope_fp8_kv_store(const void* qkv, const void* gamma_q, const void* 
  *   as in the numerics above. norm_out is required. No scale, no codes.
  */
 int add_rmsnorm(const void* x, void* residual, const void* gamma, float eps, int64_t tokens,
-                int64_t hidden, int dtype, void* norm_out, void* stream);
+                int64_t hidden, anq_dtype dtype, void* norm_out, void* stream);
 
 /*
  * quant_fp8: q_i = E4M3(in_i / s) for in [tokens, hidden] T (hidden % 16 == 0,
  *   hidden < 2^34: no ANQ_MAX_HIDDEN limit, the quantisers keep no row in
  *   registers), s = *scale; q [tokens, hidden] uint8.
  */
-int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden, int dtype,
+int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden, anq_dtype dtype,
               uint8_t* q, void* stream);
 
 /*
@@ -228,7 +235,7 @@ int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden
  *   E4M3, under G = *global_scale.
  */
 int quant_nvfp4(const void* in, const float* global_scale, int64_t tokens, int64_t hidden,
-                int dtype, uint8_t* q, uint8_t* sf, void* stream);
+                anq_dtype dtype, uint8_t* q, uint8_t* sf, void* stream);
 
 /*
  * Gated RMSNorm + NVFP4: the gated variant among the fused NVFP4 norm ops
@@ -245,7 +252,7 @@ int quant_nvfp4(const void* in, const float* global_scale, int64_t tokens, int64
  */
 int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const void* gamma,
                               const float* global_scale, float eps, int64_t tokens,
-                              int64_t hidden, int64_t group, int dtype, uint8_t* q, uint8_t* sf,
+                              int64_t hidden, int64_t group, anq_dtype dtype, uint8_t* q, uint8_t* sf,
                               void* stream);
 
 /*
@@ -253,7 +260,7 @@ int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const void* gamma,
  * binary32 steps stated there, for n elements (n % 8 == 0) of T; u [n]
  * binary32 (output). x, z and u 16-byte aligned.
  */
-int silu_gate_f32(const void* x, const void* z, int64_t n, int dtype, float* u, void* stream);
+int silu_gate_f32(const void* x, const void* z, int64_t n, anq_dtype dtype, float* u, void* stream);
 
 /*
  * NVFP4 with the block scales in the swizzled layout a block-scaled GEMM reads
@@ -270,12 +277,12 @@ int silu_gate_f32(const void* x, const void* z, int64_t n, int dtype, float* u, 
  */
 int add_rmsnorm_quant_nvfp4_swizzled(const void* x, void* residual, const void* gamma,
                                      const float* global_scale, float eps, int64_t tokens,
-                                     int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
+                                     int64_t hidden, anq_dtype dtype, uint8_t* q, uint8_t* sf,
                                      void* norm_out, void* stream);
 
 /* quant_nvfp4 with the swizzled block-scale layout above. */
 int quant_nvfp4_swizzled(const void* in, const float* global_scale, int64_t tokens,
-                         int64_t hidden, int dtype, uint8_t* q, uint8_t* sf, void* stream);
+                         int64_t hidden, anq_dtype dtype, uint8_t* q, uint8_t* sf, void* stream);
 
 /*
  * Padded shape [sf_rows, sf_cols] of the swizzled block-scale buffer:
@@ -292,6 +299,22 @@ int anq_nvfp4_swizzled_sf_shape(int64_t tokens, int64_t hidden, int64_t* sf_rows
  * Host only, no HIP call. Returns ANQ_OK, or ANQ_ERR_NULL / ANQ_ERR_SHAPE.
  */
 int anq_nvfp4_shape(int64_t tokens, int64_t hidden, int64_t* q_cols, int64_t* sf_cols);
+
+/*
+ * The calibration stream (a measurement aid, not part of the method): one pass
+ * that reads read_bytes of src and writes write_bytes of dst with the 16-byte
+ * vector accesses of the fused kernels, the non-temporal hint on every access
+ * when nontemporal == 1 (0: none). Timed with the read/write byte counts of a
+ * call, it is the practical streaming ceiling of that mix on this GPU.
+ * With n_in = read_bytes / 16 and n_out = write_bytes / 16 units of 16 bytes,
+ * unit j < n_out of dst receives the XOR of source units j, j + n_out, ...
+ * below n_in (each source unit is read once); where j >= n_in that XOR starts
+ * from the unit (j as a little-endian 64-bit integer, then 8 zero bytes).
+ * Both sizes are multiples of 16 (ANQ_ERR_SHAPE otherwise, also when bytes are
+ * read but none written); src and dst 16-byte aligned and disjoint.
+ */
+int anq_stream_rw(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                  int nontemporal, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* anq_status_string(int status);

@@ -10,6 +10,7 @@ without a GPU, every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch  # loads the HIP runtime the library binds to
@@ -18,15 +19,15 @@ __all__ = ["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4", "qk_norm_rope_fp8
            "qk_norm_rope_fp8_kv_store", "add_rmsnorm_quant_nvfp4_swizzled",
            "gated_rmsnorm_quant_nvfp4", "silu_gate_f32",
            "quant_nvfp4_swizzled", "nvfp4_swizzled_sf_shape", "add_rmsnorm", "quant_fp8", "quant_nvfp4",
-           "nvfp4_shape", "status_string", "selfcheck_arith", "lib", "AnqError", "LIB_PATH",
-           "ANQ_F16", "ANQ_BF16", "STATUS"]
+           "nvfp4_shape", "status_string", "selfcheck_arith", "stream_rw", "lib", "AnqError",
+           "LIB_PATH", "ANQ_F16", "ANQ_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddnormq.so")
 
 ANQ_F16, ANQ_BF16 = 0, 1
 STATUS = {0: "ANQ_OK", 1: "ANQ_ERR_NULL", 2: "ANQ_ERR_SHAPE", 3: "ANQ_ERR_DTYPE",
           4: "ANQ_ERR_ALIGN", 5: "ANQ_ERR_ALIAS", 6: "ANQ_ERR_UNSUPPORTED", 7: "ANQ_ERR_LAUNCH",
-          8: "ANQ_ERR_VALUE"}
+          8: "ANQ_ERR_VALUE", 9: "ANQ_ERR_CONFIG"}
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -51,6 +52,7 @@ _SIGS = {
     "anq_nvfp4_swizzled_sf_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "anq_nvfp4_shape": [_I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "anq_status_string": [ctypes.c_int],
+    "anq_stream_rw": [_P, _I64, _P, _I64, ctypes.c_int, _P],
 }
 
 _lib = None
@@ -62,6 +64,16 @@ class AnqError(RuntimeError):
         super().__init__(f"{fn}: {STATUS.get(code, code)} ({status_string(code)})")
 
 
+def load(path: str) -> ctypes.CDLL:
+    """Open a build of the C ABI at `path` and declare its signatures."""
+    L = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "anq_status_string" else ctypes.c_int
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """The loaded C-ABI library (raises if it has not been built)."""
     global _lib
@@ -69,12 +81,7 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m nvfp4_quantization_place_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, args in _SIGS.items():
-            fn = getattr(L, name)
-            fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name == "anq_status_string" else ctypes.c_int
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 
@@ -82,8 +89,11 @@ def status_string(code: int) -> str:
     return lib().anq_status_string(code).decode()
 
 
+@functools.lru_cache(maxsize=1024)
 def nvfp4_shape(tokens: int, hidden: int) -> tuple[int, int]:
-    """(q_cols, sf_cols) of the NVFP4 outputs: hidden/2 packed bytes and hidden/16 scales per row."""
+    """(q_cols, sf_cols) of the NVFP4 outputs, from the library's one shape
+    helper (anq_nvfp4_shape): hidden/2 packed bytes and hidden/16 scales per
+    row. Raises AnqError (ANQ_ERR_SHAPE) for a hidden size the ops reject."""
     q, s = _I64(), _I64()
     st = lib().anq_nvfp4_shape(tokens, hidden, ctypes.byref(q), ctypes.byref(s))
     if st:
@@ -91,6 +101,7 @@ def nvfp4_shape(tokens: int, hidden: int) -> tuple[int, int]:
     return q.value, s.value
 
 
+@functools.lru_cache(maxsize=1024)
 def nvfp4_swizzled_sf_shape(tokens: int, hidden: int) -> tuple[int, int]:
     """(rows, cols) of the swizzled block-scale buffer: tokens padded to 128,
     hidden/16 padded to 4."""
@@ -174,12 +185,24 @@ def _tail_shapes(x, residual, gamma, norm, other: str = "residual"):
     return tokens, hidden
 
 
-def _nvfp4_outs(q, sf, tokens: int, hidden: int):
-    """q [tokens, hidden/2] and sf [tokens, hidden/16] uint8 (sizes the library
-    accepts: other hidden sizes are rejected there, with ANQ_ERR_SHAPE)."""
-    if hidden > 0 and hidden % 16 == 0:
-        _need(q, tokens * (hidden // 2), torch.uint8, "q")
-        _need(sf, tokens * (hidden // 16), torch.uint8, "sf")
+def _nvfp4_outs(q, sf, lead: tuple, tokens: int, hidden: int, dev: int, swizzled: bool = False):
+    """The NVFP4 outputs of a call: q [.., q_cols] and sf [.., sf_cols] uint8
+    (or the padded swizzled sf buffer), the caller's after a size check or new
+    ones, with every shape from the library's shape helpers."""
+    qc, sc = nvfp4_shape(tokens, hidden)
+    _need(q, tokens * qc, torch.uint8, "q")
+    if q is None:
+        q = torch.empty(*lead, qc, dtype=torch.uint8, device=dev)
+    if swizzled:
+        r, c = nvfp4_swizzled_sf_shape(tokens, hidden)
+        _need(sf, r * c, torch.uint8, "sf (swizzled)")
+        if sf is None:
+            sf = torch.empty(r, c, dtype=torch.uint8, device=dev)
+    else:
+        _need(sf, tokens * sc, torch.uint8, "sf")
+        if sf is None:
+            sf = torch.empty(*lead, sc, dtype=torch.uint8, device=dev)
+    return q, sf
 
 
 def add_rmsnorm_quant_fp8(x, residual, gamma, scale, eps: float, norm_out: bool = False,
@@ -210,15 +233,7 @@ def add_rmsnorm_quant_nvfp4(x, residual, gamma, global_scale, eps: float, norm_o
     dev = _check_gpu(x, residual, gamma, global_scale, q, sf, norm)
     _scalar(global_scale, "global_scale")
     tokens, hidden = _tail_shapes(x, residual, gamma, norm)
-    _nvfp4_outs(q, sf, tokens, hidden)
-    if hidden % 16 == 0 and hidden > 0:
-        qc, sc = hidden // 2, hidden // 16
-    else:
-        qc, sc = max(hidden // 2, 1), max(hidden // 16, 1)
-    if q is None:
-        q = torch.empty(*x.shape[:-1], qc, dtype=torch.uint8, device=dev)
-    if sf is None:
-        sf = torch.empty(*x.shape[:-1], sc, dtype=torch.uint8, device=dev)
+    q, sf = _nvfp4_outs(q, sf, x.shape[:-1], tokens, hidden, dev)
     if norm_out and norm is None:
         norm = torch.empty_like(x)
     st = lib().add_rmsnorm_quant_nvfp4(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(global_scale),
@@ -344,12 +359,7 @@ def quant_nvfp4(t, global_scale, q=None, sf=None, stream=None):
     dev = _check_gpu(t, global_scale, q, sf)
     _scalar(global_scale, "global_scale")
     tokens, hidden = _rows(t)
-    _nvfp4_outs(q, sf, tokens, hidden)
-    qc, sc = (hidden // 2, hidden // 16) if hidden % 16 == 0 and hidden > 0 else (1, 1)
-    if q is None:
-        q = torch.empty(*t.shape[:-1], qc, dtype=torch.uint8, device=dev)
-    if sf is None:
-        sf = torch.empty(*t.shape[:-1], sc, dtype=torch.uint8, device=dev)
+    q, sf = _nvfp4_outs(q, sf, t.shape[:-1], tokens, hidden, dev)
     st = lib().quant_nvfp4(_ptr(t), _ptr(global_scale), tokens, hidden, _dtype_code(t), _ptr(q),
                            _ptr(sf), _stream(dev, stream))
     if st:
@@ -360,16 +370,6 @@ def quant_nvfp4(t, global_scale, q=None, sf=None, stream=None):
 # ------------------------------------------------------------ swizzled block scales
 
 
-def _swizzled_sf(t, dev, sf, tokens, hidden):
-    if sf is not None and hidden > 0 and hidden % 16 == 0:
-        r, c = nvfp4_swizzled_sf_shape(tokens, hidden)
-        _need(sf, r * c, torch.uint8, "sf (swizzled)")
-    if sf is None and hidden > 0 and hidden % 16 == 0:
-        r, c = nvfp4_swizzled_sf_shape(tokens, hidden)
-        sf = torch.empty(r, c, dtype=torch.uint8, device=dev)
-    return sf if sf is not None else torch.empty(1, dtype=torch.uint8, device=dev)
-
-
 def add_rmsnorm_quant_nvfp4_swizzled(x, residual, gamma, global_scale, eps: float,
                                      norm_out: bool = False, q=None, sf=None, norm=None,
                                      stream=None):
@@ -378,11 +378,7 @@ def add_rmsnorm_quant_nvfp4_swizzled(x, residual, gamma, global_scale, eps: floa
     dev = _check_gpu(x, residual, gamma, global_scale, q, sf, norm)
     _scalar(global_scale, "global_scale")
     tokens, hidden = _tail_shapes(x, residual, gamma, norm)
-    if hidden > 0 and hidden % 16 == 0:
-        _need(q, tokens * (hidden // 2), torch.uint8, "q")
-    if q is None:
-        q = torch.empty(*x.shape[:-1], max(hidden // 2, 1), dtype=torch.uint8, device=dev)
-    sf = _swizzled_sf(x, dev, sf, tokens, hidden)
+    q, sf = _nvfp4_outs(q, sf, x.shape[:-1], tokens, hidden, dev, swizzled=True)
     if norm_out and norm is None:
         norm = torch.empty_like(x)
     st = lib().add_rmsnorm_quant_nvfp4_swizzled(
@@ -398,11 +394,7 @@ def quant_nvfp4_swizzled(t, global_scale, q=None, sf=None, stream=None):
     dev = _check_gpu(t, global_scale, q, sf)
     _scalar(global_scale, "global_scale")
     tokens, hidden = _rows(t)
-    if hidden > 0 and hidden % 16 == 0:
-        _need(q, tokens * (hidden // 2), torch.uint8, "q")
-    if q is None:
-        q = torch.empty(*t.shape[:-1], max(hidden // 2, 1), dtype=torch.uint8, device=dev)
-    sf = _swizzled_sf(t, dev, sf, tokens, hidden)
+    q, sf = _nvfp4_outs(q, sf, t.shape[:-1], tokens, hidden, dev, swizzled=True)
     st = lib().quant_nvfp4_swizzled(_ptr(t), _ptr(global_scale), tokens, hidden, _dtype_code(t),
                                     _ptr(q), _ptr(sf), _stream(dev, stream))
     if st:
@@ -420,13 +412,8 @@ def gated_rmsnorm_quant_nvfp4(x, z, gamma, global_scale, eps: float, group: int 
     dev = _check_gpu(x, z, gamma, global_scale, q, sf)
     _scalar(global_scale, "global_scale")
     tokens, hidden = _tail_shapes(x, z, gamma, None, other="z")
-    _nvfp4_outs(q, sf, tokens, hidden)
+    q, sf = _nvfp4_outs(q, sf, x.shape[:-1], tokens, hidden, dev)
     group = hidden if group is None else group
-    qc, sc = (hidden // 2, hidden // 16) if hidden % 16 == 0 and hidden > 0 else (1, 1)
-    if q is None:
-        q = torch.empty(*x.shape[:-1], qc, dtype=torch.uint8, device=dev)
-    if sf is None:
-        sf = torch.empty(*x.shape[:-1], sc, dtype=torch.uint8, device=dev)
     st = lib().gated_rmsnorm_quant_nvfp4(_ptr(x), _ptr(z), _ptr(gamma), _ptr(global_scale), eps,
                                          tokens, hidden, group, _dtype_code(x), _ptr(q), _ptr(sf),
                                          _stream(dev, stream))
@@ -463,3 +450,20 @@ def silu_gate_f32(x, z, u=None, stream=None):
     if st:
         raise AnqError("silu_gate_f32", st)
     return u
+
+
+def stream_rw(src, read_bytes: int, dst, write_bytes: int, nontemporal: bool = True,
+              stream=None):
+    """The calibration stream (anq_stream_rw): one pass reading read_bytes of
+    src and writing write_bytes of dst, no arithmetic; src and dst are uint8
+    device tensors at least that large."""
+    dev = _check_gpu(src, dst)
+    if src.dtype != torch.uint8 or dst.dtype != torch.uint8:
+        raise ValueError("src and dst must be uint8")
+    if src.numel() < read_bytes or dst.numel() < write_bytes:
+        raise ValueError("src / dst smaller than the bytes asked for")
+    st = lib().anq_stream_rw(_ptr(src), read_bytes, _ptr(dst), write_bytes, int(nontemporal),
+                             _stream(dev, stream))
+    if st:
+        raise AnqError("anq_stream_rw", st)
+    return dst

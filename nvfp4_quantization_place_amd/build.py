@@ -22,7 +22,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libaddnormq.so")
-SOURCES = ["anq_api.hip", "anq_tail.hip", "anq_qk.hip", "anq_quant.hip", "anq_selfcheck.hip"]
+# host C++ (the front end and the tiling choice; no device code) and HIP sources
+HOST_SOURCES = ["anq_api.cpp", "anq_tiling.cpp"]
+HIP_SOURCES = ["anq_tail.hip", "anq_qk.hip", "anq_quant.hip", "anq_selfcheck.hip", "anq_stream.hip"]
+SOURCES = HOST_SOURCES + HIP_SOURCES
 ARCH = "gfx950"
 
 
@@ -48,7 +51,8 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(tmp, src + ".o") for src in SOURCES]
 
     def compile_one(i: int) -> None:
-        cmd = [cc, *flags(), "-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]]
+        lang = ["-x", "c++"] if SOURCES[i] in HOST_SOURCES else []
+        cmd = [cc, *flags(), *lang, "-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)

@@ -1,9 +1,11 @@
 // C-ABI front end: argument validation (host only, before any HIP call),
 // tiling choice and launch. The contract of every entry point is stated in
-// include/addnormq.h.
+// include/addnormq.h. Plain host C++: the launchers it calls are declared in
+// anq_internal.h and defined next to their kernels.
 #include <math.h>
-#include <stdlib.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "../../include/addnormq.h"
 #include "anq_internal.h"
@@ -58,13 +60,13 @@ int check_tail(const void* x, const void* residual, const void* gamma, const flo
   return ANQ_OK;
 }
 
-int launch_status(hipError_t e) { return e == hipSuccess ? ANQ_OK : ANQ_ERR_LAUNCH; }
+int launch_status(int e) { return e == 0 ? ANQ_OK : ANQ_ERR_LAUNCH; }
 
 }  // namespace
 
 extern "C" int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* gamma,
                                      const float* scale, float eps, int64_t tokens, int64_t hidden,
-                                     int dtype, uint8_t* q, void* norm_out, void* stream) {
+                                     anq_dtype dtype, uint8_t* q, void* norm_out, void* stream) {
   int64_t act = 0;
   int st = check_tail(x, residual, gamma, scale, eps, tokens, hidden, dtype, q, norm_out, &act);
   if (st != ANQ_OK) return st;
@@ -85,10 +87,10 @@ extern "C" int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* 
   p.tokens = tokens;
   p.hidden = (int32_t)hidden;
   p.vec = (int32_t)(hidden / 8);
-  const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
+  anq::Tiling t;
+  if ((st = anq::pick_tail_tiling(p.vec, tokens, &t)) != ANQ_OK) return st;
   p.rows_per_group = t.rows;
-  return launch_status(anq::launch_tail(dtype, anq::kEpiFp8, norm_out != nullptr, p, t,
-                                        static_cast<hipStream_t>(stream)));
+  return launch_status(anq::launch_tail(dtype, anq::kEpiFp8, norm_out != nullptr, p, t, stream));
 }
 
 namespace {
@@ -129,18 +131,18 @@ int rmsnorm_nvfp4(const void* x, void* residual, const void* gamma, const float*
   p.hidden = (int32_t)hidden;
   p.vec = (int32_t)(hidden / 8);
   p.sf_tiles = swizzled ? (int32_t)sf_tiles_of(hidden) : 0;
-  const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
+  anq::Tiling t;
+  if ((st = anq::pick_tail_tiling(p.vec, tokens, &t)) != ANQ_OK) return st;
   p.rows_per_group = t.rows;
   return launch_status(anq::launch_tail(dtype, swizzled ? anq::kEpiNvfp4Swz : anq::kEpiNvfp4,
-                                        norm_out != nullptr, p, t,
-                                        static_cast<hipStream_t>(stream)));
+                                        norm_out != nullptr, p, t, stream));
 }
 
 }  // namespace
 
 extern "C" int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
                                        const float* global_scale, float eps, int64_t tokens,
-                                       int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
+                                       int64_t hidden, anq_dtype dtype, uint8_t* q, uint8_t* sf,
                                        void* norm_out, void* stream) {
   return rmsnorm_nvfp4(x, residual, gamma, global_scale, eps, tokens, hidden, dtype, q, sf,
                        norm_out, false, stream);
@@ -148,7 +150,7 @@ extern "C" int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void
 
 extern "C" int add_rmsnorm_quant_nvfp4_swizzled(const void* x, void* residual, const void* gamma,
                                                 const float* global_scale, float eps,
-                                                int64_t tokens, int64_t hidden, int dtype,
+                                                int64_t tokens, int64_t hidden, anq_dtype dtype,
                                                 uint8_t* q, uint8_t* sf, void* norm_out,
                                                 void* stream) {
   return rmsnorm_nvfp4(x, residual, gamma, global_scale, eps, tokens, hidden, dtype, q, sf,
@@ -157,7 +159,7 @@ extern "C" int add_rmsnorm_quant_nvfp4_swizzled(const void* x, void* residual, c
 
 extern "C" int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const void* gamma,
                                          const float* global_scale, float eps, int64_t tokens,
-                                         int64_t hidden, int64_t group, int dtype, uint8_t* q,
+                                         int64_t hidden, int64_t group, anq_dtype dtype, uint8_t* q,
                                          uint8_t* sf, void* stream) {
   if (!gamma || !global_scale || (tokens != 0 && (!x || !z || !q || !sf))) return ANQ_ERR_NULL;
   if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
@@ -194,16 +196,21 @@ extern "C" int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const voi
   // below 1024 (the 32 KiB copy per workgroup is then not amortised).
   bool lut = dtype == ANQ_BF16 && group <= 1024 && p.tokens >= 2048;
   if (const char* e = getenv("ANQ_GATE_LUT")) {
-    if (*e) lut = atoi(e) != 0 && dtype == ANQ_BF16 && group <= 1024;
+    if (*e) {
+      if (strcmp(e, "0") != 0 && strcmp(e, "1") != 0) return ANQ_ERR_CONFIG;
+      lut = e[0] == '1' && dtype == ANQ_BF16 && group <= 1024;  // the table covers bf16 z only
+    }
   }
-  const anq::Tiling t = lut ? anq::pick_gate_lut_tiling(p.vec, p.tokens)
-                            : anq::pick_tail_tiling(p.vec, p.tokens);
+  anq::Tiling t;
+  const int st = lut ? anq::pick_gate_lut_tiling(p.vec, p.tokens, &t)
+                     : anq::pick_tail_tiling(p.vec, p.tokens, &t);
+  if (st != ANQ_OK) return st;
   p.rows_per_group = t.rows;
   return launch_status(anq::launch_tail(dtype, lut ? anq::kEpiGatedNvfp4Lut : anq::kEpiGatedNvfp4,
-                                        false, p, t, static_cast<hipStream_t>(stream)));
+                                        false, p, t, stream));
 }
 
-extern "C" int silu_gate_f32(const void* x, const void* z, int64_t n, int dtype, float* u,
+extern "C" int silu_gate_f32(const void* x, const void* z, int64_t n, anq_dtype dtype, float* u,
                              void* stream) {
   if (n != 0 && (!x || !z || !u)) return ANQ_ERR_NULL;
   if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
@@ -213,15 +220,15 @@ extern "C" int silu_gate_f32(const void* x, const void* z, int64_t n, int dtype,
   const Span ins[2] = {span(x, n * 2), span(z, n * 2)};
   if (any_alias(outs, 1, ins, 2)) return ANQ_ERR_ALIAS;
   if (n == 0) return ANQ_OK;
-  return launch_status(anq::launch_gate(dtype, x, z, u, n / 8, static_cast<hipStream_t>(stream)));
+  if ((n / 8 + 255) / 256 > 0x7FFFFFFF) return ANQ_ERR_SHAPE;
+  return launch_status(anq::launch_gate(dtype, x, z, u, n / 8, stream));
 }
 
 extern "C" int anq_selfcheck_arith(uint64_t* counts, void* stream) {
   if (!counts) return ANQ_ERR_NULL;
   if (!aligned(counts, 8)) return ANQ_ERR_ALIGN;
   static_assert(anq::kSelfcheckCounts == ANQ_SELFCHECK_COUNTS, "count array length");
-  return launch_status(anq::launch_selfcheck(reinterpret_cast<unsigned long long*>(counts),
-                                             static_cast<hipStream_t>(stream)));
+  return launch_status(anq::launch_selfcheck(reinterpret_cast<unsigned long long*>(counts), stream));
 }
 
 namespace {
@@ -272,7 +279,7 @@ int check_qk(const void* qkv, const void* gamma_q, const void* gamma_k, const in
 anq::QKParams qk_params(const void* qkv, const void* gamma_q, const void* gamma_k,
                         const int64_t* positions, const float* cos_sin, int64_t max_pos,
                         const float* scale, float eps, int64_t tokens, int32_t nq, int32_t nk,
-                        int32_t nv, int32_t head_dim, uint8_t* out) {
+                        int32_t nv, int32_t head_dim, int32_t rotary_dim, uint8_t* out) {
   anq::QKParams p{};
   p.qkv = qkv;
   p.gamma_q = gamma_q;
@@ -288,7 +295,16 @@ anq::QKParams qk_params(const void* qkv, const void* gamma_q, const void* gamma_
   p.nk = nk;
   p.nv = nv;
   p.head_dim = head_dim;
+  p.rotary_dim = rotary_dim;
   return p;
+}
+
+int launch_qk_op(int dtype, int store, anq::QKParams& p, void* stream) {
+  anq::QKTiling t;
+  const int st = anq::pick_qk_tiling(p, &t);
+  if (st != ANQ_OK) return st;
+  p.waves_per_token = t.waves_per_token;
+  return launch_status(anq::launch_qk(dtype, store, p, t, stream));
 }
 
 }  // namespace
@@ -297,20 +313,20 @@ extern "C" int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void
                                 const int64_t* positions, const float* cos_sin, int64_t max_pos,
                                 const float* scale, float eps, int64_t tokens, int32_t nq,
                                 int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
-                                int dtype, uint8_t* out, void* stream) {
+                                anq_dtype dtype, uint8_t* out, void* stream) {
   const int st = check_qk(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens, nq,
                           nk, nv, head_dim, rotary_dim, dtype, out, false, nullptr, 0, nullptr);
   if (st != ANQ_OK || tokens == 0) return st;
-  const anq::QKParams p = qk_params(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps,
-                                    tokens, nq, nk, nv, head_dim, out);
-  return launch_status(anq::launch_qk(dtype, false, p, static_cast<hipStream_t>(stream)));
+  anq::QKParams p = qk_params(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps,
+                              tokens, nq, nk, nv, head_dim, rotary_dim, out);
+  return launch_qk_op(dtype, anq::kStoreNone, p, stream);
 }
 
 extern "C" int qk_norm_rope_fp8_kv_store(const void* qkv, const void* gamma_q, const void* gamma_k,
                                          const int64_t* positions, const float* cos_sin,
                                          int64_t max_pos, const float* scale, float eps,
                                          int64_t tokens, int32_t nq, int32_t nk, int32_t nv,
-                                         int32_t head_dim, int32_t rotary_dim, int dtype,
+                                         int32_t head_dim, int32_t rotary_dim, anq_dtype dtype,
                                          const int64_t* slot_mapping, int64_t num_slots,
                                          uint8_t* q_out, uint8_t* kv_cache, void* stream) {
   const int st = check_qk(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens, nq,
@@ -318,15 +334,15 @@ extern "C" int qk_norm_rope_fp8_kv_store(const void* qkv, const void* gamma_q, c
                           kv_cache);
   if (st != ANQ_OK || tokens == 0) return st;
   anq::QKParams p = qk_params(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens,
-                              nq, nk, nv, head_dim, q_out);
+                              nq, nk, nv, head_dim, rotary_dim, q_out);
   p.kv = kv_cache;
   p.slots = slot_mapping;
   p.num_slots = nk + nv > 0 ? num_slots : 0;
-  return launch_status(anq::launch_qk(dtype, true, p, static_cast<hipStream_t>(stream)));
+  return launch_qk_op(dtype, anq::kStoreUniform, p, stream);
 }
 
 extern "C" int add_rmsnorm(const void* x, void* residual, const void* gamma, float eps,
-                           int64_t tokens, int64_t hidden, int dtype, void* norm_out, void* stream) {
+                           int64_t tokens, int64_t hidden, anq_dtype dtype, void* norm_out, void* stream) {
   if (!gamma || (tokens != 0 && (!x || !residual || !norm_out))) return ANQ_ERR_NULL;
   if (!valid_dtype(dtype)) return ANQ_ERR_DTYPE;
   if (tokens < 0 || hidden <= 0 || hidden % 16 != 0) return ANQ_ERR_SHAPE;
@@ -353,10 +369,11 @@ extern "C" int add_rmsnorm(const void* x, void* residual, const void* gamma, flo
   p.tokens = tokens;
   p.hidden = (int32_t)hidden;
   p.vec = (int32_t)(hidden / 8);
-  const anq::Tiling t = anq::pick_tail_tiling(p.vec, tokens);
+  anq::Tiling t;
+  const int st = anq::pick_tail_tiling(p.vec, tokens, &t);
+  if (st != ANQ_OK) return st;
   p.rows_per_group = t.rows;
-  return launch_status(anq::launch_tail(dtype, anq::kEpiNone, true, p, t,
-                                        static_cast<hipStream_t>(stream)));
+  return launch_status(anq::launch_tail(dtype, anq::kEpiNone, true, p, t, stream));
 }
 
 namespace {
@@ -385,24 +402,26 @@ int quant_common(const void* in, const float* scale, int64_t tokens, int64_t hid
   p.sf_tiles = swizzled ? (int32_t)sf_tiles_of(hidden) : 0;
   p.pad_rows = swizzled ? ((tokens + 127) / 128) * 128 - tokens : 0;
   const int epi = !nvfp4 ? anq::kEpiFp8 : (swizzled ? anq::kEpiNvfp4Swz : anq::kEpiNvfp4);
-  return launch_status(anq::launch_quant(dtype, epi, p,
-                                         static_cast<hipStream_t>(stream)));
+  anq::QuantTiling t;
+  const int st = anq::pick_quant_tiling(epi, p, &t);
+  if (st != ANQ_OK) return st;
+  return launch_status(anq::launch_quant(dtype, epi, p, t, stream));
 }
 
 }  // namespace
 
 extern "C" int quant_fp8(const void* in, const float* scale, int64_t tokens, int64_t hidden,
-                         int dtype, uint8_t* q, void* stream) {
+                         anq_dtype dtype, uint8_t* q, void* stream) {
   return quant_common(in, scale, tokens, hidden, dtype, q, nullptr, false, false, stream);
 }
 
 extern "C" int quant_nvfp4(const void* in, const float* global_scale, int64_t tokens,
-                           int64_t hidden, int dtype, uint8_t* q, uint8_t* sf, void* stream) {
+                           int64_t hidden, anq_dtype dtype, uint8_t* q, uint8_t* sf, void* stream) {
   return quant_common(in, global_scale, tokens, hidden, dtype, q, sf, true, false, stream);
 }
 
 extern "C" int quant_nvfp4_swizzled(const void* in, const float* global_scale, int64_t tokens,
-                                    int64_t hidden, int dtype, uint8_t* q, uint8_t* sf,
+                                    int64_t hidden, anq_dtype dtype, uint8_t* q, uint8_t* sf,
                                     void* stream) {
   return quant_common(in, global_scale, tokens, hidden, dtype, q, sf, true, true, stream);
 }
@@ -425,6 +444,22 @@ extern "C" int anq_nvfp4_swizzled_sf_shape(int64_t tokens, int64_t hidden, int64
   return ANQ_OK;
 }
 
+extern "C" int anq_stream_rw(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                             int nontemporal, void* stream) {
+  if ((read_bytes != 0 && !src) || (write_bytes != 0 && !dst)) return ANQ_ERR_NULL;
+  if (read_bytes < 0 || write_bytes < 0 || read_bytes % 16 != 0 || write_bytes % 16 != 0 ||
+      (read_bytes > 0 && write_bytes == 0) || (write_bytes / 16 + 255) / 256 > 0x7FFFFFFF)
+    return ANQ_ERR_SHAPE;
+  if (nontemporal != 0 && nontemporal != 1) return ANQ_ERR_VALUE;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return ANQ_ERR_ALIGN;
+  const Span outs[1] = {span(dst, write_bytes)};
+  const Span ins[1] = {span(src, read_bytes)};
+  if (any_alias(outs, 1, ins, 1)) return ANQ_ERR_ALIAS;
+  if (write_bytes == 0) return ANQ_OK;
+  return launch_status(anq::launch_stream(src, read_bytes, dst, write_bytes, nontemporal == 1,
+                                          stream));
+}
+
 extern "C" const char* anq_status_string(int status) {
   switch (status) {
     case ANQ_OK: return "ok";
@@ -436,6 +471,7 @@ extern "C" const char* anq_status_string(int status) {
     case ANQ_ERR_UNSUPPORTED: return "unsupported case (hidden > 65536, head_dim not in {32..512}, rotary_dim != head_dim): use a separated path";
     case ANQ_ERR_LAUNCH: return "HIP kernel launch failed";
     case ANQ_ERR_VALUE: return "bad scalar argument (eps < 0 or not finite, max_pos < 1, negative head count or num_slots)";
+    case ANQ_ERR_CONFIG: return "an ANQ_* tuning variable in the environment names a tiling the library has no kernel for";
     default: return "unknown status";
   }
 }

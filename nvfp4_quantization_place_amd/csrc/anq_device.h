@@ -12,10 +12,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace anq {
+#include "anq_internal.h"
 
-constexpr int kF16 = 0;
-constexpr int kBF16 = 1;
+namespace anq {
 
 // 8 activations = 16 bytes, the unit of every global load and store.
 struct alignas(16) U4 {

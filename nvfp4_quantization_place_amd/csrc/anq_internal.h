@@ -1,10 +1,19 @@
-// Launch interface between the C-ABI front end (anq_api.hip) and the kernels.
+// Interface between the C-ABI front end (anq_api.cpp, host C++), the tiling
+// choice (anq_tiling.cpp, host C++) and the kernels' launchers (the .hip files).
+//
+// Nothing here needs the HIP headers: streams travel as void* (a hipStream_t)
+// and launch results as int (0 for hipSuccess, else the HIP error code), so the
+// front end and the tiling compile as plain host C++. That is also how they are
+// built with the host sanitizers, against stand-in launchers that record what
+// would have been launched.
 #pragma once
 
-#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace anq {
+
+constexpr int kF16 = 0;
+constexpr int kBF16 = 1;
 
 // kEpiNvfp4Swz: NVFP4 with the block scales in the 128x4-tiled GEMM layout
 // (its own instantiation, so the linear-layout kernel carries none of its code).
@@ -36,7 +45,7 @@ struct TailParams {
 };
 
 // How a row is spread over lanes: `group` lanes of one wavefront per row
-// (16, 32 or 64; the workgroup holds 256 / group lane groups), or group == 0
+// (16, 32 or 64; the workgroup holds block / group lane groups), or group == 0
 // for one row at a time per workgroup of `block` lanes. Each lane owns vectors
 // lane + k*lanes, k < vec_per_lane. Each lane group walks `rows` consecutive
 // rows, loading the next while it finishes the current one.
@@ -49,11 +58,14 @@ struct Tiling {
   int64_t grid;
 };
 
-Tiling pick_tail_tiling(int32_t vec, int64_t tokens);
-Tiling pick_gate_lut_tiling(int32_t vec, int64_t rows);
+// The tiling of a call (anq_tiling.cpp): ANQ_OK, ANQ_ERR_SHAPE for a grid past
+// 2^31 - 1 workgroups, or ANQ_ERR_CONFIG when an ANQ_* tuning variable in the
+// environment names a tiling no kernel has.
+int pick_tail_tiling(int32_t vec, int64_t tokens, Tiling* t);
+int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* t);
 
-hipError_t launch_tail(int dtype, int epi, bool norm_out, const TailParams& p, const Tiling& t,
-                       hipStream_t stream);
+int launch_tail(int dtype, int epi, bool norm_out, const TailParams& p, const Tiling& t,
+                void* stream);
 
 struct QKParams {
   const void* qkv;
@@ -63,17 +75,30 @@ struct QKParams {
   const float* cos_sin;
   const float* scale;
   uint8_t* out;            // [tokens, heads*D]; with a KV store: Q codes [tokens, nq*D]
-  uint8_t* kv;             // KV store only: [num_slots, (nk+nv)*D] pool
+  uint8_t* kv;             // KV store only: the pool, num_slots rows
   const int64_t* slots;    // KV store only: [tokens] slot of each token (< 0: no store)
   int64_t num_slots;
   int64_t max_pos;
   float eps;
   int64_t tokens;
   int32_t nq, nk, nv, head_dim;
-  int32_t waves_per_token;  // set by the launcher
+  int32_t rotary_dim;       // rotated width at the end of each Q/K head (== head_dim: all of it)
+  int32_t waves_per_token;  // from the tiling
 };
 
-hipError_t launch_qk(int dtype, bool kv_store, const QKParams& p, hipStream_t stream);
+// Where the Q/K op's K and V codes go.
+enum QKStore { kStoreNone = 0, kStoreUniform = 1, kStoreMixed = 2 };
+
+struct QKTiling {
+  int waves_per_token;  // wavefronts sharing a token's head groups
+  int groups;           // the most head groups any wavefront takes (1..4)
+  int block;            // workgroup lanes
+  bool stream;
+  int64_t grid;
+};
+
+int pick_qk_tiling(const QKParams& p, QKTiling* t);
+int launch_qk(int dtype, int store, const QKParams& p, const QKTiling& t, void* stream);
 
 // Standalone quantisation of an activation tensor [tokens, hidden] (the second
 // kernel of the separated tail).
@@ -89,14 +114,24 @@ struct QuantParams {
   int64_t pad_rows;    // swizzled: padded rows past tokens (threads past vecs zero them)
 };
 
-hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t stream);
+struct QuantTiling {
+  bool stream;
+  int64_t grid;  // 256-thread workgroups, one thread per vector (and per padded scale word)
+};
+
+int pick_quant_tiling(int epi, const QuantParams& p, QuantTiling* t);
+int launch_quant(int dtype, int epi, const QuantParams& p, const QuantTiling& t, void* stream);
 
 // u = x * SiLU(z) for vecs * 8 elements (the gate of the gated RMSNorm).
-hipError_t launch_gate(int dtype, const void* x, const void* z, float* u, int64_t vecs,
-                       hipStream_t stream);
+int launch_gate(int dtype, const void* x, const void* z, float* u, int64_t vecs, void* stream);
 
 // Self-check of the device arithmetic: kSelfcheckCounts mismatch counts.
 constexpr int kSelfcheckCounts = 4;
-hipError_t launch_selfcheck(unsigned long long* counts, hipStream_t stream);
+int launch_selfcheck(unsigned long long* counts, void* stream);
+
+// A streaming kernel that reads read_bytes and writes write_bytes, 16 bytes per
+// lane access, in one pass: the practical ceiling of a given read/write mix.
+int launch_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                  bool nt, void* stream);
 
 }  // namespace anq

@@ -17,8 +17,6 @@
 // dense [tokens, nq*D] buffer, and the token's K and V codes go to its slot of
 // the pool, a row of (nk+nv)*D bytes; a slot outside [0, num_slots) stores
 // nothing.
-#include <stdlib.h>
-
 #include "anq_device.h"
 #include "anq_internal.h"
 
@@ -233,69 +231,35 @@ static const void* qk_fn(int lph) {
   }
 }
 
+// The tiling (wavefronts per token, head groups per wavefront, workgroup size,
+// streaming hints) comes from pick_qk_tiling.
 template <int DT, bool NT, bool STORE>
-static hipError_t launch_qk_nt(const QKParams& p, int groups, hipStream_t s) {
+static hipError_t launch_qk_nt(const QKParams& p, const QKTiling& t, hipStream_t s) {
   void* args[] = {const_cast<QKParams*>(&p)};
   const int lph = p.head_dim / 16;
-  const void* fn = groups == 4 ? qk_fn<DT, NT, STORE, 4>(lph)
-                 : groups == 3 ? qk_fn<DT, NT, STORE, 3>(lph)
-                 : groups == 2 ? qk_fn<DT, NT, STORE, 2>(lph)
-                               : qk_fn<DT, NT, STORE, 1>(lph);
-  if (!fn || groups < 1 || groups > 4) return hipErrorInvalidConfiguration;
-  int block = 256;  // four wavefronts
-  if (const char* e = getenv("ANQ_QK_BLOCK")) {
-    const int b = atoi(e);
-    if (b >= 64 && b <= 1024 && b % 64 == 0) block = b;
-  }
-  if (block < p.head_dim / 4) block = p.head_dim / 4;  // one gamma vector per thread (D <= 512)
-  const int64_t wpb = block / 64;
-  const int64_t grid = (p.tokens * p.waves_per_token + wpb - 1) / wpb;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(block), args, 0, s);
+  const void* fn = t.groups == 4 ? qk_fn<DT, NT, STORE, 4>(lph)
+                 : t.groups == 3 ? qk_fn<DT, NT, STORE, 3>(lph)
+                 : t.groups == 2 ? qk_fn<DT, NT, STORE, 2>(lph)
+                 : t.groups == 1 ? qk_fn<DT, NT, STORE, 1>(lph) : nullptr;
+  if (!fn || p.waves_per_token != t.waves_per_token || t.block < p.head_dim / 4)
+    return hipErrorInvalidConfiguration;
+  return hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3(t.block), args, 0, s);
 }
 
-// Streaming hints (see ld16s) on the qkv loads and code stores; ANQ_STREAM=0/1 overrides.
 template <int DT, bool STORE>
-static hipError_t launch_qk_dt(QKParams p, hipStream_t s) {
-  // Wavefronts per token W: one once the call has enough tokens to fill the
-  // GPU (~2048 wavefronts), more for fewer tokens; and at least enough that no
-  // wavefront takes more than 4 head groups, all of whose loads it issues at
-  // once. Measured on MI355X (graph of 200 calls, bf16, 4096 tokens): 16+8+8
-  // heads of 128 (4 groups) 11.0 us with one wavefront per token, 12.4 with
-  // the cap at 3 or 2 (two wavefronts); 64+8+8 heads (10 groups) 25.3, 25.0
-  // and 26.1 us with the cap at 4, 3 and 2. 256-lane workgroups: 512 lanes
-  // measured 11.4 us. ANQ_QK_WAVES, ANQ_QK_GROUPS (the cap, 1-4) and
-  // ANQ_QK_BLOCK override, for sweeps.
-  const int passes = (p.nq + p.nk + p.nv + 64 / (p.head_dim / 16) - 1) / (64 / (p.head_dim / 16));
-  const int64_t want = p.tokens > 0 ? (2048 + p.tokens - 1) / p.tokens : 1;
-  int W = (int)(want < passes ? want : passes);
-  if (const char* e = getenv("ANQ_QK_WAVES")) {
-    if (*e && atoi(e) > 0) W = atoi(e);
-  }
-  int cap = 4;
-  if (const char* e = getenv("ANQ_QK_GROUPS")) {
-    if (*e && atoi(e) >= 1 && atoi(e) <= 4) cap = atoi(e);
-  }
-  if (W < (passes + cap - 1) / cap) W = (passes + cap - 1) / cap;
-  if (W > passes) W = passes;
-  if (W < 1) W = 1;
-  p.waves_per_token = W;
-  const int groups = (passes + W - 1) / W;  // the most any wavefront takes (<= cap)
-  // streaming hints at every size: 16+8+8 heads of 128 (bf16) measured faster
-  // with them from 64 to 4096 tokens, with inputs from HBM (64: 3.48 -> 3.31 us,
-  // 2048: 9.31 -> 7.49) and with inputs in cache alike (2048: 6.97 -> 6.62)
-  bool stream = true;
-  if (const char* e = getenv("ANQ_STREAM")) {
-    if (*e) stream = atoi(e) != 0;
-  }
-  return stream ? launch_qk_nt<DT, true, STORE>(p, groups, s)
-                : launch_qk_nt<DT, false, STORE>(p, groups, s);
+static hipError_t launch_qk_dt(const QKParams& p, const QKTiling& t, hipStream_t s) {
+  return t.stream ? launch_qk_nt<DT, true, STORE>(p, t, s) : launch_qk_nt<DT, false, STORE>(p, t, s);
 }
 
-hipError_t launch_qk(int dtype, bool kv_store, const QKParams& p, hipStream_t s) {
-  if (kv_store)
-    return dtype == kBF16 ? launch_qk_dt<kBF16, true>(p, s) : launch_qk_dt<kF16, true>(p, s);
-  return dtype == kBF16 ? launch_qk_dt<kBF16, false>(p, s) : launch_qk_dt<kF16, false>(p, s);
+int launch_qk(int dtype, int store, const QKParams& p, const QKTiling& t, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.rotary_dim != p.head_dim || (store != kStoreNone && store != kStoreUniform))
+    return (int)hipErrorInvalidValue;
+  const bool kv = store == kStoreUniform;
+  hipError_t e;
+  if (kv) e = dtype == kBF16 ? launch_qk_dt<kBF16, true>(p, t, s) : launch_qk_dt<kF16, true>(p, t, s);
+  else e = dtype == kBF16 ? launch_qk_dt<kBF16, false>(p, t, s) : launch_qk_dt<kF16, false>(p, t, s);
+  return (int)e;
 }
 
 }  // namespace anq

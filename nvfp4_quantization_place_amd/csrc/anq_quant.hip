@@ -11,8 +11,6 @@
 // The encoders are the fused kernel's own (fp8_codes8, nvfp4_half_block).
 // With the swizzled scale layout (its own instantiation), threads past the
 // last vector zero the scale words of the padded rows (one 4-byte word each).
-#include <stdlib.h>
-
 #include "anq_device.h"
 #include "anq_internal.h"
 
@@ -66,34 +64,32 @@ __global__ void __launch_bounds__(256) quant_kernel(QuantParams p) {
   }
 }
 
+// The grid (one thread per vector, and per padded scale word with the swizzled
+// layout, in 256-thread workgroups) and the streaming hint come from
+// pick_quant_tiling.
 template <int DT, int EPI>
-static hipError_t launch_quant_epi(const QuantParams& p, hipStream_t s) {
+static hipError_t launch_quant_epi(const QuantParams& p, const QuantTiling& t, hipStream_t s) {
   void* args[] = {const_cast<QuantParams*>(&p)};
-  // streaming hint on the input once it is >= 32 MiB; ANQ_STREAM=0/1 overrides
-  bool stream = p.vecs * 16 >= ((int64_t)32 << 20);
-  if (const char* e = getenv("ANQ_STREAM")) {
-    if (*e) stream = atoi(e) != 0;
-  }
-  const void* fn = stream ? (const void*)&quant_kernel<DT, EPI, true>
-                          : (const void*)&quant_kernel<DT, EPI, false>;
-  const int64_t threads = p.vecs + (EPI == kEpiNvfp4Swz ? p.pad_rows * p.sf_tiles : 0);
-  const int64_t grid = (threads + 255) / 256;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s);
+  const void* fn = t.stream ? (const void*)&quant_kernel<DT, EPI, true>
+                            : (const void*)&quant_kernel<DT, EPI, false>;
+  return hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3(256), args, 0, s);
 }
 
 template <int DT>
-static hipError_t launch_quant_dt(int epi, const QuantParams& p, hipStream_t s) {
+static hipError_t launch_quant_dt(int epi, const QuantParams& p, const QuantTiling& t,
+                                  hipStream_t s) {
   switch (epi) {
-    case kEpiFp8: return launch_quant_epi<DT, kEpiFp8>(p, s);
-    case kEpiNvfp4: return launch_quant_epi<DT, kEpiNvfp4>(p, s);
-    case kEpiNvfp4Swz: return launch_quant_epi<DT, kEpiNvfp4Swz>(p, s);
+    case kEpiFp8: return launch_quant_epi<DT, kEpiFp8>(p, t, s);
+    case kEpiNvfp4: return launch_quant_epi<DT, kEpiNvfp4>(p, t, s);
+    case kEpiNvfp4Swz: return launch_quant_epi<DT, kEpiNvfp4Swz>(p, t, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_quant(int dtype, int epi, const QuantParams& p, hipStream_t s) {
-  return dtype == kBF16 ? launch_quant_dt<kBF16>(epi, p, s) : launch_quant_dt<kF16>(epi, p, s);
+int launch_quant(int dtype, int epi, const QuantParams& p, const QuantTiling& t, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return (int)(dtype == kBF16 ? launch_quant_dt<kBF16>(epi, p, t, s)
+                              : launch_quant_dt<kF16>(epi, p, t, s));
 }
 
 // u = x * SiLU(z) in binary32 (silu_gate), one thread per 8 elements: the gate
@@ -115,17 +111,16 @@ __global__ void __launch_bounds__(256) gate_kernel(const uint8_t* x, const uint8
   dst[1] = make_float4(o[4], o[5], o[6], o[7]);
 }
 
-hipError_t launch_gate(int dtype, const void* x, const void* z, float* u, int64_t vecs,
-                       hipStream_t s) {
-  const int64_t grid = (vecs + 255) / 256;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+int launch_gate(int dtype, const void* x, const void* z, float* u, int64_t vecs, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t grid = (vecs + 255) / 256;  // <= 2^31 - 1, checked by the front end
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   const uint8_t* zb = static_cast<const uint8_t*>(z);
   if (dtype == kBF16)
     hipLaunchKernelGGL(gate_kernel<kBF16>, dim3((unsigned)grid), dim3(256), 0, s, xb, zb, u, vecs);
   else
     hipLaunchKernelGGL(gate_kernel<kF16>, dim3((unsigned)grid), dim3(256), 0, s, xb, zb, u, vecs);
-  return hipGetLastError();
+  return (int)hipGetLastError();
 }
 
 }  // namespace anq

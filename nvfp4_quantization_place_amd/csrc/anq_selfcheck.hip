@@ -83,12 +83,13 @@ __global__ void __launch_bounds__(256) selfcheck_kernel(unsigned long long* coun
 
 }  // namespace
 
-hipError_t launch_selfcheck(unsigned long long* counts, hipStream_t s) {
+int launch_selfcheck(unsigned long long* counts, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(zero_counts, dim3(1), dim3(64), 0, s, counts);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess) return (int)err;
   hipLaunchKernelGGL(selfcheck_kernel, dim3(kSignificands / 256), dim3(256), 0, s, counts);
-  return hipGetLastError();
+  return (int)hipGetLastError();
 }
 
 }  // namespace anq

@@ -22,9 +22,6 @@
 //    again as a double-double, which settles the rounding of the exact sum.
 //  * NVFP4: a 16-element block is two adjacent vectors held by lanes 2j and
 //    2j+1; their amax meet through one lane swap.
-#include <stdio.h>
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "anq_device.h"
@@ -417,107 +414,14 @@ tail_kernel(TailParams p) {
 
 // ---------------------------------------------------------------- dispatch
 
-namespace {
-
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
-}
-
-}  // namespace
-
-// Tiling by row width (vec = hidden / 8 vectors of 16 bytes), one vector per
-// lane wherever a row fits in a workgroup:
-//   vec <= 16, 32, 64 : 16, 32, 64 lanes of a wavefront per row
-//   vec <= 1024       : a workgroup of vec lanes (rounded up to 64) per row
-//   larger            : a workgroup of up to 1024 lanes, 2, 4 or 8 vectors each
-// and rows per lane group chosen so that a small grid still fills the GPU.
-// ANQ_TAIL_TILING="G:K" (G in {0,16,32,64}), ANQ_ROWS_PER_GROUP and ANQ_STREAM
-// override the choice, for sweeps; every choice gives identical results.
-Tiling pick_tail_tiling(int32_t vec, int64_t tokens) {
-  Tiling t{};
-  if (vec <= 64) {
-    t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
-    t.vec_per_lane = 1;
-  } else {
-    t.group = 0;
-    t.vec_per_lane = vec <= 1024 ? 1 : (vec <= 2048 ? 2 : (vec <= 4096 ? 4 : 8));
-  }
-  if (const char* o = getenv("ANQ_TAIL_TILING")) {
-    int g = -1, k = -1;
-    if (sscanf(o, "%d:%d", &g, &k) == 2 && (g == 0 || g == 16 || g == 32 || g == 64) &&
-        (k == 1 || k == 2 || k == 4 || k == 8) && (g == 0 ? (vec + k - 1) / k <= 1024 : g * k >= vec) &&
-        (g == 0 || k <= 2)) {
-      t.group = g;
-      t.vec_per_lane = k;
-    }
-  }
-  int64_t groups_per_block;
-  if (t.group > 0) {
-    t.block = 256;
-    groups_per_block = 256 / t.group;
-  } else {
-    const int lanes = (vec + t.vec_per_lane - 1) / t.vec_per_lane;
-    t.block = (lanes + 63) / 64 * 64;
-    groups_per_block = 1;
-  }
-  // wide rows: two rows per workgroup once there are rows enough to spare, so
-  // the second row's loads overlap the first row's reduction and stores
-  t.rows = (t.group == 0 && t.block >= 512 && tokens >= 4096) ? 2 : 1;
-  const int env_rows = env_int("ANQ_ROWS_PER_GROUP", 0);
-  if (env_rows > 0) t.rows = env_rows;
-  // streaming hints from 1 MiB of x. With inputs coming from HBM they measured
-  // 10-15% faster from 1 to 32 MiB of x on MI355X (fp16 [256, 8192] NVFP4 5.25
-  // -> 4.65 us, [64, 8192] 4.08 -> 3.88) and 3% slower at 256 KiB; with inputs
-  // already in cache, 0-5% slower. ANQ_STREAM=0/1 overrides.
-  t.stream = (int64_t)vec * 16 * tokens >= ((int64_t)1 << 20);
-  const int env_stream = env_int("ANQ_STREAM", -1);
-  if (env_stream >= 0) t.stream = env_stream != 0;
-  const int64_t kMaxGrid = 0x7FFFFFFF;
-  while ((tokens + groups_per_block * t.rows - 1) / (groups_per_block * t.rows) > kMaxGrid) t.rows *= 2;
-  t.grid = (tokens + groups_per_block * t.rows - 1) / (groups_per_block * t.rows);
-  return t;
-}
-
-// Tiling of the gated variant with the gate table (rows <= 1024 elements):
-// lane groups of 16/32/64 lanes, one or two vectors per lane, in 512-lane
-// workgroups (one 32 KiB table per 8 wavefronts), each lane group walking
-// enough consecutive rows that about 512 workgroups cover the call, so each
-// workgroup copies its table once for many rows. On the gated workload
-// (bf16 [8192, 8192], groups of 1024) 512-lane workgroups with 16 rows per
-// group measured 66.8 us against 67.8 with 256 lanes (320 and 384 lanes:
-// 74-85). ANQ_GATE_BLOCK (a multiple of 64, at most 1024), ANQ_ROWS_PER_GROUP
-// and ANQ_STREAM override, for sweeps.
-Tiling pick_gate_lut_tiling(int32_t vec, int64_t rows) {
-  Tiling t{};
-  t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
-  t.vec_per_lane = vec <= 64 ? 1 : 2;
-  t.block = 512;
-  const int env_block = env_int("ANQ_GATE_BLOCK", 0);
-  if (env_block > 0 && env_block <= 1024 && env_block % 64 == 0) t.block = env_block;
-  const int64_t groups_per_block = t.block / t.group;
-  int64_t r = rows / (groups_per_block * 512);
-  t.rows = (int)(r < 1 ? 1 : (r > 64 ? 64 : r));
-  const int env_rows = env_int("ANQ_ROWS_PER_GROUP", 0);
-  if (env_rows > 0) t.rows = env_rows;
-  // streaming hints from 1 MiB of x, as in the tail tiling (bf16 groups of
-  // 1024, inputs from HBM: [2048, 1024] 6.33 -> 6.04 us, [2048, 8192] 25.6 ->
-  // 24.1, [1024, 8192] 16.4 -> 16.9)
-  t.stream = (int64_t)vec * 16 * rows >= ((int64_t)1 << 20);
-  const int env_stream = env_int("ANQ_STREAM", -1);
-  if (env_stream >= 0) t.stream = env_stream != 0;
-  const int64_t kMaxGrid = 0x7FFFFFFF;
-  while ((rows + groups_per_block * t.rows - 1) / (groups_per_block * t.rows) > kMaxGrid) t.rows *= 2;
-  t.grid = (rows + groups_per_block * t.rows - 1) / (groups_per_block * t.rows);
-  return t;
-}
-
 template <int DT, int EPI, bool NORM, bool NT>
 static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
   void* args[] = {const_cast<TailParams*>(&p)};
   const void* fn = nullptr;
-  if (t.group == 16) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 16, NT>;
-  else if (t.group == 32) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 32, NT>;
+  // (group, vectors per lane) pairs without a kernel leave fn null: an error,
+  // never a kernel that covers part of the row
+  if (t.group == 16 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 16, NT>;
+  else if (t.group == 32 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 32, NT>;
   else if (t.group == 64 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 64, NT>;
   else if (t.group == 64 && t.vec_per_lane == 2) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 64, NT>;
   else if (t.group == 0 && t.vec_per_lane == 1) fn = (const void*)&tail_kernel<DT, EPI, NORM, 1, 0, NT>;
@@ -561,11 +465,13 @@ static hipError_t launch1(int epi, bool norm, const TailParams& p, const Tiling&
   return epi == kEpiFp8 ? launch2<DT, kEpiFp8>(norm, p, t, s) : launch2<DT, kEpiNvfp4>(norm, p, t, s);
 }
 
-hipError_t launch_tail(int dtype, int epi, bool norm, const TailParams& p_in, const Tiling& t,
-                       hipStream_t s) {
+int launch_tail(int dtype, int epi, bool norm, const TailParams& p_in, const Tiling& t,
+                void* stream) {
   TailParams p = p_in;
   p.inv_w = 1.0f / (float)p.hidden;  // IEEE binary32 division on the host
-  return dtype == kBF16 ? launch1<kBF16>(epi, norm, p, t, s) : launch1<kF16>(epi, norm, p, t, s);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return (int)(dtype == kBF16 ? launch1<kBF16>(epi, norm, p, t, s)
+                              : launch1<kF16>(epi, norm, p, t, s));
 }
 
 }  // namespace anq

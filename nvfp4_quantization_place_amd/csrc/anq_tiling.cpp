@@ -1,0 +1,194 @@
+// Tiling choice of every launch: plain host C++, so that the front end and
+// its choices can be built and checked on a machine without a GPU.
+//
+// Each pick_* returns ANQ_OK, ANQ_ERR_SHAPE (a grid past 2^31 - 1 workgroups)
+// or ANQ_ERR_CONFIG. The ANQ_* environment variables below override a choice,
+// for sweeps and A/B runs. An override is either taken exactly or refused: a
+// value that is not a complete integer in range, or that names a tiling no
+// kernel has, makes the call fail with ANQ_ERR_CONFIG before anything is
+// enqueued (never a silent fallback to the default, and never a kernel that
+// covers only part of a row). Every accepted choice gives identical results.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/addnormq.h"
+#include "anq_internal.h"
+
+namespace anq {
+
+namespace {
+
+// An integer tuning variable: unset or empty leaves *v as it is; a complete
+// decimal integer in [lo, hi] is stored in *v; anything else is refused.
+bool env_int(const char* name, int lo, int hi, int* v) {
+  const char* s = getenv(name);
+  if (!s || !*s) return true;
+  char* end = nullptr;
+  const long x = strtol(s, &end, 10);
+  if (*end != '\0' || x < lo || x > hi) return false;
+  *v = (int)x;
+  return true;
+}
+
+// ANQ_STREAM: "0" or "1" when set.
+bool env_stream(bool* stream) {
+  int v = *stream ? 1 : 0;
+  if (!env_int("ANQ_STREAM", 0, 1, &v)) return false;
+  *stream = v == 1;
+  return true;
+}
+
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
+// The tail kernels that exist: (group, vectors per lane) =
+// (16, 1), (32, 1), (64, 1), (64, 2), and (0, 1 / 2 / 4 / 8) with at most
+// 1024 lanes per workgroup; a lane group must cover the row.
+bool tail_kernel_exists(int g, int k, int32_t vec) {
+  if (g == 0) return (k == 1 || k == 2 || k == 4 || k == 8) && (vec + k - 1) / k <= 1024;
+  if (g == 16 || g == 32) return k == 1 && g >= vec;
+  if (g == 64) return (k == 1 || k == 2) && g * k >= vec;
+  return false;
+}
+
+bool finish_grid(int64_t rows, int64_t groups_per_block, Tiling* t) {
+  while ((rows + groups_per_block * t->rows - 1) / (groups_per_block * t->rows) > kMaxGrid)
+    t->rows *= 2;
+  t->grid = (rows + groups_per_block * t->rows - 1) / (groups_per_block * t->rows);
+  return true;
+}
+
+}  // namespace
+
+// Tiling by row width (vec = hidden / 8 vectors of 16 bytes), one vector per
+// lane wherever a row fits in a workgroup:
+//   vec <= 16, 32, 64 : 16, 32, 64 lanes of a wavefront per row
+//   vec <= 1024       : a workgroup of vec lanes (rounded up to 64) per row
+//   larger            : a workgroup of up to 1024 lanes, 2, 4 or 8 vectors each
+// and rows per lane group chosen so that a small grid still fills the GPU.
+// ANQ_TAIL_TILING="G:K" (G lanes per row, 0 = a workgroup; K vectors per lane),
+// ANQ_ROWS_PER_GROUP (>= 1) and ANQ_STREAM (0 / 1) override the choice.
+int pick_tail_tiling(int32_t vec, int64_t tokens, Tiling* out) {
+  Tiling t{};
+  if (vec <= 64) {
+    t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
+    t.vec_per_lane = 1;
+  } else {
+    t.group = 0;
+    t.vec_per_lane = vec <= 1024 ? 1 : (vec <= 2048 ? 2 : (vec <= 4096 ? 4 : 8));
+  }
+  if (const char* o = getenv("ANQ_TAIL_TILING")) {
+    if (*o) {
+      int g = -1, k = -1, n = 0;
+      if (sscanf(o, "%d:%d%n", &g, &k, &n) != 2 || o[n] != '\0' || !tail_kernel_exists(g, k, vec))
+        return ANQ_ERR_CONFIG;
+      t.group = g;
+      t.vec_per_lane = k;
+    }
+  }
+  int64_t groups_per_block;
+  if (t.group > 0) {
+    t.block = 256;
+    groups_per_block = 256 / t.group;
+  } else {
+    const int lanes = (vec + t.vec_per_lane - 1) / t.vec_per_lane;
+    t.block = (lanes + 63) / 64 * 64;
+    groups_per_block = 1;
+  }
+  // wide rows: two rows per workgroup once there are rows enough to spare, so
+  // the second row's loads overlap the first row's reduction and stores
+  t.rows = (t.group == 0 && t.block >= 512 && tokens >= 4096) ? 2 : 1;
+  if (!env_int("ANQ_ROWS_PER_GROUP", 1, 1 << 20, &t.rows)) return ANQ_ERR_CONFIG;
+  // streaming hints from 1 MiB of x. With inputs coming from HBM they measured
+  // 10-15% faster from 1 to 32 MiB of x on MI355X (fp16 [256, 8192] NVFP4 5.25
+  // -> 4.65 us, [64, 8192] 4.08 -> 3.88) and 3% slower at 256 KiB; with inputs
+  // already in cache, 0-5% slower.
+  t.stream = (int64_t)vec * 16 * tokens >= ((int64_t)1 << 20);
+  if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
+  finish_grid(tokens, groups_per_block, &t);
+  *out = t;
+  return ANQ_OK;
+}
+
+// Tiling of the gated variant with the gate table (rows <= 1024 elements):
+// lane groups of 16/32/64 lanes, one or two vectors per lane, in 512-lane
+// workgroups (one 32 KiB table per 8 wavefronts), each lane group walking
+// enough consecutive rows that about 512 workgroups cover the call, so each
+// workgroup copies its table once for many rows. On the gated workload
+// (bf16 [8192, 8192], groups of 1024) 512-lane workgroups with 16 rows per
+// group measured 66.8 us against 67.8 with 256 lanes (320 and 384 lanes:
+// 74-85). ANQ_GATE_BLOCK (a multiple of 64, 64 to 1024), ANQ_ROWS_PER_GROUP
+// and ANQ_STREAM override.
+int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* out) {
+  Tiling t{};
+  t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
+  t.vec_per_lane = vec <= 64 ? 1 : 2;
+  t.block = 512;
+  if (!env_int("ANQ_GATE_BLOCK", 64, 1024, &t.block) || t.block % 64 != 0) return ANQ_ERR_CONFIG;
+  const int64_t groups_per_block = t.block / t.group;
+  int64_t r = rows / (groups_per_block * 512);
+  t.rows = (int)(r < 1 ? 1 : (r > 64 ? 64 : r));
+  if (!env_int("ANQ_ROWS_PER_GROUP", 1, 1 << 20, &t.rows)) return ANQ_ERR_CONFIG;
+  // streaming hints from 1 MiB of x, as in the tail tiling (bf16 groups of
+  // 1024, inputs from HBM: [2048, 1024] 6.33 -> 6.04 us, [2048, 8192] 25.6 ->
+  // 24.1, [1024, 8192] 16.4 -> 16.9)
+  t.stream = (int64_t)vec * 16 * rows >= ((int64_t)1 << 20);
+  if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
+  finish_grid(rows, groups_per_block, &t);
+  *out = t;
+  return ANQ_OK;
+}
+
+// Wavefronts per token W: one once the call has enough tokens to fill the GPU
+// (~2048 wavefronts), more for fewer tokens; and at least enough that no
+// wavefront takes more than 4 head groups, all of whose loads it issues at
+// once. Measured on MI355X (graph of 200 calls, bf16, 4096 tokens): 16+8+8
+// heads of 128 (4 groups) 11.0 us with one wavefront per token, 12.4 with the
+// cap at 3 or 2 (two wavefronts); 64+8+8 heads (10 groups) 25.3, 25.0 and 26.1
+// us with the cap at 4, 3 and 2. 256-lane workgroups: 512 lanes measured 11.4
+// us. Streaming hints at every size: 16+8+8 heads of 128 (bf16) measured
+// faster with them from 64 to 4096 tokens, with inputs from HBM (64: 3.48 ->
+// 3.31 us, 2048: 9.31 -> 7.49) and with inputs in cache alike (2048: 6.97 ->
+// 6.62). ANQ_QK_WAVES (>= 1), ANQ_QK_GROUPS (the cap, 1-4), ANQ_QK_BLOCK (a
+// multiple of 64, 64 to 1024) and ANQ_STREAM override.
+int pick_qk_tiling(const QKParams& p, QKTiling* out) {
+  QKTiling t{};
+  const int hpp = 64 / (p.head_dim / 16);  // heads per pass of a wavefront
+  const int passes = (p.nq + p.nk + p.nv + hpp - 1) / hpp;
+  const int64_t want = p.tokens > 0 ? (2048 + p.tokens - 1) / p.tokens : 1;
+  int W = (int)(want < passes ? want : passes);
+  int cap = 4, block = 256;
+  if (!env_int("ANQ_QK_WAVES", 1, 1 << 20, &W)) return ANQ_ERR_CONFIG;
+  if (!env_int("ANQ_QK_GROUPS", 1, 4, &cap)) return ANQ_ERR_CONFIG;
+  if (W < (passes + cap - 1) / cap) W = (passes + cap - 1) / cap;
+  if (W > passes) W = passes;
+  if (W < 1) W = 1;
+  t.waves_per_token = W;
+  t.groups = (passes + W - 1) / W;  // the most any wavefront takes (<= cap)
+  if (!env_int("ANQ_QK_BLOCK", 64, 1024, &block) || block % 64 != 0) return ANQ_ERR_CONFIG;
+  if (block < p.head_dim / 4) block = p.head_dim / 4;  // one gamma vector per thread (D <= 512)
+  t.block = block;
+  const int64_t wpb = block / 64;
+  t.grid = (p.tokens * W + wpb - 1) / wpb;
+  if (t.grid > kMaxGrid) return ANQ_ERR_SHAPE;
+  t.stream = true;
+  if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
+  *out = t;
+  return ANQ_OK;
+}
+
+// One thread per 16-byte vector (and, with the swizzled scales, one per padded
+// scale word), 256-thread workgroups; the streaming hint on the input once it
+// is >= 32 MiB (ANQ_STREAM overrides).
+int pick_quant_tiling(int epi, const QuantParams& p, QuantTiling* out) {
+  QuantTiling t{};
+  t.stream = p.vecs * 16 >= ((int64_t)32 << 20);
+  if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
+  const int64_t threads = p.vecs + (epi == kEpiNvfp4Swz ? p.pad_rows * p.sf_tiles : 0);
+  t.grid = (threads + 255) / 256;
+  if (t.grid > kMaxGrid) return ANQ_ERR_SHAPE;
+  *out = t;
+  return ANQ_OK;
+}
+
+}  // namespace anq

@@ -1,7 +1,11 @@
 """The C-ABI library on a machine without a GPU: it loads, exports every entry
 point that include/addnormq.h declares, and its host-side validation rejects
 bad arguments with the documented status before any HIP call (tokens == 0 is
-a no-op). No compute call is made here."""
+a no-op). No compute call is made here.
+
+With ANQ_HOSTCHECK_LIB set (tests/test_hostcheck.py does this), the same tests
+run against the host-only build of the front end under AddressSanitizer and
+UndefinedBehaviorSanitizer instead of the product library."""
 import ctypes
 import os
 import re
@@ -13,7 +17,8 @@ import nvfp4_quantization_place_amd as A
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "addnormq.h")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, LAUNCH, VALUE = range(9)
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, LAUNCH, VALUE, CONFIG = range(10)
+HOSTCHECK = os.environ.get("ANQ_HOSTCHECK_LIB")
 
 # fake, well-aligned, disjoint device addresses: validation never dereferences them
 BASE = 1 << 40
@@ -26,10 +31,16 @@ def addr(i, off=0):
 
 @pytest.fixture(scope="module")
 def L():
+    if HOSTCHECK:
+        saved = A._lib
+        A._lib = A.load(HOSTCHECK)
+        yield A._lib
+        A._lib = saved
+        return
     if not os.path.exists(A.LIB_PATH):
         from nvfp4_quantization_place_amd import build
         build.build()
-    return A.lib()
+    yield A.lib()
 
 
 def declared_functions():
@@ -46,7 +57,7 @@ def test_header_declares_the_entry_points():
                                            "quant_nvfp4_swizzled", "anq_nvfp4_swizzled_sf_shape",
                                            "gated_rmsnorm_quant_nvfp4", "silu_gate_f32",
                                            "anq_nvfp4_shape", "anq_selfcheck_arith",
-                                           "anq_status_string"])
+                                           "anq_status_string", "anq_stream_rw"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -54,14 +65,14 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
     # exported as plain C symbols (no C++ mangling)
     import subprocess
-    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True,
-                         text=True).stdout
+    out = subprocess.run(["nm", "-D", "--defined-only", HOSTCHECK or A.LIB_PATH],
+                         capture_output=True, text=True).stdout
     for name in declared_functions():
         assert re.search(rf"\bT {name}$", out, re.M), name
 
 
 def test_status_strings(L):
-    for code in range(9):
+    for code in range(10):
         s = A.status_string(code)
         assert s and s != "unknown status"
     assert A.status_string(99) == "unknown status"
@@ -148,6 +159,23 @@ def test_gated_validation(L):
     assert gate(addr(0), addr(1), 8, 1, addr(2, 4), None) == ALIGN
     assert gate(addr(0), addr(1), 8, 1, addr(1), None) == ALIAS
     assert g(tokens=4, sf=addr(4, 16)) == ALIAS              # scales over the codes
+
+
+def test_stream_validation(L):
+    """The calibration stream: sizes in 16-byte units, something to write,
+    aligned and disjoint buffers."""
+    s = L.anq_stream_rw
+    assert s(addr(0), 0, addr(1), 0, 1, None) == OK
+    assert s(None, 16, addr(1), 16, 1, None) == NULL
+    assert s(addr(0), 16, None, 16, 1, None) == NULL
+    assert s(None, 0, addr(1), 0, 1, None) == OK
+    assert s(addr(0), 24, addr(1), 16, 1, None) == SHAPE
+    assert s(addr(0), 16, addr(1), 8, 1, None) == SHAPE
+    assert s(addr(0), 32, addr(1), 0, 1, None) == SHAPE      # reads with nothing to write
+    assert s(addr(0), -16, addr(1), 16, 1, None) == SHAPE
+    assert s(addr(0), 16, addr(1), 16, 2, None) == VALUE
+    assert s(addr(0, 8), 16, addr(1), 16, 1, None) == ALIGN
+    assert s(addr(0), 64, addr(0, 32), 64, 1, None) == ALIAS
 
 
 def test_selfcheck_validation(L):

@@ -88,16 +88,18 @@ def test_gated_matches_oracle(tokens, hidden, group, dtype):
     np.testing.assert_array_equal(q, ref["q"])
 
 
-@pytest.mark.parametrize("tiling,rows,stream", [("16:1", "1", "0"), ("32:1", "2", "1"),
-                                                ("64:1", "3", "0"), ("0:1", "1", "1"),
-                                                ("0:2", "4", "0")])
-def test_gated_every_tiling(tiling, rows, stream, monkeypatch):
-    """Groups of 256 over rows of 1024: the per-group gamma slice, the lane
-    mapping and the streaming hints change no bit."""
+@pytest.mark.parametrize("group,tiling,rows,stream", [
+    (128, "16:1", "1", "0"), (256, "32:1", "2", "1"), (256, "64:1", "3", "0"),
+    (256, "64:2", "2", "1"), (256, "0:1", "1", "1"), (256, "0:2", "4", "0"),
+    (128, "32:1", "5", "1")])
+def test_gated_every_tiling(group, tiling, rows, stream, monkeypatch):
+    """Groups over rows of 1024: the per-group gamma slice, the lane mapping
+    and the streaming hints change no bit (each override names a tiling that
+    exists for the group width)."""
     monkeypatch.setenv("ANQ_TAIL_TILING", tiling)
     monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
     monkeypatch.setenv("ANQ_STREAM", stream)
-    inp = W.make_gated(61, "bf16", 23, 1024, 256)
+    inp = W.make_gated(61, "bf16", 23, 1024, group)
     G = 200.0
     q, sf = _run(inp, G)
     ref = _oracle(inp, G)

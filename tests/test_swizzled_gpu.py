@@ -31,8 +31,8 @@ def _poisoned_sf(tokens, hidden):
     return torch.full((r, c), 0xFF, dtype=torch.uint8, device="cuda")
 
 
-SHAPES = [(1, 16), (5, 48), (37, 1040), (128, 7168), (129, 1024), (300, 2048), (64, 8192),
-          (3, 16400), (2, 40976), (3, 65520)]
+SHAPES = [(1, 16), (5, 48), (7, 400), (9, 512), (37, 1040), (128, 7168), (129, 1024), (300, 2048),
+          (64, 8192), (3, 16400), (2, 40976), (3, 65520)]
 
 
 @pytest.mark.parametrize("tokens,hidden", SHAPES)
@@ -54,15 +54,20 @@ def test_fused_swizzled(tokens, hidden, dtype):
     np.testing.assert_array_equal(_np(sf), O.swizzle_block_scales(ref["sf"]))
 
 
-@pytest.mark.parametrize("tiling,rows", [("16:1", "1"), ("32:1", "3"), ("64:1", "2"),
-                                         ("0:1", "1"), ("0:2", "5"), ("0:4", "64")])
-def test_fused_swizzled_every_tiling(tiling, rows, monkeypatch):
-    """Padded rows are shared among however many lane groups the tiling launches."""
+@pytest.mark.parametrize("hidden,tiling,rows", [
+    (112, "16:1", "1"), (256, "32:1", "3"), (400, "64:1", "2"), (512, "64:1", "1"),
+    (1008, "64:2", "2"), (1040, "0:1", "1"), (1040, "0:2", "5"), (1040, "0:4", "64"),
+    (400, "0:1", "3")])
+def test_fused_swizzled_every_tiling(hidden, tiling, rows, monkeypatch):
+    """Padded rows are shared among however many lane groups the tiling
+    launches; every lane-group width gathers the four codes of a scale word.
+    Each override names a tiling that exists for its row width (others are
+    refused with ANQ_ERR_CONFIG, never replaced)."""
     monkeypatch.setenv("ANQ_TAIL_TILING", tiling)
     monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
-    inp = W.make_tail(77, "nvfp4", "bf16", 45, 1040, norm_out=False, scale=None)
+    inp = W.make_tail(77, "nvfp4", "bf16", 45, hidden, norm_out=False, scale=None)
     G = float(oracle_global_scale(inp))
-    sf = _poisoned_sf(45, 1040)
+    sf = _poisoned_sf(45, hidden)
     q, sf, _ = _A().add_rmsnorm_quant_nvfp4_swizzled(inp.x.cuda(), inp.residual.cuda(),
                                                      inp.gamma.cuda(),
                                                      torch.tensor([G], device="cuda"), inp.eps,
