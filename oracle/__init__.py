@@ -18,7 +18,8 @@ from .codecs import (E2M1_VALUES, E4M3_MAX, e2m1_decode, e2m1_encode, e4m3_decod
                      e4m3_encode, t_decode, t_encode)
 from .tail import (add_rmsnorm_quant_fp8, add_rmsnorm_quant_nvfp4, exact_sum_to_f32,
                    exp_neg_rn32, gated_rmsnorm_quant_nvfp4, silu_gate,
-                   normalize, nvfp4_global_scale, qk_norm_rope_fp8, qk_norm_rope_fp8_kv_store,
+                   mixed_kv_row_bytes, normalize, nvfp4_global_scale, qk_norm_rope_fp8,
+                   qk_norm_rope_fp8_kv_store, qk_norm_rope_kv_store_mixed,
                    quant_fp8, quant_nvfp4,
                    residual_add, rmsnorm_f32, rope_neox, row_scale, sum_of_squares,
                    swizzle_block_scales)
@@ -27,7 +28,7 @@ __all__ = [
     "E2M1_VALUES", "E4M3_MAX", "e2m1_decode", "e2m1_encode", "e4m3_decode", "e4m3_encode",
     "t_decode", "t_encode", "add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4",
     "exact_sum_to_f32", "normalize", "nvfp4_global_scale", "qk_norm_rope_fp8",
-    "qk_norm_rope_fp8_kv_store", "quant_fp8",
+    "qk_norm_rope_fp8_kv_store", "qk_norm_rope_kv_store_mixed", "mixed_kv_row_bytes", "quant_fp8",
     "quant_nvfp4", "residual_add", "rmsnorm_f32", "rope_neox", "row_scale", "sum_of_squares",
     "swizzle_block_scales", "exp_neg_rn32", "gated_rmsnorm_quant_nvfp4", "silu_gate",
 ]

@@ -27,8 +27,10 @@ the design notes of the repository):
     and 2j+1 in the high nibble; sf is stored row-major [tokens, hidden/16];
   * Q/K: each Q and K head of head_dim D is RMS-normalised over D with a
     shared gamma_q / gamma_k, rotated NeoX-style by the cos|sin row of its
-    token's position, divided by the scale and encoded E4M3; V heads are only
-    divided and encoded.
+    token's position (all of the head, or its last rotary_dim elements),
+    divided by the scale and encoded E4M3; V heads are only divided and
+    encoded. The KV stores scatter those results into a pool: uniform FP8
+    codes, or FP8 for the unrotated part and bf16 for the rotated part.
 """
 from __future__ import annotations
 
@@ -192,17 +194,27 @@ def rmsnorm_f32(x_bits, res_bits, gamma_bits, dtype: str, eps: float) -> np.ndar
 
 
 def qk_norm_rope_fp8(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin, scale: float,
-                     eps: float, nq: int, nk: int, nv: int, head_dim: int, dtype: str) -> dict:
+                     eps: float, nq: int, nk: int, nv: int, head_dim: int, dtype: str,
+                     rotary_dim: int | None = None) -> dict:
     """Q/K per-head RMSNorm + NeoX RoPE + uniform FP8 store of a fused QKV row.
 
     qkv [tokens, (nq+nk+nv)*D] holds Q heads, then K heads, then V heads; the
-    output has the same layout in E4M3 codes."""
+    output has the same layout in E4M3 codes.
+
+    rotary_dim R (default D): the RMSNorm covers all D elements of a Q/K head;
+    the rotation covers its last R elements only, as NeoX pairs
+    (D-R+k, D-R+k+R/2) for k < R/2 with the angle row cos_sin[pos] of width R
+    (cos in columns k < R/2, sin in columns R/2 + k). The first D-R elements
+    (the part without position encoding) keep their normed values. With
+    R = D this is the whole-head rotation."""
     D = head_dim
-    half = D // 2
+    R = D if rotary_dim is None else rotary_dim
+    N = D - R
+    half = R // 2
     tokens = qkv_bits.shape[0]
     heads = nq + nk + nv
     u = t_decode(qkv_bits, dtype).reshape(tokens, heads, D)
-    tab = np.asarray(cos_sin, dtype=F32)[np.asarray(positions, dtype=np.int64)]  # [tokens, D]
+    tab = np.asarray(cos_sin, dtype=F32)[np.asarray(positions, dtype=np.int64)]  # [tokens, R]
     cos, sin = tab[:, None, :half], tab[:, None, half:]
     out = np.empty((tokens, heads, D), dtype=np.uint8)
     o_all = np.empty((tokens, heads, D), dtype=F32)
@@ -213,7 +225,8 @@ def qk_norm_rope_fp8(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin, s
         ss = sum_of_squares(blk)
         r = row_scale(ss, D, eps)
         n = normalize(blk, r, t_decode(g, dtype)).reshape(tokens, hi - lo, D)
-        o = rope_neox(n, cos, sin)
+        o = n.copy()
+        o[..., N:] = rope_neox(n[..., N:], cos, sin)
         o_all[:, lo:hi] = o
         out[:, lo:hi] = e4m3_encode(o / F32(scale))
     if nv:
@@ -223,9 +236,22 @@ def qk_norm_rope_fp8(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin, s
     return dict(out=out.reshape(tokens, heads * D), o=o_all.reshape(tokens, heads * D))
 
 
+def _scatter_rows(kv_cache, slot_mapping, rows) -> np.ndarray:
+    """A copy of the pool with row slot_mapping[t] replaced by rows[t]; a slot
+    outside [0, num_slots) stores nothing, and rows no token names keep
+    their contents."""
+    kv = np.array(kv_cache, dtype=np.uint8, copy=True)
+    num_slots = kv.shape[0]
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if 0 <= slot < num_slots:
+            kv[slot] = rows[t]
+    return kv
+
+
 def qk_norm_rope_fp8_kv_store(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin,
                               scale: float, eps: float, nq: int, nk: int, nv: int, head_dim: int,
-                              dtype: str, slot_mapping, kv_cache) -> dict:
+                              dtype: str, slot_mapping, kv_cache,
+                              rotary_dim: int | None = None) -> dict:
     """The Q/K op with the KV-cache store as its epilogue (SGLang PR #32975:
     norm + RoPE + store into a uniform FP8 pool).
 
@@ -235,13 +261,51 @@ def qk_norm_rope_fp8_kv_store(qkv_bits, gamma_q_bits, gamma_k_bits, positions, c
     stores nothing, and rows no token names keep their contents."""
     D = head_dim
     codes = qk_norm_rope_fp8(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin, scale, eps,
-                             nq, nk, nv, D, dtype)["out"]
-    kv = np.array(kv_cache, dtype=np.uint8, copy=True)
-    num_slots = kv.shape[0]
-    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
-        if 0 <= slot < num_slots:
-            kv[slot] = codes[t, nq * D:]
-    return dict(q=codes[:, :nq * D].copy(), kv=kv)
+                             nq, nk, nv, D, dtype, rotary_dim)["out"]
+    return dict(q=codes[:, :nq * D].copy(), kv=_scatter_rows(kv_cache, slot_mapping, codes[:, nq * D:]))
+
+
+def mixed_kv_row_bytes(nk: int, nv: int, head_dim: int, rotary_dim: int) -> int:
+    """Bytes of one token's row of the mixed pool: per K head D-R FP8 codes and
+    R bf16 values, per V head D FP8 codes."""
+    return nk * (head_dim - rotary_dim + 2 * rotary_dim) + nv * head_dim
+
+
+def qk_norm_rope_kv_store_mixed(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin,
+                                scale: float, eps: float, nq: int, nk: int, nv: int,
+                                head_dim: int, rotary_dim: int, dtype: str, slot_mapping,
+                                kv_cache) -> dict:
+    """The Q/K op storing K into a mixed pool: the part of each K head without
+    position encoding as FP8, the rotated part as bf16 (the FP8-nope /
+    BF16-rope KV pool of the FlashMLA counterpart named in SGLang PR #32975's
+    discussion; the pages give no layout, so the reading is stated here).
+
+    The values are those of qk_norm_rope_fp8 with the same rotary_dim R: each
+    Q/K head is RMS-normalised over all D elements and its last R elements are
+    rotated. Q codes come back dense [tokens, nq*D] (E4M3 of o / s, as the
+    plain op's). Token t's pool row, written to row slot_mapping[t] of a copy
+    of kv_cache [num_slots, mixed_kv_row_bytes], holds for each K head j in
+    order: D-R bytes E4M3(fl32(o / s)) of its first D-R elements, then its
+    last R elements as bf16 RNE_bf16(o), two bytes each, little endian; then
+    for each V head D bytes E4M3(fl32(v / s)). Slots outside [0, num_slots)
+    store nothing; other rows keep their contents."""
+    D, R = head_dim, rotary_dim
+    N = D - R
+    r = qk_norm_rope_fp8(qkv_bits, gamma_q_bits, gamma_k_bits, positions, cos_sin, scale, eps,
+                         nq, nk, nv, D, dtype, R)
+    tokens = qkv_bits.shape[0]
+    heads = nq + nk + nv
+    codes = r["out"].reshape(tokens, heads, D)
+    o = r["o"].reshape(tokens, heads, D)
+    rows = np.empty((tokens, mixed_kv_row_bytes(nk, nv, D, R)), dtype=np.uint8)
+    for j in range(nk):
+        base = j * (N + 2 * R)
+        rows[:, base:base + N] = codes[:, nq + j, :N]
+        rope = t_encode(o[:, nq + j, N:], "bf16").astype("<u2")
+        rows[:, base + N:base + N + 2 * R] = rope.view(np.uint8).reshape(tokens, 2 * R)
+    rows[:, nk * (N + 2 * R):] = codes[:, nq + nk:, :].reshape(tokens, nv * D)
+    return dict(q=r["out"][:, :nq * D].copy(), kv=_scatter_rows(kv_cache, slot_mapping, rows),
+                o=r["o"])
 
 
 def swizzle_block_scales(sf: np.ndarray) -> np.ndarray:

@@ -94,15 +94,16 @@ def bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def rope_table(max_pos: int, head_dim: int, theta: float) -> np.ndarray:
-    """cos | sin table [max_pos, head_dim] float32, NeoX frequencies
-    theta**(-2k/head_dim) for k < head_dim/2, evaluated in float64 and rounded
-    once. It is an input of the Q/K kernel, identical on both sides."""
-    half = head_dim // 2
+def rope_table(max_pos: int, width: int, theta: float) -> np.ndarray:
+    """cos | sin table [max_pos, width] float32 of a NeoX rotation over `width`
+    elements (the head, or its rotated part): frequencies theta**(-2k/width)
+    for k < width/2, evaluated in float64 and rounded once. It is an input of
+    the Q/K kernel, identical on both sides."""
+    half = width // 2
     k = np.arange(half, dtype=np.float64)
-    inv = theta ** (-2.0 * k / head_dim)
+    inv = theta ** (-2.0 * k / width)
     ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
-    tab = np.empty((max_pos, head_dim), dtype=np.float64)
+    tab = np.empty((max_pos, width), dtype=np.float64)
     tab[:, :half] = np.cos(ang)
     tab[:, half:] = np.sin(ang)
     return tab.astype(np.float32)
@@ -138,9 +139,10 @@ class QKInputs:
     gamma_q: torch.Tensor
     gamma_k: torch.Tensor
     positions: torch.Tensor  # int64 [tokens]
-    cos_sin: np.ndarray      # float32 [max_pos, head_dim]
+    cos_sin: np.ndarray      # float32 [max_pos, rotary_dim]
     eps: float
     scale: float
+    rotary_dim: int = 0      # rotated width at the end of each Q/K head (0: the whole head)
 
 
 # The workloads. "sizes" are the shapes the pages name or that are fixed here.
@@ -204,7 +206,9 @@ def make_tail(seed: int, op: str, dtype: str, tokens: int, hidden: int, *,
 def make_qk(seed: int, dtype: str, tokens: int, nq: int, nk: int, nv: int, head_dim: int, *,
             theta: float = 1e6, eps: float = 1e-6, scale: float = 0.05,
             max_pos: int | None = None, positions: np.ndarray | None = None,
-            name: str = "custom") -> QKInputs:
+            rotary_dim: int | None = None, name: str = "custom") -> QKInputs:
+    """Inputs of one Q/K call. rotary_dim R (default head_dim): the cos|sin
+    table is [max_pos, R], with the NeoX frequencies of an R-wide rotation."""
     cols = (nq + nk + nv) * head_dim
     qkv = to_dtype(normal(seed, TID_QKV, tokens * cols), dtype).reshape(tokens, cols)
     gq = to_dtype(1.0 + 0.1 * normal(seed, TID_GAMMA, head_dim), dtype)
@@ -213,10 +217,11 @@ def make_qk(seed: int, dtype: str, tokens: int, nq: int, nk: int, nv: int, head_
         positions = np.arange(tokens, dtype=np.int64)
     if max_pos is None:
         max_pos = max(int(positions.max()) + 1 if tokens else 1, 1)
+    R = head_dim if rotary_dim is None else rotary_dim
     return QKInputs(name=name, dtype=dtype, tokens=tokens, nq=nq, nk=nk, nv=nv,
                     head_dim=head_dim, qkv=qkv, gamma_q=gq, gamma_k=gk,
                     positions=torch.from_numpy(np.ascontiguousarray(positions, dtype=np.int64)),
-                    cos_sin=rope_table(max_pos, head_dim, theta), eps=eps, scale=scale)
+                    cos_sin=rope_table(max_pos, R, theta), eps=eps, scale=scale, rotary_dim=R)
 
 
 def make_gated(seed: int, dtype: str, tokens: int, hidden: int, group: int, *,
