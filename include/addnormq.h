@@ -7,7 +7,8 @@
  *   q        <- FP8 E4M3 (per-tensor scale) or NVFP4 (E2M1 + per-16 E4M3 scales)
  *   norm_out <- n rounded to the activation type   (optional)
  *
- * and of the Q/K per-head RMSNorm + NeoX RoPE + uniform FP8 store.
+ * and of the Q/K per-head RMSNorm + NeoX RoPE + FP8 store (into dense codes, a
+ * uniform FP8 KV pool, or a pool with FP8 unrotated and bf16 rotated parts).
  *
  * Sources of the operations (the pages these ops are built from):
  *  - TensorRT-LLM issue #17900, "[Performance]: Fuse local NVFP4 tail after
@@ -50,8 +51,8 @@
  *                           in bits 0-3 and element 2j+1 in bits 4-7
  *   NVFP4 sf              : [tokens, hidden/16] bytes, E4M3 code of block b at column b
  *   qkv, out (Q/K op)     : [tokens, (nq+nk+nv)*head_dim]: Q heads, then K, then V
- *   cos_sin               : [max_pos, head_dim] binary32; columns k < head_dim/2 hold
- *                           cos(angle_k), columns head_dim/2 + k hold sin(angle_k)
+ *   cos_sin               : [max_pos, rotary_dim] binary32; columns k < rotary_dim/2
+ *                           hold cos(angle_k), columns rotary_dim/2 + k sin(angle_k)
  *
  * Conventions shared by every entry point:
  *  - Pointers are device pointers unless stated; the caller owns every buffer.
@@ -114,7 +115,7 @@ enum {
   ANQ_ERR_DTYPE = 3,       /* dtype is not ANQ_F16 / ANQ_BF16 */
   ANQ_ERR_ALIGN = 4,       /* a pointer breaks the alignment rule above */
   ANQ_ERR_ALIAS = 5,       /* buffers overlap where they must not */
-  ANQ_ERR_UNSUPPORTED = 6, /* hidden > ANQ_MAX_HIDDEN, head_dim not supported, rotary_dim != head_dim */
+  ANQ_ERR_UNSUPPORTED = 6, /* hidden > ANQ_MAX_HIDDEN, head_dim or rotary_dim not supported */
   ANQ_ERR_LAUNCH = 7,      /* the HIP launch failed (message via anq_status_string) */
   ANQ_ERR_VALUE = 8,       /* eps negative or not finite, max_pos < 1, negative head counts or num_slots */
   ANQ_ERR_CONFIG = 9       /* an ANQ_* tuning variable in the environment names no kernel of the library */
@@ -157,22 +158,29 @@ int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
 
 /*
  * Q/K per-head RMSNorm + NeoX RoPE + uniform FP8 E4M3 store of a fused QKV
- * buffer (SGLang PR #32975; Q/K RMSNorm and RoPE of TensorRT-LLM PR #17288).
+ * buffer (SGLang PR #32975; Q/K RMSNorm and RoPE of TensorRT-LLM PR #17288,
+ * Description; its Test Coverage guards the RoPE width).
  *
- * For token t and each of its nq Q heads and nk K heads (head_dim D each):
- *   n = RMSNorm over D with gamma_q (Q) or gamma_k (K), binary32;
- *   o_k       = n_k * cos_k - n_{k+D/2} * sin_k,
- *   o_{k+D/2} = n_{k+D/2} * cos_k + n_k * sin_k   (k < D/2; each product and sum rounded),
- *   with cos_k = cos_sin[positions[t], k], sin_k = cos_sin[positions[t], D/2 + k];
+ * For token t and each of its nq Q heads and nk K heads (head_dim D each),
+ * with R = rotary_dim and N = D - R:
+ *   n = RMSNorm over all D elements with gamma_q (Q) or gamma_k (K), binary32;
+ *   the first N elements keep o = n; the last R rotate as NeoX pairs
+ *   (N + k, N + k + R/2), k < R/2, each product and sum rounded:
+ *     o_{N+k}     = n_{N+k} * cos_k - n_{N+k+R/2} * sin_k,
+ *     o_{N+k+R/2} = n_{N+k+R/2} * cos_k + n_{N+k} * sin_k,
+ *   with cos_k = cos_sin[positions[t], k], sin_k = cos_sin[positions[t], R/2 + k];
  *   out = E4M3(o / s).  V heads: out = E4M3(v / s).
+ * R = D rotates the whole head.
  *
  *   qkv        [tokens, (nq+nk+nv)*D] T, read only
  *   gamma_q,gamma_k [D] T
  *   positions  [tokens] int64 (device)
- *   cos_sin    [max_pos, D] binary32
+ *   cos_sin    [max_pos, R] binary32
  *   scale      device pointer to one binary32 s
- *   rotary_dim must equal head_dim (partial rotation is not fused: ANQ_ERR_UNSUPPORTED)
  *   head_dim   one of 32, 64, 128, 256, 512
+ *   rotary_dim a power of two from 16 to head_dim; other values (and other
+ *              head_dim) return ANQ_ERR_UNSUPPORTED, the "keep a separated
+ *              path" answer
  *   nq, nk, nv >= 0, at least one head and at most 2^20 in all (ANQ_ERR_VALUE
  *              for a negative count, ANQ_ERR_SHAPE otherwise)
  *   out        [tokens, (nq+nk+nv)*D] uint8 E4M3 codes (output)
@@ -180,8 +188,8 @@ int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
 int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
                      const int64_t* positions, const float* cos_sin, int64_t max_pos,
                      const float* scale, float eps, int64_t tokens, int32_t nq, int32_t nk,
-                     int32_t nv, int32_t head_dim, int32_t rotary_dim, anq_dtype dtype, uint8_t* out,
-                     void* stream);
+                     int32_t nv, int32_t head_dim, int32_t rotary_dim, anq_dtype dtype,
+                     uint8_t* out, void* stream);
 
 /*
  * The same op with the KV-cache store as its epilogue: the norm + RoPE + store
@@ -206,6 +214,30 @@ int qk_norm_rope_fp8_kv_store(const void* qkv, const void* gamma_q, const void* 
                               int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
                               anq_dtype dtype, const int64_t* slot_mapping, int64_t num_slots,
                               uint8_t* q_out, uint8_t* kv_cache, void* stream);
+
+/*
+ * The same op with the mixed KV pool as its epilogue: FP8 for the part of a
+ * K head that carries no position encoding, bf16 for the rotated part (the
+ * FP8-nope / BF16-rope pool of the FlashMLA counterpart that the SGLang PR
+ * #32975 discussion names). The pages give no layout; this is the one the
+ * library writes, with R = rotary_dim and N = head_dim - R:
+ *
+ *   q_out        [tokens, nq*D] uint8: the Q heads' E4M3 codes, as qk_norm_rope_fp8's
+ *   kv_cache     [num_slots, nk*(D+R) + nv*D] uint8, in/out. Row slot_mapping[t]
+ *                receives token t's K heads, each as N bytes E4M3(o_i / s) of its
+ *                first N elements followed by R bf16 values RNE_bf16(o_i) of its
+ *                last R (2 bytes each, little endian; bf16 whatever T is), then
+ *                its V heads, D bytes E4M3(v_i / s) each. Every other row keeps
+ *                its contents.
+ * The values o are those of qk_norm_rope_fp8 with the same rotary_dim; slots,
+ * NULL rules, alignment and races as for qk_norm_rope_fp8_kv_store.
+ */
+int qk_norm_rope_kv_store_mixed(const void* qkv, const void* gamma_q, const void* gamma_k,
+                                const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                const float* scale, float eps, int64_t tokens, int32_t nq,
+                                int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
+                                anq_dtype dtype, const int64_t* slot_mapping, int64_t num_slots,
+                                uint8_t* q_out, uint8_t* kv_cache, void* stream);
 
 /*
  * The separated local tail, kept as the measured baseline of the fused ops and

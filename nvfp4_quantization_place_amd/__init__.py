@@ -16,7 +16,8 @@ import os
 import torch  # loads the HIP runtime the library binds to
 
 __all__ = ["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4", "qk_norm_rope_fp8",
-           "qk_norm_rope_fp8_kv_store", "add_rmsnorm_quant_nvfp4_swizzled",
+           "qk_norm_rope_fp8_kv_store", "qk_norm_rope_kv_store_mixed", "mixed_kv_row_bytes",
+           "add_rmsnorm_quant_nvfp4_swizzled",
            "gated_rmsnorm_quant_nvfp4", "silu_gate_f32",
            "quant_nvfp4_swizzled", "nvfp4_swizzled_sf_shape", "add_rmsnorm", "quant_fp8", "quant_nvfp4",
            "nvfp4_shape", "status_string", "selfcheck_arith", "stream_rw", "lib", "AnqError",
@@ -40,6 +41,8 @@ _SIGS = {
                          ctypes.c_int, _P, _P],
     "qk_norm_rope_fp8_kv_store": [_P, _P, _P, _P, _P, _I64, _P, _F, _I64, _I32, _I32, _I32, _I32,
                                   _I32, ctypes.c_int, _P, _I64, _P, _P, _P],
+    "qk_norm_rope_kv_store_mixed": [_P, _P, _P, _P, _P, _I64, _P, _F, _I64, _I32, _I32, _I32,
+                                    _I32, _I32, ctypes.c_int, _P, _I64, _P, _P, _P],
     "add_rmsnorm": [_P, _P, _P, _F, _I64, _I64, ctypes.c_int, _P, _P],
     "quant_fp8": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P],
     "quant_nvfp4": [_P, _P, _I64, _I64, ctypes.c_int, _P, _P, _P],
@@ -244,43 +247,75 @@ def add_rmsnorm_quant_nvfp4(x, residual, gamma, global_scale, eps: float, norm_o
     return q, sf, norm
 
 
-def _qk_inputs(qkv, gamma_q, gamma_k, positions, cos_sin, nq, nk, head_dim, tokens):
+def _qk_inputs(qkv, gamma_q, gamma_k, positions, cos_sin, nq, nk, head_dim, rotary_dim, tokens):
     """gamma_q / gamma_k [head_dim] in the dtype of qkv where there are Q / K
-    heads, one position per token, and a [max_pos, head_dim] cos|sin table."""
+    heads, one position per token, and a [max_pos, rotary_dim] cos|sin table."""
     if nq > 0:
         _need(gamma_q, head_dim, qkv.dtype, "gamma_q")
     if nk > 0:
         _need(gamma_k, head_dim, qkv.dtype, "gamma_k")
     _need(positions, tokens, torch.int64, "positions")
-    if cos_sin.dim() != 2 or cos_sin.shape[1] != head_dim:
-        raise ValueError(f"cos_sin must be [max_pos, head_dim={head_dim}] float32")
+    if positions.dtype != torch.int64 or cos_sin.dtype != torch.float32:
+        raise ValueError("positions must be int64 and cos_sin float32")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != rotary_dim:
+        raise ValueError(f"cos_sin must be [max_pos, rotary_dim={rotary_dim}] float32")
+
+
+def _qk_tokens(qkv, nq, nk, nv, head_dim) -> int:
+    cols = (nq + nk + nv) * head_dim
+    if qkv.shape[-1] != cols:
+        raise ValueError(f"qkv last dim {qkv.shape[-1]} != (nq+nk+nv)*head_dim = {cols}")
+    return qkv.numel() // cols if cols else 0
 
 
 def qk_norm_rope_fp8(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: float, nq: int,
                      nk: int, nv: int, head_dim: int, rotary_dim: int | None = None, out=None,
                      stream=None):
-    """Q/K per-head RMSNorm + NeoX RoPE + FP8 E4M3 of o / scale; V heads E4M3 of v / scale.
-    Returns out (uint8, the shape of qkv)."""
+    """Q/K per-head RMSNorm + NeoX RoPE (of the last rotary_dim elements of
+    each Q/K head; default all of it) + FP8 E4M3 of o / scale; V heads E4M3 of
+    v / scale. cos_sin is [max_pos, rotary_dim]. Returns out (uint8, the shape of qkv)."""
     dev = _check_gpu(qkv, gamma_q, gamma_k, positions, cos_sin, scale, out)
     _scalar(scale, "scale")
-    if positions.dtype != torch.int64 or cos_sin.dtype != torch.float32:
-        raise ValueError("positions must be int64 and cos_sin float32")
-    cols = (nq + nk + nv) * head_dim
-    if qkv.shape[-1] != cols:
-        raise ValueError(f"qkv last dim {qkv.shape[-1]} != (nq+nk+nv)*head_dim = {cols}")
-    tokens = qkv.numel() // cols if cols else 0
-    _qk_inputs(qkv, gamma_q, gamma_k, positions, cos_sin, nq, nk, head_dim, tokens)
+    rot = head_dim if rotary_dim is None else rotary_dim
+    tokens = _qk_tokens(qkv, nq, nk, nv, head_dim)
+    _qk_inputs(qkv, gamma_q, gamma_k, positions, cos_sin, nq, nk, head_dim, rot, tokens)
     _need(out, qkv.numel(), torch.uint8, "out")
     if out is None:
         out = torch.empty(qkv.shape, dtype=torch.uint8, device=dev)
-    max_pos = cos_sin.shape[0]
     st = lib().qk_norm_rope_fp8(_ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), _ptr(positions),
-                                _ptr(cos_sin), max_pos, _ptr(scale), eps, tokens, nq, nk, nv,
-                                head_dim, head_dim if rotary_dim is None else rotary_dim,
-                                _dtype_code(qkv), _ptr(out), _stream(dev, stream))
+                                _ptr(cos_sin), cos_sin.shape[0], _ptr(scale), eps, tokens, nq, nk,
+                                nv, head_dim, rot, _dtype_code(qkv), _ptr(out),
+                                _stream(dev, stream))
     if st:
         raise AnqError("qk_norm_rope_fp8", st)
     return out
+
+
+def _qk_store(fn_name, kv_cols, qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps, nq, nk,
+              nv, head_dim, rot, slot_mapping, kv_cache, q_out, stream):
+    dev = _check_gpu(qkv, gamma_q, gamma_k, positions, cos_sin, scale, slot_mapping, kv_cache,
+                     q_out)
+    _scalar(scale, "scale")
+    if slot_mapping.dtype != torch.int64 or kv_cache.dtype != torch.uint8:
+        raise ValueError("slot_mapping must be int64 and kv_cache uint8")
+    tokens = _qk_tokens(qkv, nq, nk, nv, head_dim)
+    if kv_cache.dim() < 1 or (kv_cols and kv_cache.numel() % kv_cols):
+        raise ValueError(f"kv_cache must hold whole rows of {kv_cols} bytes")
+    num_slots = kv_cache.numel() // kv_cols if kv_cols else 0
+    if slot_mapping.numel() != tokens:
+        raise ValueError("slot_mapping must hold one slot per token")
+    _qk_inputs(qkv, gamma_q, gamma_k, positions, cos_sin, nq, nk, head_dim, rot, tokens)
+    _need(q_out, tokens * nq * head_dim, torch.uint8, "q_out")
+    if q_out is None:
+        q_out = torch.empty(*qkv.shape[:-1], nq * head_dim, dtype=torch.uint8, device=dev)
+    st = getattr(lib(), fn_name)(
+        _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), _ptr(positions), _ptr(cos_sin), cos_sin.shape[0],
+        _ptr(scale), eps, tokens, nq, nk, nv, head_dim, rot, _dtype_code(qkv), _ptr(slot_mapping),
+        num_slots, _ptr(q_out) if q_out.numel() else None,
+        _ptr(kv_cache) if kv_cache.numel() else None, _stream(dev, stream))
+    if st:
+        raise AnqError(fn_name, st)
+    return q_out
 
 
 def qk_norm_rope_fp8_kv_store(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: float,
@@ -290,36 +325,28 @@ def qk_norm_rope_fp8_kv_store(qkv, gamma_q, gamma_k, positions, cos_sin, scale, 
     [.., nq*head_dim]; token t's K and V codes to kv_cache[slot_mapping[t]]
     (a [num_slots, (nk+nv)*head_dim] uint8 pool, updated in place; slots
     outside [0, num_slots) store nothing). Returns q_out."""
-    dev = _check_gpu(qkv, gamma_q, gamma_k, positions, cos_sin, scale, slot_mapping, kv_cache,
-                     q_out)
-    _scalar(scale, "scale")
-    if positions.dtype != torch.int64 or cos_sin.dtype != torch.float32:
-        raise ValueError("positions must be int64 and cos_sin float32")
-    if slot_mapping.dtype != torch.int64 or kv_cache.dtype != torch.uint8:
-        raise ValueError("slot_mapping must be int64 and kv_cache uint8")
-    cols = (nq + nk + nv) * head_dim
-    if qkv.shape[-1] != cols:
-        raise ValueError(f"qkv last dim {qkv.shape[-1]} != (nq+nk+nv)*head_dim = {cols}")
-    kv_cols = (nk + nv) * head_dim
-    if kv_cache.dim() < 1 or (kv_cols and kv_cache.numel() % kv_cols):
-        raise ValueError("kv_cache must hold whole rows of (nk+nv)*head_dim bytes")
-    num_slots = kv_cache.numel() // kv_cols if kv_cols else 0
-    tokens = qkv.numel() // cols if cols else 0
-    if slot_mapping.numel() != tokens:
-        raise ValueError("slot_mapping must hold one slot per token")
-    _qk_inputs(qkv, gamma_q, gamma_k, positions, cos_sin, nq, nk, head_dim, tokens)
-    _need(q_out, tokens * nq * head_dim, torch.uint8, "q_out")
-    if q_out is None:
-        q_out = torch.empty(*qkv.shape[:-1], nq * head_dim, dtype=torch.uint8, device=dev)
-    st = lib().qk_norm_rope_fp8_kv_store(
-        _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), _ptr(positions), _ptr(cos_sin), cos_sin.shape[0],
-        _ptr(scale), eps, tokens, nq, nk, nv, head_dim,
-        head_dim if rotary_dim is None else rotary_dim, _dtype_code(qkv), _ptr(slot_mapping),
-        num_slots, _ptr(q_out) if q_out.numel() else None, _ptr(kv_cache) if kv_cache.numel() else None,
-        _stream(dev, stream))
-    if st:
-        raise AnqError("qk_norm_rope_fp8_kv_store", st)
-    return q_out
+    rot = head_dim if rotary_dim is None else rotary_dim
+    return _qk_store("qk_norm_rope_fp8_kv_store", (nk + nv) * head_dim, qkv, gamma_q, gamma_k,
+                     positions, cos_sin, scale, eps, nq, nk, nv, head_dim, rot, slot_mapping,
+                     kv_cache, q_out, stream)
+
+
+def mixed_kv_row_bytes(nk: int, nv: int, head_dim: int, rotary_dim: int) -> int:
+    """Bytes of one row of the mixed KV pool: nk*(head_dim + rotary_dim) + nv*head_dim."""
+    return nk * (head_dim + rotary_dim) + nv * head_dim
+
+
+def qk_norm_rope_kv_store_mixed(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: float,
+                                nq: int, nk: int, nv: int, head_dim: int, rotary_dim: int,
+                                slot_mapping, kv_cache, q_out=None, stream=None):
+    """The Q/K op with the mixed KV pool: Q codes to q_out [.., nq*head_dim];
+    token t's row kv_cache[slot_mapping[t]] (rows of mixed_kv_row_bytes) gets,
+    per K head, the E4M3 codes of its first head_dim - rotary_dim elements and
+    then its last rotary_dim elements as bf16, then the V heads' codes.
+    Returns q_out."""
+    return _qk_store("qk_norm_rope_kv_store_mixed", mixed_kv_row_bytes(nk, nv, head_dim, rotary_dim),
+                     qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps, nq, nk, nv, head_dim,
+                     rotary_dim, slot_mapping, kv_cache, q_out, stream)
 
 
 # ------------------------------------------------------------ separated tail

@@ -24,7 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libaddnormq.so")
 # host C++ (the front end and the tiling choice; no device code) and HIP sources
 HOST_SOURCES = ["anq_api.cpp", "anq_tiling.cpp"]
-HIP_SOURCES = ["anq_tail.hip", "anq_qk.hip", "anq_quant.hip", "anq_selfcheck.hip", "anq_stream.hip"]
+HIP_SOURCES = ["anq_tail.hip", "anq_qk.hip", "anq_qk_part.hip", "anq_quant.hip", "anq_selfcheck.hip",
+               "anq_stream.hip"]
 SOURCES = HOST_SOURCES + HIP_SOURCES
 ARCH = "gfx950"
 

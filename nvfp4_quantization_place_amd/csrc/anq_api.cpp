@@ -233,14 +233,15 @@ extern "C" int anq_selfcheck_arith(uint64_t* counts, void* stream) {
 
 namespace {
 
-// Checks shared by the two Q/K entry points. q_cols is the width of `out` in
-// bytes per token (all heads, or the Q heads with a KV store); kv_bytes the
-// pool size (0 without a store).
+// Checks shared by the Q/K entry points. `store` is the epilogue (none,
+// uniform pool, mixed pool); `out` is the dense code buffer (all heads, or the
+// Q heads with a store).
 int check_qk(const void* qkv, const void* gamma_q, const void* gamma_k, const int64_t* positions,
              const float* cos_sin, int64_t max_pos, const float* scale, float eps, int64_t tokens,
              int32_t nq, int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim, int dtype,
-             const uint8_t* out, bool kv_store, const int64_t* slots, int64_t num_slots,
+             const uint8_t* out, int store, const int64_t* slots, int64_t num_slots,
              const uint8_t* kv) {
+  const bool kv_store = store != anq::kStoreNone;
   const bool need_out = !kv_store || nq > 0;
   const bool need_kv = kv_store && (int64_t)nk + nv > 0;
   if (!cos_sin || !scale ||
@@ -255,22 +256,29 @@ int check_qk(const void* qkv, const void* gamma_q, const void* gamma_k, const in
   if (tokens < 0 || head_dim <= 0 || heads == 0 || heads > (1 << 20)) return ANQ_ERR_SHAPE;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
     return ANQ_ERR_UNSUPPORTED;
-  if (rotary_dim != head_dim) return ANQ_ERR_UNSUPPORTED;
+  // the rotated width: a power of two from 16 to head_dim (the last rotary_dim
+  // elements of each Q/K head rotate); other widths keep a separated path
+  if (rotary_dim < 16 || rotary_dim > head_dim || (rotary_dim & (rotary_dim - 1)) != 0)
+    return ANQ_ERR_UNSUPPORTED;
   if (!valid_eps(eps)) return ANQ_ERR_VALUE;
   const int64_t cols = heads * head_dim;
-  if (tokens > INT64_MAX / (2 * cols) || max_pos > INT64_MAX / (4 * (int64_t)head_dim) ||
-      (kv_store && num_slots > INT64_MAX / cols))
+  // bytes of one pool row: uniform (nk+nv)*D; mixed nk*(D+R) + nv*D
+  const int64_t kv_cols = store == anq::kStoreMixed
+                              ? (int64_t)nk * (head_dim + rotary_dim) + (int64_t)nv * head_dim
+                              : ((int64_t)nk + nv) * head_dim;
+  if (tokens > INT64_MAX / (2 * cols) || max_pos > INT64_MAX / (4 * (int64_t)rotary_dim) ||
+      (kv_store && kv_cols > 0 && num_slots > INT64_MAX / kv_cols))
     return ANQ_ERR_SHAPE;
   if (!aligned(qkv, 16) || !aligned(out, 16) || !aligned(cos_sin, 16) || !aligned(positions, 8) ||
       !aligned(scale, 4) || (nq > 0 && !aligned(gamma_q, 16)) || (nk > 0 && !aligned(gamma_k, 16)) ||
       (kv_store && (!aligned(kv, 16) || !aligned(slots, 8))))
     return ANQ_ERR_ALIGN;
   const int64_t out_cols = kv_store ? (int64_t)nq * head_dim : cols;
-  const int64_t kv_bytes = need_kv ? num_slots * ((int64_t)nk + nv) * head_dim : 0;
+  const int64_t kv_bytes = need_kv ? num_slots * kv_cols : 0;
   const Span outs[2] = {span(out, tokens * out_cols), span(kv, kv_bytes)};
   const Span ins[7] = {span(qkv, tokens * cols * 2), span(nq ? gamma_q : nullptr, nq ? head_dim * 2 : 0),
                        span(nk ? gamma_k : nullptr, nk ? head_dim * 2 : 0), span(positions, tokens * 8),
-                       span(cos_sin, max_pos * head_dim * 4), span(scale, 4),
+                       span(cos_sin, max_pos * rotary_dim * 4), span(scale, 4),
                        span(need_kv ? slots : nullptr, need_kv ? tokens * 8 : 0)};
   if (any_alias(outs, 2, ins, 7)) return ANQ_ERR_ALIAS;
   return ANQ_OK;
@@ -307,6 +315,24 @@ int launch_qk_op(int dtype, int store, anq::QKParams& p, void* stream) {
   return launch_status(anq::launch_qk(dtype, store, p, t, stream));
 }
 
+// The two KV-store entry points: Q codes dense, K and V to the pool.
+int qk_store(const void* qkv, const void* gamma_q, const void* gamma_k, const int64_t* positions,
+             const float* cos_sin, int64_t max_pos, const float* scale, float eps, int64_t tokens,
+             int32_t nq, int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim, int dtype,
+             const int64_t* slot_mapping, int64_t num_slots, uint8_t* q_out, uint8_t* kv_cache,
+             int store, void* stream) {
+  const int st = check_qk(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens, nq,
+                          nk, nv, head_dim, rotary_dim, dtype, q_out, store, slot_mapping, num_slots,
+                          kv_cache);
+  if (st != ANQ_OK || tokens == 0) return st;
+  anq::QKParams p = qk_params(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens,
+                              nq, nk, nv, head_dim, rotary_dim, q_out);
+  p.kv = kv_cache;
+  p.slots = slot_mapping;
+  p.num_slots = nk + nv > 0 ? num_slots : 0;
+  return launch_qk_op(dtype, store, p, stream);
+}
+
 }  // namespace
 
 extern "C" int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void* gamma_k,
@@ -315,7 +341,8 @@ extern "C" int qk_norm_rope_fp8(const void* qkv, const void* gamma_q, const void
                                 int32_t nk, int32_t nv, int32_t head_dim, int32_t rotary_dim,
                                 anq_dtype dtype, uint8_t* out, void* stream) {
   const int st = check_qk(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens, nq,
-                          nk, nv, head_dim, rotary_dim, dtype, out, false, nullptr, 0, nullptr);
+                          nk, nv, head_dim, rotary_dim, dtype, out, anq::kStoreNone, nullptr, 0,
+                          nullptr);
   if (st != ANQ_OK || tokens == 0) return st;
   anq::QKParams p = qk_params(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps,
                               tokens, nq, nk, nv, head_dim, rotary_dim, out);
@@ -329,16 +356,22 @@ extern "C" int qk_norm_rope_fp8_kv_store(const void* qkv, const void* gamma_q, c
                                          int32_t head_dim, int32_t rotary_dim, anq_dtype dtype,
                                          const int64_t* slot_mapping, int64_t num_slots,
                                          uint8_t* q_out, uint8_t* kv_cache, void* stream) {
-  const int st = check_qk(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens, nq,
-                          nk, nv, head_dim, rotary_dim, dtype, q_out, true, slot_mapping, num_slots,
-                          kv_cache);
-  if (st != ANQ_OK || tokens == 0) return st;
-  anq::QKParams p = qk_params(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens,
-                              nq, nk, nv, head_dim, rotary_dim, q_out);
-  p.kv = kv_cache;
-  p.slots = slot_mapping;
-  p.num_slots = nk + nv > 0 ? num_slots : 0;
-  return launch_qk_op(dtype, anq::kStoreUniform, p, stream);
+  return qk_store(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens, nq, nk,
+                  nv, head_dim, rotary_dim, dtype, slot_mapping, num_slots, q_out, kv_cache,
+                  anq::kStoreUniform, stream);
+}
+
+extern "C" int qk_norm_rope_kv_store_mixed(const void* qkv, const void* gamma_q,
+                                           const void* gamma_k, const int64_t* positions,
+                                           const float* cos_sin, int64_t max_pos,
+                                           const float* scale, float eps, int64_t tokens,
+                                           int32_t nq, int32_t nk, int32_t nv, int32_t head_dim,
+                                           int32_t rotary_dim, anq_dtype dtype,
+                                           const int64_t* slot_mapping, int64_t num_slots,
+                                           uint8_t* q_out, uint8_t* kv_cache, void* stream) {
+  return qk_store(qkv, gamma_q, gamma_k, positions, cos_sin, max_pos, scale, eps, tokens, nq, nk,
+                  nv, head_dim, rotary_dim, dtype, slot_mapping, num_slots, q_out, kv_cache,
+                  anq::kStoreMixed, stream);
 }
 
 extern "C" int add_rmsnorm(const void* x, void* residual, const void* gamma, float eps,
@@ -468,7 +501,7 @@ extern "C" const char* anq_status_string(int status) {
     case ANQ_ERR_DTYPE: return "dtype must be ANQ_F16 or ANQ_BF16";
     case ANQ_ERR_ALIGN: return "misaligned pointer (16 bytes for tensors, 4 for scalars, 8 for positions)";
     case ANQ_ERR_ALIAS: return "output buffers overlap another buffer";
-    case ANQ_ERR_UNSUPPORTED: return "unsupported case (hidden > 65536, head_dim not in {32..512}, rotary_dim != head_dim): use a separated path";
+    case ANQ_ERR_UNSUPPORTED: return "unsupported case (hidden > 65536, head_dim not in {32..512}, rotary_dim not a power of two in [16, head_dim]): use a separated path";
     case ANQ_ERR_LAUNCH: return "HIP kernel launch failed";
     case ANQ_ERR_VALUE: return "bad scalar argument (eps < 0 or not finite, max_pos < 1, negative head count or num_slots)";
     case ANQ_ERR_CONFIG: return "an ANQ_* tuning variable in the environment names a tiling the library has no kernel for";

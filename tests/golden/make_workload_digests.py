@@ -31,7 +31,6 @@ OUT = os.path.join(HERE, "workload_digests.json")
 SCALARS = os.path.join(HERE, "workload_scalars.json")
 
 KV_SENTINEL = 0xA5          # initial byte of every KV-pool row
-KV_SLOT_FACTOR = (5, 4)     # pool rows = tokens * 5 / 4
 SEPARATED = (2, 3, 4)       # workloads the separated (two-kernel) tail is timed on
 SWIZZLED = (2, 4)           # workloads the swizzled block-scale layout is timed on
 
@@ -56,7 +55,8 @@ def _rows(r0: int, r1: int) -> dict:
     if isinstance(inp, W.QKInputs):
         out = O.qk_norm_rope_fp8(W.bits(inp.qkv)[r0:r1], W.bits(inp.gamma_q), W.bits(inp.gamma_k),
                                  inp.positions.numpy()[r0:r1], inp.cos_sin, inp.scale, inp.eps,
-                                 inp.nq, inp.nk, inp.nv, inp.head_dim, inp.dtype)["out"]
+                                 inp.nq, inp.nk, inp.nv, inp.head_dim, inp.dtype,
+                                 rotary_dim=inp.rotary_dim)["out"]
         return {"out": out}
     xb, rb, gb = W.bits(inp.x)[r0:r1], W.bits(inp.residual)[r0:r1], W.bits(inp.gamma)
     if inp.op == "gated":
@@ -107,18 +107,25 @@ def workload(k: int, procs: int) -> dict:
     full = {name: np.concatenate([p[name] for p in parts]) for name in parts[0]}
     e = {"name": inp.name, "rows": rows}
     if isinstance(inp, W.QKInputs):
-        D = inp.head_dim
-        num_slots = rows * KV_SLOT_FACTOR[0] // KV_SLOT_FACTOR[1]
+        D, R = inp.head_dim, inp.rotary_dim
+        num_slots = rows * W.KV_POOL_FACTOR[0] // W.KV_POOL_FACTOR[1]
         slots = W.kv_slots(k, rows, num_slots)
-        pool0 = np.full((num_slots, (inp.nk + inp.nv) * D), KV_SENTINEL, np.uint8)
-        st = O.qk_norm_rope_fp8_kv_store(W.bits(inp.qkv), W.bits(inp.gamma_q), W.bits(inp.gamma_k),
-                                         inp.positions.numpy(), inp.cos_sin, inp.scale, inp.eps,
-                                         inp.nq, inp.nk, inp.nv, D, inp.dtype, slots, pool0)
+        args = (W.bits(inp.qkv), W.bits(inp.gamma_q), W.bits(inp.gamma_k), inp.positions.numpy(),
+                inp.cos_sin, inp.scale, inp.eps, inp.nq, inp.nk, inp.nv, D)
+        if inp.name.startswith("qk_norm_rope_kv_mixed"):   # the mixed pool
+            pool0 = np.full((num_slots, O.mixed_kv_row_bytes(inp.nk, inp.nv, D, R)), KV_SENTINEL,
+                            np.uint8)
+            st = O.qk_norm_rope_kv_store_mixed(*args, R, inp.dtype, slots, pool0)
+            prefix = "kv_mixed"
+        else:                                               # the uniform FP8 pool
+            pool0 = np.full((num_slots, (inp.nk + inp.nv) * D), KV_SENTINEL, np.uint8)
+            st = O.qk_norm_rope_fp8_kv_store(*args, inp.dtype, slots, pool0, rotary_dim=R)
+            prefix = "kv_store"
         assert np.array_equal(st["q"], full["out"][:, :inp.nq * D])
-        full["kv_store_q"] = st["q"]
-        full["kv_store_pool"] = st["kv"]
+        full[prefix + "_q"] = st["q"]
+        full[prefix + "_pool"] = st["kv"]
         e["kv_store"] = {"num_slots": num_slots, "slots": "workloads.kv_slots(%d, %d, %d)"
-                         % (k, rows, num_slots), "sentinel": KV_SENTINEL}
+                         % (k, rows, num_slots), "sentinel": KV_SENTINEL, "rotary_dim": R}
     if k in SWIZZLED:
         full["sf_swizzled"] = O.swizzle_block_scales(full["sf"])
     e["outputs"] = _digests(full)

@@ -75,7 +75,8 @@ def gpu_full_workload(k: int, variant: str = "fused") -> dict:
 
     variant: "fused" (the workload's own op), "separated" (add_rmsnorm, then the
     standalone quantiser on its T norm output), "swizzled" (NVFP4 with the
-    128x4-tiled block scales) or "kv_store" (the Q/K op into a KV pool)."""
+    128x4-tiled block scales), "kv_store" (the Q/K op into a uniform FP8 pool)
+    or "kv_mixed" (the Q/K op into the mixed FP8 / bf16 pool)."""
     import json
     import os
 
@@ -90,16 +91,21 @@ def gpu_full_workload(k: int, variant: str = "fused") -> dict:
                 torch.from_numpy(inp.cos_sin).to(dev),
                 torch.tensor([inp.scale], dtype=torch.float32, device=dev), inp.eps, inp.nq,
                 inp.nk, inp.nv, inp.head_dim)
+        R = inp.rotary_dim
         if variant == "fused":
-            out = {"out": A.qk_norm_rope_fp8(*args)}
-        elif variant == "kv_store":
+            out = {"out": A.qk_norm_rope_fp8(*args, rotary_dim=R)}
+        elif variant in ("kv_store", "kv_mixed"):
             with open(os.path.join(golden, "workload_digests.json")) as fh:
                 kv = json.load(fh)[str(k)]["kv_store"]
             slots = torch.from_numpy(W.kv_slots(k, inp.tokens, kv["num_slots"])).to(dev)
-            pool = torch.full((kv["num_slots"], (inp.nk + inp.nv) * inp.head_dim), kv["sentinel"],
-                              dtype=torch.uint8, device=dev)
-            q = A.qk_norm_rope_fp8_kv_store(*args, slots, pool)
-            out = {"kv_store_q": q, "kv_store_pool": pool}
+            width = (A.mixed_kv_row_bytes(inp.nk, inp.nv, inp.head_dim, R) if variant == "kv_mixed"
+                     else (inp.nk + inp.nv) * inp.head_dim)
+            pool = torch.full((kv["num_slots"], width), kv["sentinel"], dtype=torch.uint8, device=dev)
+            if variant == "kv_mixed":
+                q = A.qk_norm_rope_kv_store_mixed(*args, R, slots, pool)
+            else:
+                q = A.qk_norm_rope_fp8_kv_store(*args, slots, pool, rotary_dim=R)
+            out = {variant + "_q": q, variant + "_pool": pool}
         else:
             raise ValueError(variant)
         torch.cuda.synchronize()

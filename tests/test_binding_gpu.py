@@ -117,6 +117,14 @@ def test_qk_sizes_are_checked():
     with pytest.raises(ValueError, match="q_out"):
         A.qk_norm_rope_fp8_kv_store(qkv, gq, gk, pos, cs, s, 1e-6, 2, 1, 1, 128, slots, pool,
                                     q_out=_u8(5 * 128))
+    # the mixed pool: rows of nk*(D+R) + nv*D bytes, a table as wide as the rotary width
+    csr = torch.from_numpy(W.rope_table(5, 64, 1e6)).cuda()
+    with pytest.raises(ValueError, match="whole rows"):
+        A.qk_norm_rope_kv_store_mixed(qkv, gq, gk, pos, csr, s, 1e-6, 2, 1, 1, 128, 64, slots,
+                                      _u8(9 * 256).view(9, 256))
+    with pytest.raises(ValueError, match="cos_sin"):
+        A.qk_norm_rope_kv_store_mixed(qkv, gq, gk, pos, cs, s, 1e-6, 2, 1, 1, 128, 64, slots,
+                                      _u8(9 * 320).view(9, 320))
     # a layout without K heads does not look at gamma_k at all
     inp2 = W.make_qk(4, "bf16", 5, 2, 0, 1, 128)
     out = A.qk_norm_rope_fp8(inp2.qkv.cuda(), inp2.gamma_q.cuda(), None, inp2.positions.cuda(),

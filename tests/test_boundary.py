@@ -57,7 +57,8 @@ def test_header_declares_the_entry_points():
                                            "quant_nvfp4_swizzled", "anq_nvfp4_swizzled_sf_shape",
                                            "gated_rmsnorm_quant_nvfp4", "silu_gate_f32",
                                            "anq_nvfp4_shape", "anq_selfcheck_arith",
-                                           "anq_status_string", "anq_stream_rw"])
+                                           "anq_status_string", "anq_stream_rw",
+                                           "qk_norm_rope_kv_store_mixed"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -262,7 +263,10 @@ def test_qk_validation(L):
     assert qk(L, gq=None, nq=0) == OK                   # gamma_q unused without Q heads
     assert qk(L, gk=None, nk=0) == OK
     assert qk(L, dtype=5) == DTYPE
-    assert qk(L, rot=64) == UNSUP                        # partial rotary width is not fused
+    for rot in (16, 32, 64):                             # the last rot elements rotate
+        assert qk(L, rot=rot) == OK, rot
+    for rot in (0, 8, 48, 96, 256, -128):                # below 16, not a power of two, past D
+        assert qk(L, rot=rot) == UNSUP, rot
     for d in (48, 96, 1024, 16):
         assert qk(L, D=d, rot=d) == UNSUP, d
     assert qk(L, nq=-1) == VALUE
@@ -300,13 +304,48 @@ def test_qk_kv_store_validation(L):
     assert qks(L, nq=0, q=None, gq=None) == OK           # no Q heads: q_out unused
     assert qks(L, nk=0, nv=0, slots=None, kv=None) == OK  # no K/V heads: no pool
     assert qks(L, num_slots=-1) == VALUE
-    assert qks(L, rot=64) == UNSUP
+    assert qks(L, rot=64) == OK
+    assert qks(L, rot=24) == UNSUP
     assert qks(L, kv=addr(9, 8)) == ALIGN
     assert qks(L, slots=addr(8, 4)) == ALIGN
     assert qks(L, tokens=4, kv=addr(0)) == ALIAS         # pool over qkv
     assert qks(L, tokens=4, kv=addr(6)) == ALIAS         # pool over q_out
     assert qks(L, tokens=4, slots=addr(9)) == ALIAS      # slots inside the pool
     assert qks(L, tokens=4, num_slots=1 << 62) == SHAPE  # pool size overflow
+
+
+def qkm(L, **kw):
+    a = dict(qkv=addr(0), gq=addr(1), gk=addr(2), pos=addr(3), cs=addr(4), max_pos=4096,
+             scale=addr(5), eps=1e-6, tokens=0, nq=16, nk=8, nv=8, D=128, rot=64, dtype=1,
+             slots=addr(8), num_slots=1024, q=addr(6), kv=addr(9), stream=None)
+    a.update(kw)
+    return L.qk_norm_rope_kv_store_mixed(a["qkv"], a["gq"], a["gk"], a["pos"], a["cs"],
+                                         a["max_pos"], a["scale"], a["eps"], a["tokens"], a["nq"],
+                                         a["nk"], a["nv"], a["D"], a["rot"], a["dtype"], a["slots"],
+                                         a["num_slots"], a["q"], a["kv"], a["stream"])
+
+
+def test_qk_mixed_store_validation(L):
+    """The mixed pool's rows are nk*(D+R) + nv*D bytes: the alias check uses
+    that size, and a pool whose rows are that wide may end right before
+    another buffer."""
+    assert qkm(L) == OK
+    for k in ("qkv", "pos", "q", "slots", "kv"):
+        assert qkm(L, tokens=4, **{k: None}) == NULL, k
+        assert qkm(L, tokens=0, **{k: None}) == OK, k
+    assert qkm(L, nk=0, nv=0, slots=None, kv=None) == OK
+    assert qkm(L, rot=128) == OK                         # the whole head in bf16
+    for rot in (8, 24, 256):
+        assert qkm(L, rot=rot) == UNSUP, rot
+    assert qkm(L, num_slots=-1) == VALUE
+    assert qkm(L, kv=addr(9, 8)) == ALIGN
+    row = 8 * (128 + 64) + 8 * 128                       # 2560 bytes per slot
+    # a pool ending where q_out starts passes validation (then the launch: no GPU here, so
+    # ANQ_ERR_LAUNCH from the product library, ANQ_OK from the host-check build)
+    assert qkm(L, tokens=4, num_slots=4, kv=addr(6) - 4 * row) in (OK, LAUNCH)
+    assert qkm(L, tokens=4, num_slots=4, kv=addr(6) - 4 * row + 16) == ALIAS
+    assert qkm(L, tokens=4, cs=addr(9) + 1024 * row - 16) == ALIAS        # table inside the pool
+    assert qkm(L, tokens=4, num_slots=1 << 62) == SHAPE
 
 
 def addnorm(L, **kw):

@@ -82,5 +82,17 @@ def test_qk_ops_write_inside_their_buffers():
     bkv, kv = _guarded((5, 2 * 64))
     slots = torch.tensor([4, -1, 0, 9, 2, 3, 1], dtype=torch.int64, device="cuda")
     A.qk_norm_rope_fp8_kv_store(*args, slot_mapping=slots, kv_cache=kv, q_out=q)
-    for buf, n in ((bo, out.numel()), (bq, q.numel()), (bkv, kv.numel())):
-        assert _guard_intact(buf, n)
+    checks = [(bo, out.numel()), (bq, q.numel()), (bkv, kv.numel())]
+    for R in (16, 32):       # partial rotation, and the mixed pool (rows of nk*(D+R) + nv*D)
+        p = W.make_qk(4, "bf16", 7, 2, 1, 1, 64, rotary_dim=R)
+        pargs = (p.qkv.cuda(), p.gamma_q.cuda(), p.gamma_k.cuda(), p.positions.cuda(),
+                 torch.from_numpy(p.cos_sin).cuda(), torch.tensor([0.05], device="cuda"), 1e-6, 2,
+                 1, 1, 64)
+        bo2, out2 = _guarded((7, 4 * 64))
+        A.qk_norm_rope_fp8(*pargs, rotary_dim=R, out=out2)
+        bqm, qm = _guarded((7, 2 * 64))
+        bkm, km = _guarded((5, A.mixed_kv_row_bytes(1, 1, 64, R)))
+        A.qk_norm_rope_kv_store_mixed(*pargs, R, slot_mapping=slots, kv_cache=km, q_out=qm)
+        checks += [(bo2, out2.numel()), (bqm, qm.numel()), (bkm, km.numel())]
+    for i, (buf, n) in enumerate(checks):
+        assert _guard_intact(buf, n), i

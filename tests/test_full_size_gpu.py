@@ -31,7 +31,7 @@ DIGESTS = os.path.join(HERE, "golden", "workload_digests.json")
 
 CASES = [(1, "fused"), (2, "fused"), (3, "fused"), (4, "fused"), (5, "fused"), (6, "fused"),
          (2, "separated"), (3, "separated"), (4, "separated"),
-         (2, "swizzled"), (4, "swizzled"), (5, "kv_store")]
+         (2, "swizzled"), (4, "swizzled"), (5, "kv_store"), (7, "fused"), (7, "kv_mixed")]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -63,7 +63,7 @@ def _explain(k, name, got, want, bad_chunks):
     c = bad_chunks[0]
     msg = f"workload {k} {name}: {len(bad_chunks)} of {len(want['chunks'])} chunks differ " \
           f"(first rows {c * cr}..{(c + 1) * cr - 1})"
-    if name in ("kv_store_pool", "sf_swizzled", "kv_store_q"):
+    if name in ("kv_store_pool", "sf_swizzled", "kv_store_q", "kv_mixed_pool", "kv_mixed_q"):
         return msg
     ref = _oracle_rows(k, c * cr, min((c + 1) * cr, got.shape[0]))
     if name not in ref:

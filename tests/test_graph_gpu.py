@@ -33,8 +33,11 @@ def _calls(A, b):
     A.qk_norm_rope_fp8_kv_store(b["qkv"], b["gq"], b["gk"], b["pos"], b["cs"], b["s"], 1e-6, 4, 2,
                                 2, 128, slot_mapping=b["slots"], kv_cache=b["kv"], q_out=b["qq"])
     A.quant_nvfp4(b["n4"], b["G"], q=b["qq4"], sf=b["qsf4"])
+    A.qk_norm_rope_kv_store_mixed(b["qkv"], b["gq"], b["gk"], b["pos"], b["cs64"], b["s"], 1e-6,
+                                  4, 2, 2, 128, 64, slot_mapping=b["slots"], kv_cache=b["kvm"],
+                                  q_out=b["qqm"])
     return [b[k] for k in ("res", "q4", "sf4", "n4", "res2", "q8", "n8", "res3", "qs", "sfs", "qg",
-                           "sfg", "qko", "qq", "kv", "qq4", "qsf4")]
+                           "sfg", "qko", "qq", "kv", "qq4", "qsf4", "qqm", "kvm")]
 
 
 def test_graph_replays_match_eager():
@@ -64,13 +67,17 @@ def test_graph_replays_match_eager():
              kv=torch.zeros(100, 4 * 128, dtype=torch.uint8, device=dev),
              slots=torch.from_numpy(np.random.default_rng(3).permutation(100)[:77].astype(np.int64)).to(dev),
              qq4=torch.empty(M, H // 2, dtype=torch.uint8, device=dev),
-             qsf4=torch.empty(M, H // 16, dtype=torch.uint8, device=dev))
+             qsf4=torch.empty(M, H // 16, dtype=torch.uint8, device=dev),
+             cs64=torch.from_numpy(W.rope_table(77, 64, 1e6)).to(dev),
+             qqm=torch.empty(77, 4 * 128, dtype=torch.uint8, device=dev),
+             kvm=torch.zeros(100, A.mixed_kv_row_bytes(2, 2, 128, 64), dtype=torch.uint8, device=dev))
     res0 = inp.residual.to(dev)
 
     def refill():
         for k in ("res", "res2", "res3"):
             b[k].copy_(res0)
         b["kv"].zero_()
+        b["kvm"].zero_()
 
     refill()
     eager = [t.clone() for t in _calls(A, b)]
@@ -89,7 +96,7 @@ def test_graph_replays_match_eager():
     for rep in range(4):
         refill()
         for t in outs:                              # stale results would show
-            if t is b["kv"] or t is b["res"] or t is b["res2"] or t is b["res3"]:
+            if any(t is b[k] for k in ("kv", "kvm", "res", "res2", "res3")):
                 continue
             t.fill_(0xEE if t.dtype == torch.uint8 else float("nan"))
         torch.cuda.synchronize()

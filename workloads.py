@@ -166,7 +166,14 @@ CONFIGS = {
     6: dict(name="gated_nvfp4_bf16_8192x8192_g1024", op="gated", dtype="bf16", tokens=8192,
             hidden=8192, group=1024, x=("normal", 1.0), z=("normal", 2.0),
             gamma=("one_plus", 0.1), eps=1e-5),
+    # the Q/K op storing K into the mixed pool (FP8 unrotated part, bf16 rotated part) with the
+    # last 64 of 128 elements rotated; the pages give no shape, so workload 5's layout is kept
+    7: dict(name="qk_norm_rope_kv_mixed_bf16_4096x32x128_rot64", op="qk_mixed", dtype="bf16",
+            tokens=4096, nq=16, nk=8, nv=8, head_dim=128, rotary_dim=64, theta=1e6, eps=1e-6,
+            scale=0.05),
 }
+
+KV_POOL_FACTOR = (5, 4)   # KV-store workloads: a pool of tokens * 5 / 4 slots, tokens shuffled in
 
 
 def _draw(spec, seed: int, tid: int, n: int) -> np.ndarray:
@@ -239,15 +246,16 @@ def make_gated(seed: int, dtype: str, tokens: int, hidden: int, group: int, *,
 
 
 def make_config(k: int):
-    """Inputs of workload k (1..5), seed k. NVFP4 global scales are not drawn:
+    """Inputs of workload k (1..7), seed k. NVFP4 global scales are not drawn:
     they are derived from the normed tensor and stored beside the tests."""
     c = dict(CONFIGS[k])
     if c["op"] == "gated":
         return make_gated(k, c["dtype"], c["tokens"], c["hidden"], c["group"], x=c["x"], z=c["z"],
                           gamma=c["gamma"], eps=c["eps"], name=c["name"])
-    if c["op"] == "qk":
+    if c["op"] in ("qk", "qk_mixed"):
         return make_qk(k, c["dtype"], c["tokens"], c["nq"], c["nk"], c["nv"], c["head_dim"],
-                       theta=c["theta"], eps=c["eps"], scale=c["scale"], name=c["name"])
+                       theta=c["theta"], eps=c["eps"], scale=c["scale"],
+                       rotary_dim=c.get("rotary_dim"), name=c["name"])
     return make_tail(k, c["op"], c["dtype"], c["tokens"], c["hidden"], x=c["x"], res=c["res"],
                      gamma=c["gamma"], eps=c["eps"], scale=c["scale"], norm_out=c["norm_out"],
                      outliers=c["outliers"], name=c["name"])
