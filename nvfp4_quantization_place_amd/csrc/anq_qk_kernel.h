@@ -12,9 +12,11 @@
 //     every NeoX pair (k, k + D/2) lives in one lane;
 //   partial rotation over the last R elements (PART true, N = D - R): lanes
 //     j < R/16 hold a = [N + 8j, ...) and b = [N + R/2 + 8j, ...), the pairs
-//     (N + k, N + k + R/2); lanes j >= R/16 hold 16 consecutive elements of
-//     the unrotated part, a = [16m, 16m+8) and b = [16m+8, 16m+16) with
-//     m = j - R/16. With R = D this is the whole-head layout.
+//     (N + k, N + k + R/2); lanes j >= R/16 (m = j - R/16) hold unrotated
+//     elements a = [8m, ...) and b = [N/2 + 8m, ...), so each of the two
+//     vector loads of a wavefront still covers two contiguous ranges of a
+//     head (R = 16, a single rotated lane: a = [16m, ...), b = [16m + 8, ...)).
+//     With R = D this is the whole-head layout.
 // A wavefront takes at most four groups of heads of its token and issues all
 // of their loads at once, with the token's cos|sin slice; the workgroup
 // shares gamma_q and gamma_k as binary32 in LDS. A head's sum of squares
@@ -49,9 +51,15 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
   const int RL = R >> 4;
   const int N = D - R;
   const bool rope_lane = !PART || j < RL;
-  // element offsets of the lane's two vectors inside a head
-  const uint32_t ea = rope_lane ? (uint32_t)(N + 8 * j) : (uint32_t)(16 * (j - RL));
-  const uint32_t eb = rope_lane ? (uint32_t)(N + R / 2 + 8 * j) : ea + 8u;
+  // element offsets of the lane's two vectors inside a head; with two or more
+  // rotated lanes (RL even) the unrotated lanes split their part in halves as
+  // the rotated ones do, so rotated and unrotated lanes alike pair up (j, j^1)
+  // for the code stores below
+  const bool halves = RL >= 2;
+  const int m = j - RL;  // the unrotated lanes' index
+  const uint32_t ea = rope_lane ? (uint32_t)(N + 8 * j) : (uint32_t)(halves ? 8 * m : 16 * m);
+  const uint32_t eb = rope_lane ? (uint32_t)(N + R / 2 + 8 * j)
+                                : (uint32_t)(halves ? N / 2 + 8 * m : 16 * m + 8);
   // wavefront-uniform indices and row bases live in scalar registers; the
   // lanes add 32-bit byte offsets (a token row is < 2^31 bytes)
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) +
@@ -151,14 +159,15 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
       if (sl >= 0 && sl < p.num_slots) kvrow = p.kv + (size_t)sl * row_bytes;
     }
   }
-  // Code stores of 16 contiguous bytes per lane. Rotated lanes pair up (2m,
-  // 2m+1) and swap one 8-byte half (see below): the even lane stores elements
-  // [N + 16m', +16) of the first rotated half, the odd lane the same range of
-  // the second half. A single rotated lane (R = 16) and the unrotated lanes
-  // already hold 16 consecutive elements.
+  // Code stores of 16 contiguous bytes per lane. Lanes pair up (j, j^1) and
+  // swap one 8-byte half (see below): the even lane stores 16 consecutive
+  // elements of the first half of its part (rotated or not), the odd lane the
+  // same range of the second half. With a single rotated lane (R = 16) no lane
+  // swaps: every lane already holds 16 consecutive elements.
   const bool odd = (j & 1) != 0;
-  const bool swap = rope_lane && RL >= 2;
-  const uint32_t st_off = swap ? (odd ? (uint32_t)(N + R / 2 + 8 * (j - 1)) : ea) : ea;
+  const bool swap = halves;
+  const uint32_t half_off = rope_lane ? (uint32_t)(R / 2) : (uint32_t)(N / 2);  // eb - ea
+  const uint32_t st_off = swap && odd ? ea - 8u + half_off : ea;
 
   // one group of heads: the slot's head h = pass * HPP + slot, from its two
   // unpacked vectors
@@ -248,8 +257,8 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
           if (rope_lane) {  // the rotated part in bf16: elements N + 8j and N + R/2 + 8j
             st16s<NT>(kh + (uint32_t)N + 16u * (uint32_t)j, bfa);
             st16s<NT>(kh + (uint32_t)(N + R) + 16u * (uint32_t)j, bfb);
-          } else {          // the unrotated part in E4M3: 16 codes at element ea
-            st16s<NT>(kh + ea, v);
+          } else {          // the unrotated part in E4M3: the lane's 16 codes
+            st16s<NT>(kh + st_off, v);
           }
         } else {  // V heads (and K heads of the uniform pool): codes
           const uint32_t base = STORE == kStoreMixed

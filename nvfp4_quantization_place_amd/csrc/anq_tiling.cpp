@@ -76,6 +76,12 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, Tiling* out) {
   } else {
     t.group = 0;
     t.vec_per_lane = vec <= 1024 ? 1 : (vec <= 2048 ? 2 : (vec <= 4096 ? 4 : 8));
+    // rows of 4104 to 8184 elements, many of them: two vectors per lane and
+    // one row per workgroup. bf16 NVFP4 + norm output, inputs from HBM, same
+    // box: [8192, 7168] 85.8 -> 82.7 us, [4096, 7168] 47.6 -> 44.9, [16384,
+    // 7168] 158.6 -> 157.4, [8192, 5120] 62.8 -> 61.1, [4096, 4608] 31.5 ->
+    // 30.5, [8192, 6144] 71.6 -> 72.1 (the one loss)
+    if (vec > 512 && vec < 1024 && tokens >= 2048) t.vec_per_lane = 2;
   }
   if (const char* o = getenv("ANQ_TAIL_TILING")) {
     if (*o) {
@@ -96,8 +102,9 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, Tiling* out) {
     groups_per_block = 1;
   }
   // wide rows: two rows per workgroup once there are rows enough to spare, so
-  // the second row's loads overlap the first row's reduction and stores
-  t.rows = (t.group == 0 && t.block >= 512 && tokens >= 4096) ? 2 : 1;
+  // the second row's loads overlap the first row's reduction and stores (one
+  // vector per lane; with two, one row per workgroup measured faster above)
+  t.rows = (t.group == 0 && t.block >= 512 && tokens >= 4096 && t.vec_per_lane == 1) ? 2 : 1;
   if (!env_int("ANQ_ROWS_PER_GROUP", 1, 1 << 20, &t.rows)) return ANQ_ERR_CONFIG;
   // streaming hints from 1 MiB of x. With inputs coming from HBM they measured
   // 10-15% faster from 1 to 32 MiB of x on MI355X (fp16 [256, 8192] NVFP4 5.25

@@ -5,8 +5,8 @@ numpy code; nothing on the product path may import it.
 
 Formats:
   * fp16 (IEEE binary16) and bf16 (the top half of binary32): the activation
-    types the pages allow ("contiguous FP16/BF16 with matching dtypes",
-    TensorRT-LLM issue #17900, Proposal).
+    types of the fused case, one type per call (TensorRT-LLM issue #17900,
+    Proposal).
   * E4M3FN, the OCP 8-bit float with 4 exponent bits (bias 7) and 3 mantissa
     bits, no infinities, S.1111.111 = NaN, max finite 448. Used for the
     per-tensor FP8 output and for the NVFP4 block scales (the pages say "FP8"

@@ -74,7 +74,9 @@ def tail(L, op, tokens, hidden, dtype=1, norm=True):
     (16, 128, dict(group="16", vec_per_lane="1", block="256", rows="1")),
     (64, 8192, dict(group="0", vec_per_lane="1", block="1024", rows="1", stream="1")),
     (65536, 1024, dict(group="0", vec_per_lane="1", block="128", rows="1", stream="1")),
-    (8192, 7168, dict(group="0", vec_per_lane="1", block="896", rows="2", stream="1")),
+    (8192, 7168, dict(group="0", vec_per_lane="2", block="448", rows="1", stream="1")),
+    (1024, 7168, dict(group="0", vec_per_lane="1", block="896", rows="1", stream="1")),
+    (8192, 8192, dict(group="0", vec_per_lane="1", block="1024", rows="2", stream="1")),
     (3, 65536, dict(group="0", vec_per_lane="8", block="1024")),
 ])
 def test_workload_tilings(L, tokens, hidden, want):
