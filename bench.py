@@ -381,6 +381,11 @@ class StreamCalib:
 
 SPREAD_REPLAYS = 10
 GRAPH_WARM_S = 0.025
+# a spin kernel of this many GPU cycles (~0.1 ms) runs before each timed
+# replay, so the host has submitted the graph by the time the start event is
+# reached: the events then bracket the GPU's work on the K calls, not the
+# host's submission of the graph
+LEAD_CYCLES = 250_000
 
 
 def time_workload(w, steps: int, warmup: int, eager: bool = True, spread: bool = True) -> dict:
@@ -445,6 +450,7 @@ def time_workload(w, steps: int, warmup: int, eager: bool = True, spread: bool =
         if flush is not None:
             assert int(flush.sum()) == flush.numel()
         torch.cuda.synchronize()
+        torch.cuda._sleep(LEAD_CYCLES)
         ev0.record()
         replay_next()
         ev1.record()
@@ -474,6 +480,7 @@ def time_workload(w, steps: int, warmup: int, eager: bool = True, spread: bool =
             w.call(0)
     gh.replay()
     torch.cuda.synchronize()
+    torch.cuda._sleep(LEAD_CYCLES)
     ev0.record()
     gh.replay()
     ev1.record()

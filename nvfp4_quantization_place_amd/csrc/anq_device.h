@@ -534,7 +534,8 @@ constexpr uint32_t kGateTabLo = 102u << 7;  // bf16 exponent field 102: 2^-25
 // table), b is in the table iff bits 12..14 of t are clear: positive z in
 // range give t < 4096, negative ones 0x8000 <= t < 0x9000, and every other b
 // sets one of those bits. The entry is (t & 4095) | (b's sign at bit 12), one
-// bitfield insert of b >> 3 (b has 16 bits, so b >> 3 has nothing above bit 12).
+// bitfield insert of b >> 3 (b has 16 bits, so b >> 3 has nothing above bit
+// 12); every index is below kGateTab whatever b is.
 __device__ __forceinline__ void gate_lut8(const float (&x)[8], const U4& zv, const float* tab,
                                           const double* exp2_tab, float (&u)[8]) {
   float s[8];

@@ -83,12 +83,13 @@ __device__ __forceinline__ void fill_gate_tab(uint4* tab) {
 
 // ---------------------------------------------------------------- the kernel
 
-// Start of a row in a tensor. With one row per workgroup the row is the same in
-// every lane, and its offset goes to scalar registers (SGPR base + 32-bit lane
-// offsets instead of a 64-bit address per lane).
+// Start of a row in a tensor. With one row per workgroup, or per 64-lane
+// group (a whole wavefront), the row is the same in every lane of a
+// wavefront, and its offset goes to scalar registers (SGPR base + 32-bit lane
+// offsets instead of a 64-bit address computed per lane).
 template <int G, class T>
 __device__ __forceinline__ T* row_ptr(T* base, size_t off) {
-  if constexpr (G == 0) return base + uniform_u64(off);
+  if constexpr (G == 0 || G == 64) return base + uniform_u64(off);
   return base + off;
 }
 
@@ -150,7 +151,10 @@ tail_kernel(TailParams p) {
   if constexpr (G > 0) {
     lane = threadIdx.x & (G - 1);
     L = G;
-    group = (int64_t)blockIdx.x * (blockDim.x / G) + threadIdx.x / G;
+    // a 64-lane group is a whole wavefront: its index (and so its rows) is
+    // made wavefront-uniform here, so row arithmetic runs on the scalar unit
+    const uint32_t gw = G == 64 ? __builtin_amdgcn_readfirstlane(threadIdx.x / G) : threadIdx.x / G;
+    group = (int64_t)blockIdx.x * (blockDim.x / G) + gw;
   } else {
     lane = threadIdx.x;
     L = blockDim.x;
@@ -208,13 +212,18 @@ tail_kernel(TailParams p) {
     sc = *p.scale;
     if constexpr (EPI == kEpiFp8) inv_sc = recip_rn(sc);  // s is a positive normal <= 2^119
   }
-  extern __shared__ uint4 gate_tab4[];  // kLut: kGateTab entries (dynamic shared memory)
-  const float* gate_tab = reinterpret_cast<const float*>(gate_tab4);
+  // kLut: the bf16 gate table, kGateTab binary32 entries, in static shared
+  // memory (its address is then a constant the LDS reads take as an offset)
+  const float* gate_tab = nullptr;
   static_assert(!kLut || DT == kBF16, "the gate table covers bf16 z");
   if constexpr (kNvfp4) {
     fill_mult_tab(mult_tab, sc);
     if constexpr (kGated) fill_exp2_tab(exp2_tab);
-    if constexpr (kLut) fill_gate_tab(gate_tab4);
+    if constexpr (kLut) {
+      __shared__ uint4 gate_tab4[kGateTab / 4];
+      fill_gate_tab(gate_tab4);
+      gate_tab = reinterpret_cast<const float*>(gate_tab4);
+    }
     __syncthreads();
   }
   // gamma stays packed in registers (4 per vector) and is unpacked per row:
@@ -280,7 +289,10 @@ tail_kernel(TailParams p) {
   };
 
   int parity = 0;
-  for (; row < row_end; ++row, parity ^= 1) {
+  // gated: the gamma slice of the row, row % gamma_period, kept as a running
+  // counter (one modulo for the first row, none per row)
+  int32_t gslice = kGated && p.gamma_period > 1 ? (int32_t)(row % p.gamma_period) : 0;
+  for (; row < row_end; ++row, parity ^= 1, gslice = gslice + 1 == p.gamma_period ? 0 : gslice + 1) {
     uint8_t* rrow = row_ptr<G>(res, (size_t)row * row_bytes);
     // the rare double-double pass re-reads the lane's own just-stored residual
     // elements (the gated variant recomputes u from x and z below)
@@ -342,7 +354,7 @@ tail_kernel(TailParams p) {
     } else {
     if constexpr (kGated) {  // each group of a token has its own gamma slice
       if (p.gamma_period > 1) {
-        const uint8_t* grow = gam + (size_t)(row % p.gamma_period) * row_bytes;
+        const uint8_t* grow = gam + (size_t)gslice * row_bytes;
 #pragma unroll
         for (int k = 0; k < K; ++k) gv[k] = ld16(grow + voff[k]);
       }
@@ -439,8 +451,7 @@ static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
   else if (t.group == 0 && t.vec_per_lane == 4) fn = (const void*)&tail_kernel<DT, EPI, NORM, 4, 0, NT>;
   else if (t.group == 0 && t.vec_per_lane == 8) fn = (const void*)&tail_kernel<DT, EPI, NORM, 8, 0, NT>;
   if (!fn) return hipErrorInvalidConfiguration;
-  const size_t dyn_lds = EPI == kEpiGatedNvfp4Lut ? kGateTab * sizeof(float) : 0;
-  return hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3((unsigned)t.block), args, dyn_lds, s);
+  return hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3((unsigned)t.block), args, 0, s);
 }
 
 template <int DT, int EPI, bool NORM>
