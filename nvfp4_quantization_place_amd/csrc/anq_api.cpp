@@ -88,7 +88,7 @@ extern "C" int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* 
   p.hidden = (int32_t)hidden;
   p.vec = (int32_t)(hidden / 8);
   anq::Tiling t;
-  if ((st = anq::pick_tail_tiling(p.vec, tokens, &t)) != ANQ_OK) return st;
+  if ((st = anq::pick_tail_tiling(p.vec, tokens, false, &t)) != ANQ_OK) return st;
   p.rows_per_group = t.rows;
   return launch_status(anq::launch_tail(dtype, anq::kEpiFp8, norm_out != nullptr, p, t, stream));
 }
@@ -132,7 +132,7 @@ int rmsnorm_nvfp4(const void* x, void* residual, const void* gamma, const float*
   p.vec = (int32_t)(hidden / 8);
   p.sf_tiles = swizzled ? (int32_t)sf_tiles_of(hidden) : 0;
   anq::Tiling t;
-  if ((st = anq::pick_tail_tiling(p.vec, tokens, &t)) != ANQ_OK) return st;
+  if ((st = anq::pick_tail_tiling(p.vec, tokens, swizzled, &t)) != ANQ_OK) return st;
   p.rows_per_group = t.rows;
   return launch_status(anq::launch_tail(dtype, swizzled ? anq::kEpiNvfp4Swz : anq::kEpiNvfp4,
                                         norm_out != nullptr, p, t, stream));
@@ -203,7 +203,7 @@ extern "C" int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const voi
   }
   anq::Tiling t;
   const int st = lut ? anq::pick_gate_lut_tiling(p.vec, p.tokens, &t)
-                     : anq::pick_tail_tiling(p.vec, p.tokens, &t);
+                     : anq::pick_tail_tiling(p.vec, p.tokens, false, &t);
   if (st != ANQ_OK) return st;
   p.rows_per_group = t.rows;
   return launch_status(anq::launch_tail(dtype, lut ? anq::kEpiGatedNvfp4Lut : anq::kEpiGatedNvfp4,
@@ -403,7 +403,7 @@ extern "C" int add_rmsnorm(const void* x, void* residual, const void* gamma, flo
   p.hidden = (int32_t)hidden;
   p.vec = (int32_t)(hidden / 8);
   anq::Tiling t;
-  const int st = anq::pick_tail_tiling(p.vec, tokens, &t);
+  const int st = anq::pick_tail_tiling(p.vec, tokens, false, &t);
   if (st != ANQ_OK) return st;
   p.rows_per_group = t.rows;
   return launch_status(anq::launch_tail(dtype, anq::kEpiNone, true, p, t, stream));

@@ -61,7 +61,7 @@ struct Tiling {
 // The tiling of a call (anq_tiling.cpp): ANQ_OK, ANQ_ERR_SHAPE for a grid past
 // 2^31 - 1 workgroups, or ANQ_ERR_CONFIG when an ANQ_* tuning variable in the
 // environment names a tiling no kernel has.
-int pick_tail_tiling(int32_t vec, int64_t tokens, Tiling* t);
+int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled_scales, Tiling* t);
 int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* t);
 
 int launch_tail(int dtype, int epi, bool norm_out, const TailParams& p, const Tiling& t,

@@ -253,12 +253,15 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
         st16s<NT>(orow + ((uint32_t)h * D + st_off), v);
       } else if (kvrow) {
         if (STORE == kStoreMixed && k_mixed) {
+          // a K head's D + R bytes need not fill whole 128-byte lines, and its
+          // three stores are separate instructions: without the streaming
+          // hint the L2 merges the shared lines before writing them back
           uint8_t* kh = kvrow + (uint32_t)(h - p.nq) * k_bytes;
           if (rope_lane) {  // the rotated part in bf16: elements N + 8j and N + R/2 + 8j
-            st16s<NT>(kh + (uint32_t)N + 16u * (uint32_t)j, bfa);
-            st16s<NT>(kh + (uint32_t)(N + R) + 16u * (uint32_t)j, bfb);
+            st16s<false>(kh + (uint32_t)N + 16u * (uint32_t)j, bfa);
+            st16s<false>(kh + (uint32_t)(N + R) + 16u * (uint32_t)j, bfb);
           } else {          // the unrotated part in E4M3: the lane's 16 codes
-            st16s<NT>(kh + st_off, v);
+            st16s<false>(kh + st_off, v);
           }
         } else {  // V heads (and K heads of the uniform pool): codes
           const uint32_t base = STORE == kStoreMixed

@@ -68,7 +68,7 @@ bool finish_grid(int64_t rows, int64_t groups_per_block, Tiling* t) {
 // and rows per lane group chosen so that a small grid still fills the GPU.
 // ANQ_TAIL_TILING="G:K" (G lanes per row, 0 = a workgroup; K vectors per lane),
 // ANQ_ROWS_PER_GROUP (>= 1) and ANQ_STREAM (0 / 1) override the choice.
-int pick_tail_tiling(int32_t vec, int64_t tokens, Tiling* out) {
+int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
   Tiling t{};
   if (vec <= 64) {
     t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
@@ -80,8 +80,9 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, Tiling* out) {
     // one row per workgroup. bf16 NVFP4 + norm output, inputs from HBM, same
     // box: [8192, 7168] 85.8 -> 82.7 us, [4096, 7168] 47.6 -> 44.9, [16384,
     // 7168] 158.6 -> 157.4, [8192, 5120] 62.8 -> 61.1, [4096, 4608] 31.5 ->
-    // 30.5, [8192, 6144] 71.6 -> 72.1 (the one loss)
-    if (vec > 512 && vec < 1024 && tokens >= 2048) t.vec_per_lane = 2;
+    // 30.5, [8192, 6144] 71.6 -> 72.1 (the one loss). Not with the swizzled
+    // scales: [8192, 7168] 84.1 -> 86.7 us.
+    if (vec > 512 && vec < 1024 && tokens >= 2048 && !swizzled) t.vec_per_lane = 2;
   }
   if (const char* o = getenv("ANQ_TAIL_TILING")) {
     if (*o) {
