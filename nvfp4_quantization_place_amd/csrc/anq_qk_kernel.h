@@ -1,22 +1,22 @@
 // Q/K per-head RMSNorm + NeoX RoPE + FP8 E4M3 of a fused QKV buffer, with its
-// store epilogues (SGLang PR #32975 "fused norm + RoPE + uniform fp8 store";
-// the Q/K RMSNorm and RoPE of TensorRT-LLM PR #17288, Description, whose Test
-// Coverage guards the RoPE width). Included by anq_qk.hip (whole-head
-// rotation) and anq_qk_part.hip (partial rotation, mixed pool), which
-// instantiate it in two translation units that compile in parallel.
+// store epilogues (SGLang PR #32975, the fused norm, RoPE and uniform FP8
+// store; the Q/K RMSNorm and RoPE of TensorRT-LLM PR #17288, Description,
+// whose Test Coverage guards the RoPE width). Included by anq_qk.hip
+// (whole-head rotation) and anq_qk_part.hip (partial rotation), which
+// instantiate it, each with every store, in two translation units that
+// compile in parallel.
 //
 // gfx950 mapping: one or a few wavefronts per token. 64 lanes form 64/(D/16)
-// head slots of D/16 lanes, and each lane holds two 8-element vectors a and b
-// of its slot's head:
-//   whole-head rotation (PART false): a = [8j, 8j+8), b = [D/2 + 8j, ...), so
-//     every NeoX pair (k, k + D/2) lives in one lane;
-//   partial rotation over the last R elements (PART true, N = D - R): lanes
-//     j < R/16 hold a = [N + 8j, ...) and b = [N + R/2 + 8j, ...), the pairs
-//     (N + k, N + k + R/2); lanes j >= R/16 (m = j - R/16) hold unrotated
-//     elements a = [8m, ...) and b = [N/2 + 8m, ...), so each of the two
-//     vector loads of a wavefront still covers two contiguous ranges of a
-//     head (R = 16, a single rotated lane: a = [16m, ...), b = [16m + 8, ...)).
-//     With R = D this is the whole-head layout.
+// head slots of D/16 lanes, and lane j of a slot holds two 8-element vectors
+// of its head, a = [8j, 8j+8) and b = [D/2 + 8j, ...), so each of a
+// wavefront's two vector loads reads whole contiguous halves of its heads.
+//   whole-head rotation (PART false): every NeoX pair (k, k + D/2) lives in
+//     one lane, as elements i of a and b;
+//   partial rotation over the last R <= D/2 elements (PART true, N = D - R):
+//     a is never rotated; the rotated part [N, D) is the b vectors of lanes
+//     j >= D/16 - R/8, and the pair (N + k, N + k + R/2) is element i of b in
+//     lanes j and j ^ R/16 of the same head, which exchange their normalised
+//     b vectors through ds_bpermute.
 // A wavefront takes at most four groups of heads of its token and issues all
 // of their loads at once, with the token's cos|sin slice; the workgroup
 // shares gamma_q and gamma_k as binary32 in LDS. A head's sum of squares
@@ -28,8 +28,8 @@
 // token's K and V codes to its slot of a uniform FP8 pool (rows of (nk+nv)*D
 // bytes); kStoreMixed writes the Q codes the same way and the token's pool row
 // as, per K head, the unrotated part's E4M3 codes then the rotated part as
-// bf16, then the V heads' codes (rows of nk*(D+R) + nv*D bytes). A slot
-// outside [0, num_slots) stores nothing.
+// bf16 (with R = D the whole head in bf16), then the V heads' codes (rows of
+// nk*(D+R) + nv*D bytes). A slot outside [0, num_slots) stores nothing.
 #pragma once
 
 #include "anq_device.h"
@@ -41,25 +41,18 @@ template <int DT, int LPH, bool NT, int STORE, int PF, bool PART>
 __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
   constexpr int D = LPH * 16;
   constexpr int HPP = 64 / LPH;  // heads per pass of a wavefront
-  static_assert(!(STORE == kStoreMixed && !PART), "the mixed pool uses the partial-rotation layout");
   const int lane = threadIdx.x & 63;
   const int j = lane & (LPH - 1);
   const int slot = lane / LPH;
-  // the rotated width R (a power of two, 16 <= R <= D), its lanes RL, and
-  // the unrotated width N; compile-time constants without PART
+  constexpr uint32_t kHalf = D / 2;
+  const uint32_t ea = 8u * (uint32_t)j;  // element offsets of the lane's a and b in its head
+  // the rotated width R (R = D without PART), and with PART: whether the
+  // lane's b vector is rotated, and whether it holds the second element of
+  // its pairs (partner lane = lane ^ RL)
   const int R = PART ? p.rotary_dim : D;
   const int RL = R >> 4;
-  const int N = D - R;
-  const bool rope_lane = !PART || j < RL;
-  // element offsets of the lane's two vectors inside a head; with two or more
-  // rotated lanes (RL even) the unrotated lanes split their part in halves as
-  // the rotated ones do, so rotated and unrotated lanes alike pair up (j, j^1)
-  // for the code stores below
-  const bool halves = RL >= 2;
-  const int m = j - RL;  // the unrotated lanes' index
-  const uint32_t ea = rope_lane ? (uint32_t)(N + 8 * j) : (uint32_t)(halves ? 8 * m : 16 * m);
-  const uint32_t eb = rope_lane ? (uint32_t)(N + R / 2 + 8 * j)
-                                : (uint32_t)(halves ? N / 2 + 8 * m : 16 * m + 8);
+  const bool rope_b = !PART || j >= LPH - 2 * RL;
+  const bool upper = (j & RL) != 0;
   // wavefront-uniform indices and row bases live in scalar registers; the
   // lanes add 32-bit byte offsets (a token row is < 2^31 bytes)
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) +
@@ -74,7 +67,7 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
   // every load below is unconditional
   const uint8_t* row = static_cast<const uint8_t*>(p.qkv) + (size_t)(active ? t : 0) * row_elems * 2;
   const uint32_t lane_off = ((uint32_t)slot * D + ea) * 2;  // bytes, the lane's a vector
-  const uint32_t b_off = (eb - ea) * 2;                     // bytes from a to b
+  constexpr uint32_t b_off = kHalf * 2;                     // bytes from a to b
 
   // gamma_q | gamma_k: thread i < D/4 loads 16-byte vector i first of all, so
   // that waiting for it (to fill LDS below) does not wait for the row loads
@@ -108,13 +101,13 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
     rb[0] = ld16s<NT>(row + o + b_off);
   }
 
-  // per-token constants: the lane's cos|sin values (lanes of the unrotated
-  // part read the last rotated lane's, unused)
+  // per-token constants: the lane's cos|sin values, those of frequency
+  // 8j + i (whole head) or 8 (j mod RL) + i (partial)
   float c[8], s[8];
   if (active && qk_heads > 0) {
     pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);  // never read outside the table
-    const int jr = rope_lane ? j : RL - 1;
-    const float* cs = p.cos_sin + (size_t)pos * R + 8 * jr;
+    const int kc = PART ? 8 * (j & (RL - 1)) : 8 * j;
+    const float* cs = p.cos_sin + (size_t)pos * R + kc;
     const float4 c0 = *reinterpret_cast<const float4*>(cs);
     const float4 c1 = *reinterpret_cast<const float4*>(cs + 4);
     const float4 s0 = *reinterpret_cast<const float4*>(cs + R / 2);
@@ -160,24 +153,23 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
     }
   }
   // Code stores of 16 contiguous bytes per lane. Lanes pair up (j, j^1) and
-  // swap one 8-byte half (see below): the even lane stores 16 consecutive
-  // elements of the first half of its part (rotated or not), the odd lane the
-  // same range of the second half. With a single rotated lane (R = 16) no lane
-  // swaps: every lane already holds 16 consecutive elements.
+  // swap one 8-byte half (see below): the even lane stores the codes of
+  // elements [8j, 8j + 16) (both a vectors), the odd lane those of
+  // [D/2 + 8(j-1), D/2 + 8(j+1)) (both b vectors).
   const bool odd = (j & 1) != 0;
-  const bool swap = halves;
-  const uint32_t half_off = rope_lane ? (uint32_t)(R / 2) : (uint32_t)(N / 2);  // eb - ea
-  const uint32_t st_off = swap && odd ? ea - 8u + half_off : ea;
+  const uint32_t st_off = odd ? ea - 8u + kHalf : ea;
 
   // one group of heads: the slot's head h = pass * HPP + slot, from its two
-  // unpacked vectors
-  auto group = [&](int pass, float (&a)[8], float (&b)[8]) {
+  // unpacked vectors, to the lane's 16 codes v and (K heads of the mixed
+  // pool) its rotated values in bf16
+  auto group = [&](int pass, float (&a)[8], float (&b)[8], U4& v, U4& bfa, U4& bfb) {
     const int h = pass * HPP + slot;
+    const bool qk = h < qk_heads;  // uniform over the head's lanes
     float oa[8], ob[8];
-    if (h < qk_heads) {  // uniform over the head's lanes
+    if (qk) {
       const float4* gl = gam_lds + (h < p.nq ? 0 : D / 4);
       const float4 ga0 = gl[ea / 4], ga1 = gl[ea / 4 + 1];
-      const float4 gb0 = gl[eb / 4], gb1 = gl[eb / 4 + 1];
+      const float4 gb0 = gl[(kHalf + ea) / 4], gb1 = gl[(kHalf + ea) / 4 + 1];
       const float ga[8] = {ga0.x, ga0.y, ga0.z, ga0.w, ga1.x, ga1.y, ga1.z, ga1.w};
       const float gb[8] = {gb0.x, gb0.y, gb0.z, gb0.w, gb1.x, gb1.y, gb1.z, gb1.w};
       double acc = 0.0;
@@ -206,10 +198,13 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
       for (int i = 0; i < 8; ++i) {
         const float na = (a[i] * r) * ga[i];
         const float nb = (b[i] * r) * gb[i];
-        const float ra_ = (na * c[i]) - (nb * s[i]);
-        const float rb_ = (nb * c[i]) + (na * s[i]);
-        oa[i] = rope_lane ? ra_ : na;
-        ob[i] = rope_lane ? rb_ : nb;
+        if constexpr (PART) {
+          oa[i] = na;
+          ob[i] = nb;
+        } else {
+          oa[i] = (na * c[i]) - (nb * s[i]);
+          ob[i] = (nb * c[i]) + (na * s[i]);
+        }
       }
     } else {
 #pragma unroll
@@ -218,12 +213,24 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
         ob[i] = b[i];
       }
     }
+    if constexpr (PART) {
+      // the partner of each rotated element is element i of b in lane ^ RL,
+      // of the same head; the whole wavefront takes part in the exchange.
+      // The first element of a pair takes x c - y s as x c + (-y) s (the
+      // same binary32 result), the second x c + y s.
+      const int src = (lane ^ RL) << 2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(ob[i])));
+        const float rot = (ob[i] * c[i]) + ((upper ? y : -y) * s[i]);
+        if (qk && rope_b) ob[i] = rot;
+      }
+    }
     // the mixed pool keeps a K head's rotated part in bf16, before the division
-    U4 bfa{}, bfb{};
-    const bool k_mixed = STORE == kStoreMixed && h >= p.nq && h < qk_heads;  // uniform per head
+    const bool k_mixed = STORE == kStoreMixed && h >= p.nq && qk;  // uniform per head
     if constexpr (STORE == kStoreMixed) {
       if (k_mixed) {
-        bfa = pack8<kBF16>(oa);
+        if (!PART) bfa = pack8<kBF16>(oa);
         bfb = pack8<kBF16>(ob);
       }
     }
@@ -237,15 +244,19 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
     const uint32_t a1 = e4m3x4_in_range(qa[4], qa[5], qa[6], qa[7]);
     const uint32_t b0 = e4m3x4_in_range(qb[0], qb[1], qb[2], qb[3]);
     const uint32_t b1 = e4m3x4_in_range(qb[4], qb[5], qb[6], qb[7]);
-    // every lane takes part in the swap (it reads its partner's registers);
-    // lanes that do not pair keep their own a and b codes
+    // every lane takes part in the swap (it reads its partner's registers)
     const uint32_t r0 = dpp_u32<0xB1>(odd ? a0 : b0), r1 = dpp_u32<0xB1>(odd ? a1 : b1);
-    U4 v;
-    v.w[0] = swap && odd ? r0 : a0;
-    v.w[1] = swap && odd ? r1 : a1;
-    v.w[2] = swap && !odd ? r0 : b0;
-    v.w[3] = swap && !odd ? r1 : b1;
+    v.w[0] = odd ? r0 : a0;
+    v.w[1] = odd ? r1 : a1;
+    v.w[2] = odd ? b0 : r0;
+    v.w[3] = odd ? b1 : r1;
+  };
+
+  // the stores of one group
+  auto store = [&](int pass, const U4& v, const U4& bfa, const U4& bfb) {
+    const int h = pass * HPP + slot;
     if (h >= heads) return;
+    const bool k_mixed = STORE == kStoreMixed && h >= p.nq && h < qk_heads;
     if constexpr (STORE == kStoreNone) {
       st16s<NT>(orow + ((uint32_t)h * D + st_off), v);
     } else {
@@ -254,14 +265,20 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
       } else if (kvrow) {
         if (STORE == kStoreMixed && k_mixed) {
           // a K head's D + R bytes need not fill whole 128-byte lines, and its
-          // three stores are separate instructions: without the streaming
-          // hint the L2 merges the shared lines before writing them back
+          // stores are separate instructions: without the streaming hint the
+          // L2 merges the shared lines before writing them back. Element e
+          // of the rotated part is bf16 at byte N + 2 (e - N) of the head.
           uint8_t* kh = kvrow + (uint32_t)(h - p.nq) * k_bytes;
-          if (rope_lane) {  // the rotated part in bf16: elements N + 8j and N + R/2 + 8j
-            st16s<false>(kh + (uint32_t)N + 16u * (uint32_t)j, bfa);
-            st16s<false>(kh + (uint32_t)(N + R) + 16u * (uint32_t)j, bfb);
-          } else {          // the unrotated part in E4M3: the lane's 16 codes
-            st16s<false>(kh + st_off, v);
+          if constexpr (PART) {
+            // b of the rotated lanes in bf16; the unrotated codes come from
+            // the even lanes (elements < D/2 <= N) and the odd lanes whose b
+            // vectors are unrotated (the rotated part starts on a 16-element
+            // boundary, so a pair of lanes is rotated or not together)
+            if (rope_b) st16s<false>(kh + (uint32_t)R + 16u * (uint32_t)j, bfb);
+            if (!odd || !rope_b) st16s<false>(kh + st_off, v);
+          } else {  // R = D: the whole head in bf16
+            st16s<false>(kh + 16u * (uint32_t)j, bfa);
+            st16s<false>(kh + kHalf * 2 + 16u * (uint32_t)j, bfb);
           }
         } else {  // V heads (and K heads of the uniform pool): codes
           const uint32_t base = STORE == kStoreMixed
@@ -274,15 +291,21 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
   };
 
   const int mine = (passes - w + W - 1) / W;  // groups of this wavefront, <= PF (w < W <= passes)
+  U4 v[PF], bfa[PF], bfb[PF];
 #pragma unroll
   for (int u = 0; u < PF; ++u) {
     if (u < mine) {  // uniform over the wavefront
       float a[8], b[8];
       unpack8<DT>(ra[u], a);
       unpack8<DT>(rb[u], b);
-      group(w + u * W, a, b);
+      group(w + u * W, a, b, v[u], bfa[u], bfb[u]);
     }
   }
+  // every store after every group: the wait for a group's loads then never
+  // also waits for an earlier group's stores (one counter covers both)
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+    if (u < mine) store(w + u * W, v[u], bfa[u], bfb[u]);
 }
 
 template <int DT, bool NT, int STORE, int PF, bool PART>
@@ -318,9 +341,8 @@ hipError_t launch_qk_store(const QKParams& p, const QKTiling& t, hipStream_t s) 
                   : launch_qk_nt<DT, false, STORE, PART>(p, t, s);
 }
 
-// Launchers of the two translation units: whole-head rotation (anq_qk.hip,
-// stores none and uniform) and partial rotation (anq_qk_part.hip, every
-// store, the mixed pool at any width).
+// Launchers of the two translation units: whole-head rotation (anq_qk.hip)
+// and partial rotation (anq_qk_part.hip), each with every store.
 hipError_t launch_qk_whole(int dtype, int store, const QKParams& p, const QKTiling& t,
                            hipStream_t s);
 hipError_t launch_qk_partial(int dtype, int store, const QKParams& p, const QKTiling& t,

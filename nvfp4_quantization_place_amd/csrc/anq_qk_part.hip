@@ -1,6 +1,6 @@
-// The Q/K op's launches with a partial rotary width (the last rotary_dim
-// elements of each Q/K head rotate) and every launch of the mixed FP8/bf16
-// pool store. The kernel is in anq_qk_kernel.h.
+// The Q/K op's launches with a partial rotary width (the last rotary_dim <=
+// head_dim / 2 elements of each Q/K head rotate), with every store. The
+// kernel is in anq_qk_kernel.h.
 #include "anq_qk_kernel.h"
 
 namespace anq {
