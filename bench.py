@@ -70,9 +70,11 @@ MAX_CPU_PROCS = 16                     # a one-GPU machine's share of host cores
 
 # ---------------------------------------------------------------- byte counts
 
-def rw_bytes(inp, kind: str = "fused") -> tuple[int, int]:
+def rw_bytes(inp, kind: str = "fused", stored: int | None = None) -> tuple[int, int]:
     """(read, write) algorithmic bytes per call: what the method must move,
-    gamma and scales counted once, the KV slot per token where there is a store.
+    gamma and scales counted once; with a KV store, each token's slot index is
+    read and the pool row written for the `stored` tokens whose slot is in the
+    pool (all tokens if not given).
 
     fused tail  reads x, residual (2 + 2 B/element), gamma (2H) and the scale;
                 writes residual 2, codes (FP8 1 | NVFP4 0.5 + 1/16), norm 2 if asked
@@ -81,15 +83,19 @@ def rw_bytes(inp, kind: str = "fused") -> tuple[int, int]:
                 quantiser (reads norm 2, writes codes)
     Q/K         reads qkv (2 B/element), positions (8 B/token), the cos|sin row
                 (4R B/token), gamma_q and gamma_k (2D each), the scale; writes
-                codes (1 B/element), the mixed pool's bf16 part 2 B/element"""
+                codes (1 B/element: Q for every token, K and V for the stored
+                ones), the mixed pool's rotated K part 2 B/element"""
     import workloads as W
     if isinstance(inp, W.QKInputs):
         D, R, T = inp.head_dim, inp.rotary_dim, inp.tokens
         C = (inp.nq + inp.nk + inp.nv) * D
-        read = T * C * 2 + T * (4 * R + 8) + 4 * D + 4 + (T * 8 if kind in ("kv_store", "kv_mixed")
-                                                           else 0)
-        write = T * C + (T * inp.nk * R if kind == "kv_mixed" else 0)
-        return read, write
+        kv = kind in ("kv_store", "kv_mixed")
+        read = T * C * 2 + T * (4 * R + 8) + 4 * D + 4 + (T * 8 if kv else 0)
+        if not kv:
+            return read, T * C
+        st = T if stored is None else stored
+        pool_row = (inp.nk + inp.nv) * D + (inp.nk * R if kind == "kv_mixed" else 0)
+        return read, T * inp.nq * D + st * pool_row
     M, H = inp.tokens, inp.hidden
     n = M * H
     codes = n if inp.op == "fp8" else n // 2 + n // 16
@@ -220,7 +226,9 @@ def cpu_baseline(workloads: list, scalars: dict, budget_s: float) -> dict:
             done = sum(pool.map(_oracle_rows, tasks))
             el_all = time.perf_counter() - t0
             all_rows_s = done / el_all
-            rd, wr = rw_bytes(inp)
+            # the sample stores every row of the mixed workload's pool
+            rd, wr = rw_bytes(inp, "kv_mixed" if inp.name.startswith("qk_norm_rope_kv_mixed")
+                              else "fused")
             per_row_bytes = (rd + wr) / rows_total
             out["per_workload"][str(k)] = {
                 "workload": inp.name,
@@ -270,9 +278,16 @@ class Workload:
 
         import workloads as W
         import nvfp4_quantization_place_amd as A
-        self.k, self.kind = k, kind
         self.inp = inp if inp is not None else W.make_config(k)
-        rd, wr = rw_bytes(self.inp, kind)
+        self.name = self.inp.name + ("" if kind == "fused" else "_" + kind)
+        if self.inp.name.startswith("qk_norm_rope_kv_mixed") and kind == "fused":
+            kind = "kv_mixed"  # this workload is the op with its mixed pool store
+        self.k, self.kind = k, kind
+        slots = None
+        if kind in ("kv_store", "kv_mixed"):
+            T = self.inp.tokens
+            slots = W.kv_slots(k, T, T * W.KV_POOL_FACTOR[0] // W.KV_POOL_FACTOR[1])
+        rd, wr = rw_bytes(self.inp, kind, None if slots is None else int((slots >= 0).sum()))
         self.read_bytes, self.write_bytes = rd, wr
         self.bytes = rd + wr
         self.sets = rotating_sets(self.bytes, steps)
@@ -284,7 +299,6 @@ class Workload:
         def u8(*shape):
             return torch.empty(S, *shape, dtype=torch.uint8, device=dev)
 
-        self.name = inp.name + ("" if kind == "fused" else "_" + kind)
         self.dtype = inp.dtype
         if isinstance(inp, W.QKInputs):
             D, R = inp.head_dim, inp.rotary_dim
@@ -294,13 +308,9 @@ class Workload:
             self.cs = torch.from_numpy(inp.cos_sin).to(dev)
             self.scale = torch.tensor([inp.scale], dtype=torch.float32, device=dev)
             T = inp.tokens
-            if inp.name.startswith("qk_norm_rope_kv_mixed") and kind == "fused":
-                self.kind = kind = "kv_mixed"
-                rd, wr = rw_bytes(inp, kind)
-                self.read_bytes, self.write_bytes, self.bytes = rd, wr, rd + wr
             if kind in ("kv_store", "kv_mixed"):
                 nslots = T * W.KV_POOL_FACTOR[0] // W.KV_POOL_FACTOR[1]
-                self.slots = torch.from_numpy(W.kv_slots(k, T, nslots)).to(dev)
+                self.slots = torch.from_numpy(slots).to(dev)
                 width = (A.mixed_kv_row_bytes(inp.nk, inp.nv, D, R) if kind == "kv_mixed"
                          else (inp.nk + inp.nv) * D)
                 self.pool = torch.zeros(S, nslots, width, dtype=torch.uint8, device=dev)
