@@ -54,7 +54,9 @@ struct Tiling {
   int vec_per_lane;
   int block;
   int rows;
-  bool stream;  // non-temporal loads and stores of the row streams
+  bool stream;        // non-temporal loads and stores of the row streams
+  bool stream_codes;  // the same hint on the code and linear block-scale stores
+                      // (plain FP8 and NVFP4 epilogues)
   int64_t grid;
 };
 

@@ -137,7 +137,9 @@ __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int 
 // Register budget: 7 wavefronts per SIMD (<= 72 VGPRs) for one vector per
 // lane, which then needs no spills; 4 (<= 128) for rows wider than 8192 and
 // for the gated variant (its binary64 exp needs the registers).
-template <int DT, int EPI, bool NORM, int K, int G, bool NT, bool SL = (K >= 4)>
+// NT: 0 no streaming hints; 1 on the row loads and stores (x, residual, norm
+// output); 2 also on the code and linear block-scale stores
+template <int DT, int EPI, bool NORM, int K, int G, int NT, bool SL = (K >= 4)>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 && EPI != kEpiGatedNvfp4Lut ? 256 : 1024),
                                amdgpu_waves_per_eu(K == 1 && EPI != kEpiGatedNvfp4 &&
                                                            EPI != kEpiGatedNvfp4Lut ? 7 : 4)))
@@ -201,8 +203,8 @@ tail_kernel(TailParams p) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       gv[k] = ld16(gam + voff[k]);
-      xv[k] = ld16s<NT>(x + rb + voff[k]);
-      rv[k] = ld16s<NT>(res + rb + voff[k]);
+      xv[k] = ld16s<(NT != 0)>(x + rb + voff[k]);
+      rv[k] = ld16s<(NT != 0)>(res + rb + voff[k]);
     }
   }
   const float width_f = (float)p.hidden;  // row width (exact: <= 65536)
@@ -250,17 +252,20 @@ tail_kernel(TailParams p) {
   };
 
   // The epilogue of the lane's vector k of `row`: the norm output and the codes.
-  // Codes and block scales are stored without the streaming hint: their 8-,
-  // 4- and 1-byte stores only fill whole lines once merged in the L2, and
-  // hinting them measured ~5% slower on MI355X.
+  // Codes and linear block scales carry the streaming hint only with NT == 2
+  // (the host's choice for calls below 32 MiB of x): at large calls their 8-,
+  // 4- and 1-byte stores fill whole lines only once merged in the L2, and the
+  // hint measured 3-7% slower there. The swizzled scale words never take it.
+  // (A run-time flag choosing between a hinted and a plain store compiled to
+  // the plain store alone: the two stores were merged and the hint dropped.)
   auto emit = [&](int64_t row_, int k, const float (&n)[8]) {
     if constexpr (NORM) {
-      if (vok[k]) st16s<NT>(row_ptr<G>(nout, (size_t)row_ * row_bytes) + voff[k], pack8<DT>(n));
+      if (vok[k]) st16s<(NT != 0)>(row_ptr<G>(nout, (size_t)row_ * row_bytes) + voff[k], pack8<DT>(n));
     }
     if constexpr (EPI == kEpiFp8) {
       uint32_t lo, hi;
       fp8_codes8(n, sc, inv_sc, lo, hi);
-      if (vok[k]) st8s<false>(row_ptr<G>(p.q, (size_t)row_ * p.hidden) + voff[k] / 2, lo, hi);
+      if (vok[k]) st8s<NT == 2>(row_ptr<G>(p.q, (size_t)row_ * p.hidden) + voff[k] / 2, lo, hi);
     } else if constexpr (kNvfp4) {
       uint32_t w, sfc;
       nvfp4_half_block(n, sc, mult_tab, w, sfc);
@@ -278,11 +283,11 @@ tail_kernel(TailParams p) {
           st4s<false>(p.sf + sf_swizzled_offset(row_, (int32_t)(voff[k] / 32), p.sf_tiles), word);
       }
       if (vok[k]) {
-        st4s<false>(row_ptr<G>(p.q, (size_t)row_ * (p.hidden / 2)) + voff[k] / 4, w);
+        st4s<NT == 2>(row_ptr<G>(p.q, (size_t)row_ * (p.hidden / 2)) + voff[k] / 4, w);
         if constexpr (EPI != kEpiNvfp4Swz) {
           if ((lane & 1) == 0)  // linear [rows, width/16] (the plain and the gated variants)
-            st1s<false>(row_ptr<G>(p.sf, (size_t)row_ * (p.hidden / 16)) + voff[k] / 32,
-                        (uint8_t)sfc);
+            st1s<NT == 2>(row_ptr<G>(p.sf, (size_t)row_ * (p.hidden / 16)) + voff[k] / 32,
+                          (uint8_t)sfc);
         }
       }
     }
@@ -317,8 +322,8 @@ tail_kernel(TailParams p) {
         U4 xw[K], rw[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          xw[k] = ld16s<NT>(xrow + voff[k]);
-          rw[k] = ld16s<NT>(rrow + voff[k]);
+          xw[k] = ld16s<(NT != 0)>(xrow + voff[k]);
+          rw[k] = ld16s<(NT != 0)>(rrow + voff[k]);
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -328,7 +333,7 @@ tail_kernel(TailParams p) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) s[i] = xf[i] + rf[i];
           hv[k] = pack8<DT>(s);
-          if (vok[k]) st16s<NT>(rrow + voff[k], hv[k]);
+          if (vok[k]) st16s<(NT != 0)>(rrow + voff[k], hv[k]);
           unpack8<DT>(hv[k], h);
           double a = 0.0;  // vectors past the row end hold a clamped copy: not counted
 #pragma unroll
@@ -375,7 +380,7 @@ tail_kernel(TailParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) s[i] = xf[i] + rf[i];
         const U4 hv = pack8<DT>(s);
-        if (vok[k]) st16s<NT>(rrow + voff[k], hv);
+        if (vok[k]) st16s<(NT != 0)>(rrow + voff[k], hv);
         unpack8<DT>(hv, h[k]);
       }
       double a = 0.0;  // vectors past the row end hold a clamped copy: not counted
@@ -390,8 +395,8 @@ tail_kernel(TailParams p) {
       const uint8_t* rn = row_ptr<G>(res, (size_t)(row + 1) * row_bytes);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        xv[k] = ld16s<NT>(xn + voff[k]);
-        rv[k] = ld16s<NT>(rn + voff[k]);
+        xv[k] = ld16s<(NT != 0)>(xn + voff[k]);
+        rv[k] = ld16s<(NT != 0)>(rn + voff[k]);
       }
     }
 
@@ -426,7 +431,7 @@ tail_kernel(TailParams p) {
 
 // ---------------------------------------------------------------- dispatch
 
-template <int DT, int EPI, bool NORM, bool NT>
+template <int DT, int EPI, bool NORM, int NT>
 static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
   void* args[] = {const_cast<TailParams*>(&p)};
   const void* fn = nullptr;
@@ -456,7 +461,12 @@ static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
 
 template <int DT, int EPI, bool NORM>
 static hipError_t launch3(const TailParams& p, const Tiling& t, hipStream_t s) {
-  return t.stream ? launch4<DT, EPI, NORM, true>(p, t, s) : launch4<DT, EPI, NORM, false>(p, t, s);
+  if (!t.stream) return launch4<DT, EPI, NORM, 0>(p, t, s);
+  // the code-store hint exists for the plain FP8 and NVFP4 epilogues only
+  if constexpr (EPI == kEpiFp8 || EPI == kEpiNvfp4) {
+    if (t.stream_codes) return launch4<DT, EPI, NORM, 2>(p, t, s);
+  }
+  return launch4<DT, EPI, NORM, 1>(p, t, s);
 }
 
 template <int DT, int EPI>

@@ -39,6 +39,13 @@ bool env_stream(bool* stream) {
   return true;
 }
 
+bool env_stream_codes(bool* codes) {
+  int v = *codes ? 1 : 0;
+  if (!env_int("ANQ_STREAM_CODES", 0, 1, &v)) return false;
+  *codes = v == 1;
+  return true;
+}
+
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 
 // The tail kernels that exist: (group, vectors per lane) =
@@ -113,6 +120,14 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
   // already in cache, 0-5% slower.
   t.stream = (int64_t)vec * 16 * tokens >= ((int64_t)1 << 20);
   if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
+  // the hint on the code and linear scale stores too, for calls below 32 MiB
+  // of x: there the kernel's end waits on what its stores left dirty in the
+  // L2s. fp16 [64, 8192] NVFP4, 20-call graphs from HBM, after the first
+  // replay: 4.29 -> 3.95 us; bf16 [65536, 1024] FP8 and [8192, 7168] NVFP4
+  // measured 7% and 3% slower with it, and the swizzled scale words 28%
+  // slower at [64, 8192].
+  t.stream_codes = t.stream && !swizzled && (int64_t)vec * 16 * tokens < ((int64_t)32 << 20);
+  if (!env_stream_codes(&t.stream_codes)) return ANQ_ERR_CONFIG;
   finish_grid(tokens, groups_per_block, &t);
   *out = t;
   return ANQ_OK;
@@ -142,6 +157,8 @@ int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* out) {
   // 24.1, [1024, 8192] 16.4 -> 16.9)
   t.stream = (int64_t)vec * 16 * rows >= ((int64_t)1 << 20);
   if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
+  t.stream_codes = false;  // the gated calls are large: unhinted, as above
+  if (!env_stream_codes(&t.stream_codes)) return ANQ_ERR_CONFIG;
   finish_grid(rows, groups_per_block, &t);
   *out = t;
   return ANQ_OK;

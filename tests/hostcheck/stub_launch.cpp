@@ -54,9 +54,10 @@ int launch_tail(int dtype, int epi, bool norm_out, const TailParams& p, const Ti
                   p.vec * 8 == p.hidden && p.tokens > 0;
   return record(ok,
                 "kind=tail dtype=%d epi=%d norm=%d group=%d vec_per_lane=%d block=%d rows=%d "
-                "stream=%d grid=%lld tokens=%lld hidden=%d ok=%d",
+                "stream=%d stream_codes=%d grid=%lld tokens=%lld hidden=%d ok=%d",
                 dtype, epi, (int)norm_out, t.group, t.vec_per_lane, t.block, t.rows,
-                (int)t.stream, (long long)t.grid, (long long)p.tokens, p.hidden, (int)ok);
+                (int)t.stream, (int)t.stream_codes, (long long)t.grid, (long long)p.tokens,
+                p.hidden, (int)ok);
 }
 
 int launch_qk(int dtype, int store, const QKParams& p, const QKTiling& t, void* stream) {

@@ -24,8 +24,8 @@ import nvfp4_quantization_place_amd as A  # noqa: E402
 OK, CONFIG, LAUNCH = 0, 9, 7
 BASE = 1 << 40
 MB = 1 << 20
-ENV = ("ANQ_TAIL_TILING", "ANQ_ROWS_PER_GROUP", "ANQ_STREAM", "ANQ_GATE_LUT", "ANQ_GATE_BLOCK",
-       "ANQ_QK_WAVES", "ANQ_QK_GROUPS", "ANQ_QK_BLOCK")
+ENV = ("ANQ_TAIL_TILING", "ANQ_ROWS_PER_GROUP", "ANQ_STREAM", "ANQ_STREAM_CODES", "ANQ_GATE_LUT",
+       "ANQ_GATE_BLOCK", "ANQ_QK_WAVES", "ANQ_QK_GROUPS", "ANQ_QK_BLOCK")
 
 
 def addr(i):
@@ -71,12 +71,18 @@ def tail(L, op, tokens, hidden, dtype=1, norm=True):
 
 
 @pytest.mark.parametrize("tokens,hidden,want", [
-    (16, 128, dict(group="16", vec_per_lane="1", block="256", rows="1")),
-    (64, 8192, dict(group="0", vec_per_lane="1", block="1024", rows="1", stream="1")),
-    (65536, 1024, dict(group="0", vec_per_lane="1", block="128", rows="1", stream="1")),
-    (8192, 7168, dict(group="0", vec_per_lane="2", block="448", rows="1", stream="1")),
-    (1024, 7168, dict(group="0", vec_per_lane="1", block="896", rows="1", stream="1")),
-    (8192, 8192, dict(group="0", vec_per_lane="1", block="1024", rows="2", stream="1")),
+    (16, 128, dict(group="16", vec_per_lane="1", block="256", rows="1", stream="0",
+                   stream_codes="0")),
+    (64, 8192, dict(group="0", vec_per_lane="1", block="1024", rows="1", stream="1",
+                    stream_codes="1")),
+    (65536, 1024, dict(group="0", vec_per_lane="1", block="128", rows="1", stream="1",
+                       stream_codes="0")),
+    (8192, 7168, dict(group="0", vec_per_lane="2", block="448", rows="1", stream="1",
+                      stream_codes="0")),
+    (1024, 7168, dict(group="0", vec_per_lane="1", block="896", rows="1", stream="1",
+                      stream_codes="1")),
+    (8192, 8192, dict(group="0", vec_per_lane="1", block="1024", rows="2", stream="1",
+                      stream_codes="0")),
     (3, 65536, dict(group="0", vec_per_lane="8", block="1024")),
 ])
 def test_workload_tilings(L, tokens, hidden, want):
@@ -124,7 +130,8 @@ def test_bad_tiling_override_is_refused(L, value, monkeypatch):
 
 @pytest.mark.parametrize("name,value", [("ANQ_ROWS_PER_GROUP", "0"), ("ANQ_ROWS_PER_GROUP", "-2"),
                                         ("ANQ_ROWS_PER_GROUP", "two"), ("ANQ_STREAM", "2"),
-                                        ("ANQ_STREAM", "yes"), ("ANQ_GATE_LUT", "2"),
+                                        ("ANQ_STREAM", "yes"), ("ANQ_STREAM_CODES", "2"),
+                                        ("ANQ_GATE_LUT", "2"),
                                         ("ANQ_GATE_BLOCK", "96"), ("ANQ_GATE_BLOCK", "2048"),
                                         ("ANQ_QK_WAVES", "0"), ("ANQ_QK_GROUPS", "5"),
                                         ("ANQ_QK_BLOCK", "100"), ("ANQ_QK_BLOCK", "2048")])
@@ -148,6 +155,24 @@ def test_stream_override_is_taken(L, monkeypatch):
     assert tail(L, "fp8", 16, 128) == OK and last(L)["stream"] == "0"
     monkeypatch.setenv("ANQ_STREAM", "1")
     assert tail(L, "fp8", 16, 128) == OK and last(L)["stream"] == "1"
+
+
+def test_code_store_hint_policy_and_override(L, monkeypatch):
+    """The streaming hint on the code and scale stores: on for hinted calls
+    below 32 MiB of x with linear scales, off for larger calls, for the
+    swizzled layout and for unhinted calls; ANQ_STREAM_CODES overrides."""
+    assert tail(L, "nvfp4", 64, 8192) == OK and last(L)["stream_codes"] == "1"
+    assert tail(L, "fp8", 2047, 8192) == OK and last(L)["stream_codes"] == "1"   # 31.98 MiB
+    assert tail(L, "fp8", 2048, 8192) == OK and last(L)["stream_codes"] == "0"   # 32 MiB
+    assert tail(L, "swizzled", 64, 8192) == OK and last(L)["stream_codes"] == "0"
+    assert tail(L, "nvfp4", 16, 8192) == OK and last(L)["stream_codes"] == "0"   # unhinted
+    monkeypatch.setenv("ANQ_STREAM", "0")
+    assert tail(L, "nvfp4", 64, 8192) == OK and last(L)["stream_codes"] == "0"
+    monkeypatch.delenv("ANQ_STREAM")
+    monkeypatch.setenv("ANQ_STREAM_CODES", "0")
+    assert tail(L, "nvfp4", 64, 8192) == OK and last(L)["stream_codes"] == "0"
+    monkeypatch.setenv("ANQ_STREAM_CODES", "1")
+    assert tail(L, "fp8", 65536, 1024) == OK and last(L)["stream_codes"] == "1"
 
 
 def test_gated_table_choice(L, monkeypatch):
