@@ -122,10 +122,13 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
   if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
   // the hint on the code and linear scale stores too, for calls below 32 MiB
   // of x: there the kernel's end waits on what its stores left dirty in the
-  // L2s. fp16 [64, 8192] NVFP4, 20-call graphs from HBM, after the first
-  // replay: 4.29 -> 3.95 us; bf16 [65536, 1024] FP8 and [8192, 7168] NVFP4
-  // measured 7% and 3% slower with it, and the swizzled scale words 28%
-  // slower at [64, 8192].
+  // L2s. 20-call graphs from HBM, one box, off -> on: fp16 NVFP4 [64, 8192]
+  // 4.29 -> 4.08 us, [256, 8192] 4.96 -> 4.88, [1024, 8192] 11.95 -> 12.09,
+  // [2048, 8192] 21.2 -> 21.1; bf16 FP8 [256, 4096] 4.23 -> 3.93, [2048,
+  // 4096] 12.47 -> 12.08, [4096, 4096] 21.33 -> 21.49; bf16 NVFP4 + norm
+  // [1024, 7168] 14.37 -> 14.17, [2048, 7168] 24.16 -> 24.18, [4096, 7168]
+  // 43.5 -> 44.1. At [65536, 1024] FP8 and [8192, 7168] NVFP4 it measured 7%
+  // and 3% slower, and the swizzled scale words 28% slower at [64, 8192].
   t.stream_codes = t.stream && !swizzled && (int64_t)vec * 16 * tokens < ((int64_t)32 << 20);
   if (!env_stream_codes(&t.stream_codes)) return ANQ_ERR_CONFIG;
   finish_grid(tokens, groups_per_block, &t);
