@@ -107,7 +107,7 @@ extern "C" {
 /* Activation type T of a call. */
 typedef enum { ANQ_F16 = 0, ANQ_BF16 = 1 } anq_dtype;
 
-/* Status codes. ANQ_ERR_UNSUPPORTED is the "keep your separated path" answer
+/* Status codes. ANQ_ERR_UNSUPPORTED is the answer that leaves a call to a separated path
  * for valid arguments outside what the fused kernels cover. */
 enum {
   ANQ_OK = 0,
@@ -180,8 +180,8 @@ int add_rmsnorm_quant_nvfp4(const void* x, void* residual, const void* gamma,
  *   scale      device pointer to one binary32 s
  *   head_dim   one of 32, 64, 128, 256, 512
  *   rotary_dim a power of two from 16 to head_dim; other values (and other
- *              head_dim) return ANQ_ERR_UNSUPPORTED, the "keep a separated
- *              path" answer
+ *              head_dim) return ANQ_ERR_UNSUPPORTED, the answer that
+ *              leaves the call to a separated path
  *   nq, nk, nv >= 0, at least one head and at most 2^20 in all (ANQ_ERR_VALUE
  *              for a negative count, ANQ_ERR_SHAPE otherwise)
  *   out        [tokens, (nq+nk+nv)*D] uint8 E4M3 codes (output)
