@@ -66,7 +66,7 @@ CSRC = os.path.join(ROOT, "nvfp4_quantization_place_amd", "csrc")
 SPLIT_SHAPES = ((64, 8192), (128, 4096), (256, 2048), (512, 1024), (1024, 512))
 CPU_BUDGET_S = 1.5                     # oracle time per workload and mode (single, all cores)
 CPU_HEAD_BUDGET_S = 10.0               # the same for the workload the line reports
-MAX_CPU_PROCS = 16                     # a one-GPU machine's share of host cores
+MAX_CPU_PROCS = 16                     # worker processes at most: a host's cores per GPU
 
 
 # ---------------------------------------------------------------- byte counts
