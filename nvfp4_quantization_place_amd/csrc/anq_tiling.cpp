@@ -85,7 +85,7 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
     t.vec_per_lane = vec <= 1024 ? 1 : (vec <= 2048 ? 2 : (vec <= 4096 ? 4 : 8));
     // rows of 4104 to 8184 elements, many of them: two vectors per lane and
     // one row per workgroup. bf16 NVFP4 + norm output, inputs from HBM, same
-    // box: [8192, 7168] 85.8 -> 82.7 us, [4096, 7168] 47.6 -> 44.9, [16384,
+    // GPU: [8192, 7168] 85.8 -> 82.7 us, [4096, 7168] 47.6 -> 44.9, [16384,
     // 7168] 158.6 -> 157.4, [8192, 5120] 62.8 -> 61.1, [4096, 4608] 31.5 ->
     // 30.5, [8192, 6144] 71.6 -> 72.1 (the one loss). Not with the swizzled
     // scales: [8192, 7168] 84.1 -> 86.7 us.
@@ -122,7 +122,7 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
   if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
   // the hint on the code and linear scale stores too, for calls below 32 MiB
   // of x: there the kernel's end waits on what its stores left dirty in the
-  // L2s. 20-call graphs from HBM, one box, off -> on: fp16 NVFP4 [64, 8192]
+  // L2s. 20-call graphs from HBM, one GPU, off -> on: fp16 NVFP4 [64, 8192]
   // 4.29 -> 4.08 us, [256, 8192] 4.96 -> 4.88, [1024, 8192] 11.95 -> 12.09,
   // [2048, 8192] 21.2 -> 21.1; bf16 FP8 [256, 4096] 4.23 -> 3.93, [2048,
   // 4096] 12.47 -> 12.08, [4096, 4096] 21.33 -> 21.49; bf16 NVFP4 + norm
