@@ -44,6 +44,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -107,11 +108,26 @@ def rw_bytes(inp, kind: str = "fused", stored: int | None = None) -> tuple[int, 
     return 4 * n + 2 * H + 4, 2 * n + codes + (2 * n if inp.norm_out else 0)
 
 
+def _code_text(name: str, text: str) -> str:
+    """A source file's text without comments and with runs of whitespace
+    collapsed, so that editing a comment keeps measured counters valid."""
+    if name.endswith((".hip", ".h", ".cpp", ".c")):
+        text = re.sub(r"//[^\n]*|/\*.*?\*/", " ", text, flags=re.S)
+    elif name.endswith(".py"):
+        text = re.sub(r"#[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
+    """Hash of the kernel sources (comments and layout ignored): the counter
+    bytes of profiles/hbm_traffic.json apply only while it matches."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        path = os.path.join(CSRC, f)
+        if not os.path.isfile(path):
+            continue
+        with open(path, encoding="utf-8") as fh:
+            h.update(f.encode() + _code_text(f, fh.read()).encode())
     return h.hexdigest()[:16]
 
 
