@@ -4,8 +4,9 @@ Hidden sizes are drawn from all multiples of 16 up to 65536, so lane mappings,
 vector counts that are not multiples of a wavefront and ragged last vectors
 appear that a hand-picked grid can miss. Token counts are small (1-9, and up
 to 300 where the swizzled scale padding matters), and both input types and
-both epilogues occur. The Q/K op gets random head layouts and head sizes, and
-the gated op random group widths, with the bf16 gate table forced on for half
+both epilogues occur. The Q/K op gets random head layouts and head sizes (and
+random rotary widths through the mixed KV pool), and the gated op random group
+widths, with the bf16 gate table forced on for half
 of its cases. The seed is fixed, so every case is reproducible and named by
 its id.
 """
@@ -87,6 +88,48 @@ def test_random_qk_shapes(case):
     inp = W.make_qk(8000 + i, dtype, tokens, nq, nk, nv, head_dim,
                     positions=rng.integers(0, 97, tokens), max_pos=97, scale=0.04)
     np.testing.assert_array_equal(gpu_qk(inp), oracle_qk(inp))
+
+
+def _mixed_cases(n=24):
+    rng = np.random.default_rng(5151)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([32, 64, 128, 256, 512]))
+        R = int(rng.choice([r for r in (16, 32, 64, 128, 256, 512) if r <= D]))
+        nq, nk, nv = int(rng.integers(0, 6)), int(rng.integers(0, 4)), int(rng.integers(0, 4))
+        if nk + nv == 0:
+            nk = 1
+        out.append((i, ("f16", "bf16")[i % 2], int(rng.integers(1, 40)), nq, nk, nv, D, R))
+    return out
+
+
+@pytest.mark.parametrize("case", _mixed_cases(),
+                         ids=lambda c: f"{c[1]}-{c[2]}tok-{c[3]}.{c[4]}.{c[5]}x{c[6]}-rot{c[7]}")
+def test_random_qk_mixed_pool(case):
+    """Random head sizes, rotary widths and head layouts through the mixed
+    pool store, with padding and past-the-pool slots."""
+    i, dtype, tokens, nq, nk, nv, D, R = case
+    rng = np.random.default_rng(300 + i)
+    inp = W.make_qk(8500 + i, dtype, tokens, nq, nk, nv, D, positions=rng.integers(0, 97, tokens),
+                    max_pos=97, rotary_dim=R, scale=0.04)
+    num_slots = tokens + int(rng.integers(0, 8))
+    slots = rng.permutation(num_slots)[:tokens].astype(np.int64)
+    slots[rng.random(tokens) < 0.15] = -1
+    slots[rng.random(tokens) < 0.05] = num_slots + 3
+    A = _A()
+    width = A.mixed_kv_row_bytes(nk, nv, D, R)
+    pool = torch.full((num_slots, width), 0x5A, dtype=torch.uint8, device="cuda")
+    q = A.qk_norm_rope_kv_store_mixed(inp.qkv.cuda(), inp.gamma_q.cuda(), inp.gamma_k.cuda(),
+                                      inp.positions.cuda(), torch.from_numpy(inp.cos_sin).cuda(),
+                                      torch.tensor([inp.scale], device="cuda"), inp.eps, nq, nk,
+                                      nv, D, R, torch.from_numpy(slots).cuda(), pool)
+    torch.cuda.synchronize()
+    ref = O.qk_norm_rope_kv_store_mixed(W.bits(inp.qkv), W.bits(inp.gamma_q), W.bits(inp.gamma_k),
+                                        inp.positions.numpy(), inp.cos_sin, inp.scale, inp.eps, nq,
+                                        nk, nv, D, R, dtype, slots,
+                                        np.full((num_slots, width), 0x5A, np.uint8))
+    np.testing.assert_array_equal(_np(q), ref["q"])
+    np.testing.assert_array_equal(_np(pool), ref["kv"])
 
 
 def _gated_cases(n=24):
