@@ -360,26 +360,28 @@ class Workload:
             calls = self._calls = [self._make_call(j) for j in range(self.sets)]
         calls[i % self.sets]()
 
+    def prepared(self):
+        """The calls of every buffer set as prepared calls (the binding's
+        checks done once), or None where a call is two library calls."""
+        import nvfp4_quantization_place_amd as A
+        if self.kind == "separated":
+            return None
+        out = []
+        for j in range(self.sets):
+            fn, args, kw = self._spec(j)
+            out.append(A.prepare(fn, *args, **kw))
+        return out
+
     def _make_call(self, j: int):
         import functools
 
         import nvfp4_quantization_place_amd as A
-        inp, P = self.inp, functools.partial
-        if hasattr(self, "qkv"):
-            args = (self.qkv[j], self.gq, self.gk, self.pos, self.cs, self.scale, inp.eps, inp.nq,
-                    inp.nk, inp.nv, inp.head_dim)
-            if self.kind == "kv_mixed":
-                return P(A.qk_norm_rope_kv_store_mixed, *args, inp.rotary_dim, self.slots,
-                         self.pool[j], q_out=self.out[j])
-            if self.kind == "kv_store":
-                return P(A.qk_norm_rope_fp8_kv_store, *args, self.slots, self.pool[j],
-                         q_out=self.out[j], rotary_dim=inp.rotary_dim)
-            return P(A.qk_norm_rope_fp8, *args, rotary_dim=inp.rotary_dim, out=self.out[j])
-        x, res = self.x[j], self.res[j]
-        norm = self.norm[j] if self.norm is not None else None
-        q = self.q[j]
-        sf = self.sf[j] if self.sf is not None else None
         if self.kind == "separated":
+            inp = self.inp
+            x, res, q = self.x[j], self.res[j], self.q[j]
+            norm = self.norm[j]
+            sf = self.sf[j] if self.sf is not None else None
+
             def sep():
                 n = A.add_rmsnorm(x, res, self.g, inp.eps, norm=norm)
                 if inp.op == "fp8":
@@ -387,16 +389,36 @@ class Workload:
                 else:
                     A.quant_nvfp4(n, self.scale, q=q, sf=sf)
             return sep
+        fn, args, kw = self._spec(j)
+        return functools.partial(fn, *args, **kw)
+
+    def _spec(self, j: int):
+        """(op, args, kwargs) of the one binding call on buffer set j."""
+        import nvfp4_quantization_place_amd as A
+        inp = self.inp
+        if hasattr(self, "qkv"):
+            args = (self.qkv[j], self.gq, self.gk, self.pos, self.cs, self.scale, inp.eps, inp.nq,
+                    inp.nk, inp.nv, inp.head_dim)
+            if self.kind == "kv_mixed":
+                return (A.qk_norm_rope_kv_store_mixed, args + (inp.rotary_dim, self.slots,
+                                                               self.pool[j]),
+                        dict(q_out=self.out[j]))
+            if self.kind == "kv_store":
+                return (A.qk_norm_rope_fp8_kv_store, args + (self.slots, self.pool[j]),
+                        dict(q_out=self.out[j], rotary_dim=inp.rotary_dim))
+            return A.qk_norm_rope_fp8, args, dict(rotary_dim=inp.rotary_dim, out=self.out[j])
+        x, res = self.x[j], self.res[j]
+        norm = self.norm[j] if self.norm is not None else None
+        q = self.q[j]
+        sf = self.sf[j] if self.sf is not None else None
+        base = (x, res, self.g, self.scale, inp.eps)
         if self.kind == "swizzled":
-            return P(A.add_rmsnorm_quant_nvfp4_swizzled, x, res, self.g, self.scale, inp.eps, q=q,
-                     sf=sf, norm=norm)
+            return A.add_rmsnorm_quant_nvfp4_swizzled, base, dict(q=q, sf=sf, norm=norm)
         if inp.op == "gated":
-            return P(A.gated_rmsnorm_quant_nvfp4, x, res, self.g, self.scale, inp.eps,
-                     group=inp.meta["group"], q=q, sf=sf)
+            return A.gated_rmsnorm_quant_nvfp4, base, dict(group=inp.meta["group"], q=q, sf=sf)
         if inp.op == "fp8":
-            return P(A.add_rmsnorm_quant_fp8, x, res, self.g, self.scale, inp.eps, q=q, norm=norm)
-        return P(A.add_rmsnorm_quant_nvfp4, x, res, self.g, self.scale, inp.eps, q=q, sf=sf,
-                 norm=norm)
+            return A.add_rmsnorm_quant_fp8, base, dict(q=q, norm=norm)
+        return A.add_rmsnorm_quant_nvfp4, base, dict(q=q, sf=sf, norm=norm)
 
 
 class StreamCalib:
@@ -437,13 +459,24 @@ def time_workload(w, steps: int, warmup: int, eager: bool = True, spread: bool =
     for i in range(warmup):
         w.call(i)
     torch.cuda.synchronize()
-    eager_us = None
-    if eager:  # host-launched calls, wall clock
+    eager_us = prepared_us = None
+    if eager:  # host-launched calls, wall clock: through the binding, then prepared calls
         t0 = time.perf_counter()
         for i in range(steps):
             w.call(i)
         torch.cuda.synchronize()
         eager_us = round((time.perf_counter() - t0) / steps * 1e6, 3)
+        prep = w.prepared() if hasattr(w, "prepared") else None
+        if prep:
+            for i in range(min(steps, 5)):
+                prep[i % len(prep)]()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                prep[i % len(prep)]()
+            torch.cuda.synchronize()
+            prepared_us = round((time.perf_counter() - t0) / steps * 1e6, 3)
+            del prep
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -511,6 +544,7 @@ def time_workload(w, steps: int, warmup: int, eager: bool = True, spread: bool =
              rotating_bytes=w.sets * w.bytes, graphs=n_graphs, calls_per_graph=steps,
              flush_bytes=FLUSH_BYTES if flush is not None else 0,
              us_per_call=round(dev_us, 3), eager_us_per_call=eager_us,
+             eager_prepared_us_per_call=prepared_us,
              wall_ms_timed=round(wall_s * 1e3, 3), gbs=round(gbs, 1),
              frac_of_peak=round(gbs / PEAK_GBS, 4))
     if not spread:
@@ -757,6 +791,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": head["workload"], "io_dtype": head["io_dtype"],
                    "us_per_call": head["us_per_call"], "eager_us_per_call": head["eager_us_per_call"],
+                   "eager_prepared_us_per_call": head["eager_prepared_us_per_call"],
                    "bytes_per_call": head["bytes_per_call"], "spread_us": head.get("spread_us"),
                    "hot_us_per_call": head.get("hot_us_per_call"),
                    "rotating_sets": head["rotating_sets"], "rotating_bytes": head["rotating_bytes"],

@@ -20,7 +20,8 @@ __all__ = ["add_rmsnorm_quant_fp8", "add_rmsnorm_quant_nvfp4", "qk_norm_rope_fp8
            "add_rmsnorm_quant_nvfp4_swizzled",
            "gated_rmsnorm_quant_nvfp4", "silu_gate_f32",
            "quant_nvfp4_swizzled", "nvfp4_swizzled_sf_shape", "add_rmsnorm", "quant_fp8", "quant_nvfp4",
-           "nvfp4_shape", "status_string", "selfcheck_arith", "stream_rw", "lib", "AnqError",
+           "nvfp4_shape", "status_string", "selfcheck_arith", "stream_rw", "prepare", "Prepared",
+           "lib", "AnqError",
            "LIB_PATH", "ANQ_F16", "ANQ_BF16", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaddnormq.so")
@@ -159,6 +160,67 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+# While prepare() runs an op, the op's one library call is recorded here
+# instead of made.
+_record = None
+
+
+def _call(name: str, *args) -> int:
+    if _record is not None:
+        _record.append((name, args))
+        return 0
+    return getattr(lib(), name)(*args)
+
+
+class Prepared:
+    """One op's library call with its arguments fixed: the checks of the
+    Python binding ran once when it was prepared, and each call of this
+    object makes the library call alone (which still validates its arguments
+    on the host and enqueues the kernel). It holds its tensors, so their
+    memory stays valid; the results land in the same output tensors
+    (`outputs`, what the op returned) at every call, computed from the
+    inputs' contents at that time. Without an explicit stream it enqueues on
+    the current stream at each call. The tensors it holds must keep their
+    storage (no resize_ or set_ on them)."""
+
+    __slots__ = ("name", "outputs", "_fn", "_args", "_dev", "_current", "_keep")
+
+    def __call__(self):
+        args = self._args
+        if self._current:
+            args = args[:-1] + (_stream(self._dev, None),)
+        st = self._fn(*args)
+        if st:
+            raise AnqError(self.name, st)
+        return self.outputs
+
+
+def prepare(op, *args, **kwargs) -> Prepared:
+    """Run op(*args, **kwargs) through the binding's checks without launching
+    it, and return the Prepared call that launches it. For loops that call
+    one op on fixed buffers: each call then skips the per-call tensor checks
+    of the binding. Output tensors the op would allocate are allocated here
+    once; pass them in to reuse buffers of your own. Not thread-safe: prepare
+    from one thread at a time."""
+    global _record
+    rec = []
+    _record = rec
+    try:
+        outputs = op(*args, **kwargs)
+    finally:
+        _record = None
+    if len(rec) != 1:
+        raise ValueError(f"{getattr(op, '__name__', op)} does not make exactly one library call")
+    name, cargs = rec[0]
+    p = Prepared()
+    p.name, p.outputs, p._fn, p._args = name, outputs, getattr(lib(), name), cargs
+    tensors = [a for a in list(args) + list(kwargs.values()) if isinstance(a, torch.Tensor)]
+    p._dev = tensors[0].get_device() if tensors else torch.cuda.current_device()
+    p._current = kwargs.get("stream") is None
+    p._keep = (args, kwargs, outputs)
+    return p
+
+
 def _rows(x: torch.Tensor) -> tuple[int, int]:
     hidden = x.shape[-1]
     return (x.numel() // hidden if hidden else 0), hidden
@@ -220,7 +282,7 @@ def add_rmsnorm_quant_fp8(x, residual, gamma, scale, eps: float, norm_out: bool 
         q = torch.empty(x.shape, dtype=torch.uint8, device=dev)
     if norm_out and norm is None:
         norm = torch.empty_like(x)
-    st = lib().add_rmsnorm_quant_fp8(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(scale), eps,
+    st = _call("add_rmsnorm_quant_fp8", _ptr(x), _ptr(residual), _ptr(gamma), _ptr(scale), eps,
                                      tokens, hidden, _dtype_code(x), _ptr(q), _ptr(norm),
                                      _stream(dev, stream))
     if st:
@@ -239,7 +301,7 @@ def add_rmsnorm_quant_nvfp4(x, residual, gamma, global_scale, eps: float, norm_o
     q, sf = _nvfp4_outs(q, sf, x.shape[:-1], tokens, hidden, dev)
     if norm_out and norm is None:
         norm = torch.empty_like(x)
-    st = lib().add_rmsnorm_quant_nvfp4(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(global_scale),
+    st = _call("add_rmsnorm_quant_nvfp4", _ptr(x), _ptr(residual), _ptr(gamma), _ptr(global_scale),
                                        eps, tokens, hidden, _dtype_code(x), _ptr(q), _ptr(sf),
                                        _ptr(norm), _stream(dev, stream))
     if st:
@@ -282,7 +344,7 @@ def qk_norm_rope_fp8(qkv, gamma_q, gamma_k, positions, cos_sin, scale, eps: floa
     _need(out, qkv.numel(), torch.uint8, "out")
     if out is None:
         out = torch.empty(qkv.shape, dtype=torch.uint8, device=dev)
-    st = lib().qk_norm_rope_fp8(_ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), _ptr(positions),
+    st = _call("qk_norm_rope_fp8", _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), _ptr(positions),
                                 _ptr(cos_sin), cos_sin.shape[0], _ptr(scale), eps, tokens, nq, nk,
                                 nv, head_dim, rot, _dtype_code(qkv), _ptr(out),
                                 _stream(dev, stream))
@@ -308,7 +370,7 @@ def _qk_store(fn_name, kv_cols, qkv, gamma_q, gamma_k, positions, cos_sin, scale
     _need(q_out, tokens * nq * head_dim, torch.uint8, "q_out")
     if q_out is None:
         q_out = torch.empty(*qkv.shape[:-1], nq * head_dim, dtype=torch.uint8, device=dev)
-    st = getattr(lib(), fn_name)(
+    st = _call(fn_name, 
         _ptr(qkv), _ptr(gamma_q), _ptr(gamma_k), _ptr(positions), _ptr(cos_sin), cos_sin.shape[0],
         _ptr(scale), eps, tokens, nq, nk, nv, head_dim, rot, _dtype_code(qkv), _ptr(slot_mapping),
         num_slots, _ptr(q_out) if q_out.numel() else None,
@@ -359,7 +421,7 @@ def add_rmsnorm(x, residual, gamma, eps: float, norm=None, stream=None):
     tokens, hidden = _tail_shapes(x, residual, gamma, norm)
     if norm is None:
         norm = torch.empty_like(x)
-    st = lib().add_rmsnorm(_ptr(x), _ptr(residual), _ptr(gamma), eps, tokens, hidden,
+    st = _call("add_rmsnorm", _ptr(x), _ptr(residual), _ptr(gamma), eps, tokens, hidden,
                            _dtype_code(x), _ptr(norm), _stream(dev, stream))
     if st:
         raise AnqError("add_rmsnorm", st)
@@ -374,7 +436,7 @@ def quant_fp8(t, scale, q=None, stream=None):
     _need(q, t.numel(), torch.uint8, "q")
     if q is None:
         q = torch.empty(t.shape, dtype=torch.uint8, device=dev)
-    st = lib().quant_fp8(_ptr(t), _ptr(scale), tokens, hidden, _dtype_code(t), _ptr(q),
+    st = _call("quant_fp8", _ptr(t), _ptr(scale), tokens, hidden, _dtype_code(t), _ptr(q),
                          _stream(dev, stream))
     if st:
         raise AnqError("quant_fp8", st)
@@ -387,7 +449,7 @@ def quant_nvfp4(t, global_scale, q=None, sf=None, stream=None):
     _scalar(global_scale, "global_scale")
     tokens, hidden = _rows(t)
     q, sf = _nvfp4_outs(q, sf, t.shape[:-1], tokens, hidden, dev)
-    st = lib().quant_nvfp4(_ptr(t), _ptr(global_scale), tokens, hidden, _dtype_code(t), _ptr(q),
+    st = _call("quant_nvfp4", _ptr(t), _ptr(global_scale), tokens, hidden, _dtype_code(t), _ptr(q),
                            _ptr(sf), _stream(dev, stream))
     if st:
         raise AnqError("quant_nvfp4", st)
@@ -408,7 +470,7 @@ def add_rmsnorm_quant_nvfp4_swizzled(x, residual, gamma, global_scale, eps: floa
     q, sf = _nvfp4_outs(q, sf, x.shape[:-1], tokens, hidden, dev, swizzled=True)
     if norm_out and norm is None:
         norm = torch.empty_like(x)
-    st = lib().add_rmsnorm_quant_nvfp4_swizzled(
+    st = _call("add_rmsnorm_quant_nvfp4_swizzled", 
         _ptr(x), _ptr(residual), _ptr(gamma), _ptr(global_scale), eps, tokens, hidden,
         _dtype_code(x), _ptr(q), _ptr(sf), _ptr(norm), _stream(dev, stream))
     if st:
@@ -422,7 +484,7 @@ def quant_nvfp4_swizzled(t, global_scale, q=None, sf=None, stream=None):
     _scalar(global_scale, "global_scale")
     tokens, hidden = _rows(t)
     q, sf = _nvfp4_outs(q, sf, t.shape[:-1], tokens, hidden, dev, swizzled=True)
-    st = lib().quant_nvfp4_swizzled(_ptr(t), _ptr(global_scale), tokens, hidden, _dtype_code(t),
+    st = _call("quant_nvfp4_swizzled", _ptr(t), _ptr(global_scale), tokens, hidden, _dtype_code(t),
                                     _ptr(q), _ptr(sf), _stream(dev, stream))
     if st:
         raise AnqError("quant_nvfp4_swizzled", st)
@@ -441,7 +503,7 @@ def gated_rmsnorm_quant_nvfp4(x, z, gamma, global_scale, eps: float, group: int 
     tokens, hidden = _tail_shapes(x, z, gamma, None, other="z")
     q, sf = _nvfp4_outs(q, sf, x.shape[:-1], tokens, hidden, dev)
     group = hidden if group is None else group
-    st = lib().gated_rmsnorm_quant_nvfp4(_ptr(x), _ptr(z), _ptr(gamma), _ptr(global_scale), eps,
+    st = _call("gated_rmsnorm_quant_nvfp4", _ptr(x), _ptr(z), _ptr(gamma), _ptr(global_scale), eps,
                                          tokens, hidden, group, _dtype_code(x), _ptr(q), _ptr(sf),
                                          _stream(dev, stream))
     if st:
@@ -472,7 +534,7 @@ def silu_gate_f32(x, z, u=None, stream=None):
     _need(u, x.numel(), torch.float32, "u")
     if u is None:
         u = torch.empty(x.shape, dtype=torch.float32, device=dev)
-    st = lib().silu_gate_f32(_ptr(x), _ptr(z), x.numel(), _dtype_code(x), _ptr(u),
+    st = _call("silu_gate_f32", _ptr(x), _ptr(z), x.numel(), _dtype_code(x), _ptr(u),
                              _stream(dev, stream))
     if st:
         raise AnqError("silu_gate_f32", st)
@@ -489,7 +551,7 @@ def stream_rw(src, read_bytes: int, dst, write_bytes: int, nontemporal: bool = T
         raise ValueError("src and dst must be uint8")
     if src.numel() < read_bytes or dst.numel() < write_bytes:
         raise ValueError("src / dst smaller than the bytes asked for")
-    st = lib().anq_stream_rw(_ptr(src), read_bytes, _ptr(dst), write_bytes, int(nontemporal),
+    st = _call("anq_stream_rw", _ptr(src), read_bytes, _ptr(dst), write_bytes, int(nontemporal),
                              _stream(dev, stream))
     if st:
         raise AnqError("anq_stream_rw", st)

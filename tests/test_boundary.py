@@ -429,3 +429,8 @@ def test_product_fails_loudly_without_library_or_gpu(monkeypatch):
                                   torch.ones(1), 1e-6)
     with pytest.raises(ValueError, match="GPU"):
         A.quant_fp8(x, torch.ones(1))
+    # prepare() runs the same checks and leaves no recording behind
+    with pytest.raises(ValueError, match="GPU"):
+        A.prepare(A.add_rmsnorm_quant_nvfp4, x, x.clone(), torch.ones(64, dtype=torch.bfloat16),
+                  torch.ones(1), 1e-6)
+    assert A._record is None
