@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import functools
+import inspect
 import os
 
 import torch  # loads the HIP runtime the library binds to
@@ -216,7 +217,11 @@ def prepare(op, *args, **kwargs) -> Prepared:
     p.name, p.outputs, p._fn, p._args = name, outputs, getattr(lib(), name), cargs
     tensors = [a for a in list(args) + list(kwargs.values()) if isinstance(a, torch.Tensor)]
     p._dev = tensors[0].get_device() if tensors else torch.cuda.current_device()
-    p._current = kwargs.get("stream") is None
+    try:  # the stream argument however it was passed
+        given = inspect.signature(op).bind(*args, **kwargs).arguments.get("stream")
+    except (TypeError, ValueError):
+        given = kwargs.get("stream")
+    p._current = given is None
     p._keep = (args, kwargs, outputs)
     return p
 

@@ -111,3 +111,19 @@ def test_bad_arguments_fail_at_prepare_time():
     assert e.value.code == 8
     torch.cuda.synchronize()
     assert np.array_equal(_np(r), before)
+
+
+def test_prepared_with_an_explicit_stream_keeps_it():
+    A = _A()
+    (x, r, g), (x2, r2, g2) = _tail_pair(35, "f16", 8, 2048)
+    s = torch.tensor([300.0], device="cuda")
+    side = torch.cuda.Stream()
+    call = A.prepare(A.add_rmsnorm_quant_nvfp4, x2, r2, g2, s, 1e-6, stream=side)
+    assert not call._current
+    side.wait_stream(torch.cuda.current_stream())
+    q2, sf2, _ = call()                  # on `side`, whatever the current stream is
+    side.synchronize()
+    q, sf, _ = A.add_rmsnorm_quant_nvfp4(x, r, g, s, 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(q), _np(q2)) and np.array_equal(_np(sf), _np(sf2))
+    assert np.array_equal(_np(r), _np(r2))
