@@ -63,10 +63,9 @@
  *    so a producer kernel on the same stream may write them.
  *  - Arguments are validated on the host before any HIP call. A rejected call
  *    returns a nonzero status and enqueues nothing. The ANQ_* environment
- *    variables (ANQ_TAIL_TILING, ANQ_ROWS_PER_GROUP, ANQ_STREAM,
+ *    variables (ANQ_TAIL_TILING, ANQ_ROWS_PER_GROUP, ANQ_ROW_ORDER, ANQ_STREAM,
  *    ANQ_STREAM_CODES, ANQ_GATE_LUT, ANQ_GATE_BLOCK, ANQ_QK_WAVES, ANQ_QK_GROUPS,
- *    ANQ_QK_BLOCK) override the
- *    tiling for sweeps; a value the library has no kernel for is refused with
+ *    ANQ_QK_BLOCK) override the tiling for sweeps; a value the library has no kernel for is refused with
  *    ANQ_ERR_CONFIG, never replaced by a default. Every accepted tiling gives
  *    bit-identical results. tokens == 0 returns ANQ_OK
  *    and enqueues nothing; the token-sized buffers (x, z, residual, q, sf,

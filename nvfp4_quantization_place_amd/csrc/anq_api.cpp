@@ -90,6 +90,7 @@ extern "C" int add_rmsnorm_quant_fp8(const void* x, void* residual, const void* 
   anq::Tiling t;
   if ((st = anq::pick_tail_tiling(p.vec, tokens, false, &t)) != ANQ_OK) return st;
   p.rows_per_group = t.rows;
+  p.interleave = t.interleave ? 1 : 0;
   return launch_status(anq::launch_tail(dtype, anq::kEpiFp8, norm_out != nullptr, p, t, stream));
 }
 
@@ -134,6 +135,7 @@ int rmsnorm_nvfp4(const void* x, void* residual, const void* gamma, const float*
   anq::Tiling t;
   if ((st = anq::pick_tail_tiling(p.vec, tokens, swizzled, &t)) != ANQ_OK) return st;
   p.rows_per_group = t.rows;
+  p.interleave = t.interleave ? 1 : 0;
   return launch_status(anq::launch_tail(dtype, swizzled ? anq::kEpiNvfp4Swz : anq::kEpiNvfp4,
                                         norm_out != nullptr, p, t, stream));
 }
@@ -206,6 +208,7 @@ extern "C" int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const voi
                      : anq::pick_tail_tiling(p.vec, p.tokens, false, &t);
   if (st != ANQ_OK) return st;
   p.rows_per_group = t.rows;
+  p.interleave = t.interleave ? 1 : 0;
   return launch_status(anq::launch_tail(dtype, lut ? anq::kEpiGatedNvfp4Lut : anq::kEpiGatedNvfp4,
                                         false, p, t, stream));
 }
@@ -406,6 +409,7 @@ extern "C" int add_rmsnorm(const void* x, void* residual, const void* gamma, flo
   const int st = anq::pick_tail_tiling(p.vec, tokens, false, &t);
   if (st != ANQ_OK) return st;
   p.rows_per_group = t.rows;
+  p.interleave = t.interleave ? 1 : 0;
   return launch_status(anq::launch_tail(dtype, anq::kEpiNone, true, p, t, stream));
 }
 

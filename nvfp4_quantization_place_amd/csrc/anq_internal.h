@@ -40,6 +40,7 @@ struct TailParams {
   int32_t hidden;
   int32_t vec;         // hidden / 8: 16-byte vectors per row
   int32_t rows_per_group;  // consecutive rows each lane group processes
+  int32_t interleave;   // 1: lane group i takes rows i, i + groups, ... instead
   int32_t sf_tiles;    // swizzled NVFP4 scales: 128x4 tiles per tile row
   int32_t gamma_period;  // gated: groups per token; row r uses gamma slice r % period
 };
@@ -54,6 +55,7 @@ struct Tiling {
   int vec_per_lane;
   int block;
   int rows;
+  bool interleave;    // rows in grid-stride order (rows_per_group unused)
   bool stream;        // non-temporal loads and stores of the row streams
   bool stream_codes;  // the same hint on the code and linear block-scale stores
                       // (plain FP8 and NVFP4 epilogues)

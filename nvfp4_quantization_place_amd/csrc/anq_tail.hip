@@ -162,8 +162,20 @@ tail_kernel(TailParams p) {
     L = blockDim.x;
     group = blockIdx.x;
   }
-  int64_t row = group * p.rows_per_group;
-  const int64_t row_end = row + p.rows_per_group < p.tokens ? row + p.rows_per_group : p.tokens;
+  // consecutive: rows [group * rows_per_group, + rows_per_group); interleaved:
+  // rows group, group + groups, ... (so the rows in flight across the GPU at
+  // any time are one contiguous window of the tensor)
+  const int64_t groups = G > 0 ? (int64_t)gridDim.x * (blockDim.x / G) : (int64_t)gridDim.x;
+  int64_t row, row_end, step;
+  if (p.interleave) {
+    row = group;
+    step = groups;
+    row_end = p.tokens;
+  } else {
+    row = group * p.rows_per_group;
+    step = 1;
+    row_end = row + p.rows_per_group < p.tokens ? row + p.rows_per_group : p.tokens;
+  }
   const int64_t last = p.tokens - 1;
 
   const uint8_t* x = static_cast<const uint8_t*>(p.x);
@@ -297,7 +309,9 @@ tail_kernel(TailParams p) {
   // gated: the gamma slice of the row, row % gamma_period, kept as a running
   // counter (one modulo for the first row, none per row)
   int32_t gslice = kGated && p.gamma_period > 1 ? (int32_t)(row % p.gamma_period) : 0;
-  for (; row < row_end; ++row, parity ^= 1, gslice = gslice + 1 == p.gamma_period ? 0 : gslice + 1) {
+  const int32_t gstep = kGated && p.gamma_period > 1 ? (int32_t)(step % p.gamma_period) : 0;
+  for (; row < row_end; row += step, parity ^= 1,
+                        gslice = gslice + gstep >= p.gamma_period ? gslice + gstep - p.gamma_period : gslice + gstep) {
     uint8_t* rrow = row_ptr<G>(res, (size_t)row * row_bytes);
     // the rare double-double pass re-reads the lane's own just-stored residual
     // elements (the gated variant recomputes u from x and z below)
@@ -390,9 +404,9 @@ tail_kernel(TailParams p) {
     }
     // Prefetch this group's next row into the registers just freed; it lands
     // while this row is reduced, normalised and stored.
-    if (row + 1 < row_end) {
-      const uint8_t* xn = row_ptr<G>(x, (size_t)(row + 1) * row_bytes);
-      const uint8_t* rn = row_ptr<G>(res, (size_t)(row + 1) * row_bytes);
+    if (row + step < row_end) {
+      const uint8_t* xn = row_ptr<G>(x, (size_t)(row + step) * row_bytes);
+      const uint8_t* rn = row_ptr<G>(res, (size_t)(row + step) * row_bytes);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         xv[k] = ld16s<(NT != 0)>(xn + voff[k]);
@@ -424,7 +438,6 @@ tail_kernel(TailParams p) {
     }
   }
   if constexpr (EPI == kEpiNvfp4Swz) {  // lane groups share the padded rows
-    const int64_t groups = G > 0 ? (int64_t)gridDim.x * (blockDim.x / G) : (int64_t)gridDim.x;
     zero_padded_scale_rows(p.sf, p.tokens, p.sf_tiles, group, groups, lane, L);
   }
 }

@@ -39,6 +39,13 @@ bool env_stream(bool* stream) {
   return true;
 }
 
+bool env_interleave(bool* il) {
+  int v = *il ? 1 : 0;
+  if (!env_int("ANQ_ROW_ORDER", 0, 1, &v)) return false;
+  *il = v == 1;
+  return true;
+}
+
 bool env_stream_codes(bool* codes) {
   int v = *codes ? 1 : 0;
   if (!env_int("ANQ_STREAM_CODES", 0, 1, &v)) return false;
@@ -131,6 +138,7 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
   // and 3% slower, and the swizzled scale words 28% slower at [64, 8192].
   t.stream_codes = t.stream && !swizzled && (int64_t)vec * 16 * tokens < ((int64_t)32 << 20);
   if (!env_stream_codes(&t.stream_codes)) return ANQ_ERR_CONFIG;
+  if (!env_interleave(&t.interleave)) return ANQ_ERR_CONFIG;
   finish_grid(tokens, groups_per_block, &t);
   *out = t;
   return ANQ_OK;
@@ -138,13 +146,19 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
 
 // Tiling of the gated variant with the gate table (rows <= 1024 elements):
 // lane groups of 16/32/64 lanes, one or two vectors per lane, in 512-lane
-// workgroups (one 32 KiB table per 8 wavefronts), each lane group walking
-// enough consecutive rows that about 512 workgroups cover the call, so each
-// workgroup copies its table once for many rows. On the gated workload
-// (bf16 [8192, 8192], groups of 1024) 512-lane workgroups with 16 rows per
-// group measured 66.8 us against 67.8 with 256 lanes (320 and 384 lanes:
-// 74-85). ANQ_GATE_BLOCK (a multiple of 64, 64 to 1024), ANQ_ROWS_PER_GROUP
-// and ANQ_STREAM override.
+// workgroups (one 32 KiB table per 8 wavefronts), each lane group taking
+// enough rows that about 512 workgroups cover the call (1024 once that still
+// leaves 8 or more rows per group), so each workgroup copies its table once
+// for many rows. The rows are interleaved: lane group i takes rows i, i +
+// groups, ..., so the rows in flight across the GPU form one window that
+// sweeps the tensor. bf16, inputs from HBM, one GPU, consecutive ->
+// interleaved rows (512 workgroups): [2048, 8192] groups of 1024 22.0 -> 18.7
+// us, [4096, 8192] 37.7 -> 33.0, [16384, 8192] 136.1 -> 119.9, [8192, 4096]
+// groups of 128 36.1 -> 34.0; then 1024 workgroups at [8192, 8192] groups of
+// 1024 66.1 -> 63.9, of 512 63.2 -> 59.9, [8192, 4096] groups of 128 34.3 ->
+// 32.3. 256 and 1024 lanes per workgroup measured no better (320, 384, 768:
+// 74-85 us). ANQ_GATE_BLOCK (a multiple of 64, 64 to 1024),
+// ANQ_ROWS_PER_GROUP, ANQ_ROW_ORDER and ANQ_STREAM override.
 int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* out) {
   Tiling t{};
   t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
@@ -153,7 +167,9 @@ int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* out) {
   if (!env_int("ANQ_GATE_BLOCK", 64, 1024, &t.block) || t.block % 64 != 0) return ANQ_ERR_CONFIG;
   const int64_t groups_per_block = t.block / t.group;
   int64_t r = rows / (groups_per_block * 512);
+  if (r >= 16) r /= 2;
   t.rows = (int)(r < 1 ? 1 : (r > 64 ? 64 : r));
+  t.interleave = true;
   if (!env_int("ANQ_ROWS_PER_GROUP", 1, 1 << 20, &t.rows)) return ANQ_ERR_CONFIG;
   // streaming hints from 1 MiB of x, as in the tail tiling (bf16 groups of
   // 1024, inputs from HBM: [2048, 1024] 6.33 -> 6.04 us, [2048, 8192] 25.6 ->
@@ -162,6 +178,7 @@ int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* out) {
   if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
   t.stream_codes = false;  // the gated calls are large: unhinted, as above
   if (!env_stream_codes(&t.stream_codes)) return ANQ_ERR_CONFIG;
+  if (!env_interleave(&t.interleave)) return ANQ_ERR_CONFIG;
   finish_grid(rows, groups_per_block, &t);
   *out = t;
   return ANQ_OK;

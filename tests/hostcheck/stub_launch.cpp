@@ -49,14 +49,15 @@ int launch_tail(int dtype, int epi, bool norm_out, const TailParams& p, const Ti
                   lanes_per_row * t.vec_per_lane >= p.vec &&
                   (t.group > 0 || (int64_t)t.block - 64 < (p.vec + t.vec_per_lane - 1) / t.vec_per_lane) &&
                   t.rows == p.rows_per_group && t.rows >= 1 && t.grid >= 1 &&
+                  p.interleave == (t.interleave ? 1 : 0) &&
                   t.grid <= 0x7FFFFFFF && t.grid * groups_per_block * t.rows >= p.tokens &&
                   (t.grid - 1) * groups_per_block * t.rows < p.tokens &&
                   p.vec * 8 == p.hidden && p.tokens > 0;
   return record(ok,
                 "kind=tail dtype=%d epi=%d norm=%d group=%d vec_per_lane=%d block=%d rows=%d "
-                "stream=%d stream_codes=%d grid=%lld tokens=%lld hidden=%d ok=%d",
+                "interleave=%d stream=%d stream_codes=%d grid=%lld tokens=%lld hidden=%d ok=%d",
                 dtype, epi, (int)norm_out, t.group, t.vec_per_lane, t.block, t.rows,
-                (int)t.stream, (int)t.stream_codes, (long long)t.grid, (long long)p.tokens,
+                (int)t.interleave, (int)t.stream, (int)t.stream_codes, (long long)t.grid, (long long)p.tokens,
                 p.hidden, (int)ok);
 }
 

@@ -92,12 +92,15 @@ def test_gated_matches_oracle(tokens, hidden, group, dtype):
     (128, "16:1", "1", "0"), (256, "32:1", "2", "1"), (256, "64:1", "3", "0"),
     (256, "64:2", "2", "1"), (256, "0:1", "1", "1"), (256, "0:2", "4", "0"),
     (128, "32:1", "5", "1")])
-def test_gated_every_tiling(group, tiling, rows, stream, monkeypatch):
-    """Groups over rows of 1024: the per-group gamma slice, the lane mapping
-    and the streaming hints change no bit (each override names a tiling that
-    exists for the group width)."""
+@pytest.mark.parametrize("order", ["0", "1"])
+def test_gated_every_tiling(group, tiling, rows, stream, order, monkeypatch):
+    """Groups over rows of 1024: the per-group gamma slice (also when a lane
+    group's rows are interleaved, a whole grid of groups apart), the lane
+    mapping and the streaming hints change no bit (each override names a
+    tiling that exists for the group width)."""
     monkeypatch.setenv("ANQ_TAIL_TILING", tiling)
     monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
+    monkeypatch.setenv("ANQ_ROW_ORDER", order)
     monkeypatch.setenv("ANQ_STREAM", stream)
     inp = W.make_gated(61, "bf16", 23, 1024, group)
     G = 200.0
@@ -170,12 +173,14 @@ def test_gated_workload_size():
                                                  (64, 8192, 1024), (9, 2048, 64), (130, 4096, 512)])
 @pytest.mark.parametrize("rows", ["", "1", "3"])
 @pytest.mark.parametrize("block", ["", "256"])
-def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, block, monkeypatch):
+@pytest.mark.parametrize("order", ["", "0"])
+def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, block, order, monkeypatch):
     """The bf16 gate read from the workgroup's LDS table (forced on small
-    calls), with several rows per lane group and both workgroup sizes, gives
-    the oracle's codes."""
+    calls), with several rows per lane group, interleaved (the default) or
+    consecutive, and both workgroup sizes, gives the oracle's codes."""
     monkeypatch.setenv("ANQ_GATE_LUT", "1")
     monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
+    monkeypatch.setenv("ANQ_ROW_ORDER", order)
     monkeypatch.setenv("ANQ_GATE_BLOCK", block)
     inp = W.make_gated(hidden + 7 * group + tokens, "bf16", tokens, hidden, group,
                        z=("normal", 3.0), eps=1e-5)

@@ -252,19 +252,21 @@ def test_qk_grid(head_dim, heads, dtype, stream, monkeypatch):
 ])
 @pytest.mark.parametrize("op", ["fp8", "nvfp4"])
 def test_every_tiling_matches_the_oracle(hidden, tilings, op, monkeypatch):
-    """The lane mapping (lanes per row, vectors per lane, rows per lane group)
-    and the streaming hints (none, on the row streams, on the row streams and
-    the code stores) change only the order of float64 partial sums and cache
-    behaviour, never a result bit."""
+    """The lane mapping (lanes per row, vectors per lane, rows per lane group,
+    consecutive or interleaved rows) and the streaming hints (none, on the row
+    streams, on the row streams and the code stores) change only the order of
+    float64 partial sums and cache behaviour, never a result bit."""
     inp = W.make_tail(900 + hidden, op, "bf16", 67, hidden, norm_out=True,
                       scale=0.03 if op == "fp8" else None, outliers=0.002)
     scale = _scale(inp)
     ref = oracle_tail(inp, scale)
     for t in tilings:
-        for rows, stream, codes in (("", "", ""), ("1", "1", ""), ("1", "1", "0"), ("3", "0", ""),
-                                    ("64", "1", "1")):
+        for rows, order, stream, codes in (("", "", "", ""), ("1", "1", "1", ""),
+                                           ("1", "0", "1", "0"), ("3", "1", "0", ""),
+                                           ("64", "0", "1", "1"), ("5", "1", "1", "1")):
             monkeypatch.setenv("ANQ_TAIL_TILING", t)
             monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
+            monkeypatch.setenv("ANQ_ROW_ORDER", order)
             monkeypatch.setenv("ANQ_STREAM", stream)
             monkeypatch.setenv("ANQ_STREAM_CODES", codes)
             got = gpu_tail(inp, scale)

@@ -58,13 +58,15 @@ def test_fused_swizzled(tokens, hidden, dtype):
     (112, "16:1", "1"), (256, "32:1", "3"), (400, "64:1", "2"), (512, "64:1", "1"),
     (1008, "64:2", "2"), (1040, "0:1", "1"), (1040, "0:2", "5"), (1040, "0:4", "64"),
     (400, "0:1", "3")])
-def test_fused_swizzled_every_tiling(hidden, tiling, rows, monkeypatch):
+@pytest.mark.parametrize("order", ["0", "1"])
+def test_fused_swizzled_every_tiling(hidden, tiling, rows, order, monkeypatch):
     """Padded rows are shared among however many lane groups the tiling
     launches; every lane-group width gathers the four codes of a scale word.
     Each override names a tiling that exists for its row width (others are
     refused with ANQ_ERR_CONFIG, never replaced)."""
     monkeypatch.setenv("ANQ_TAIL_TILING", tiling)
     monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
+    monkeypatch.setenv("ANQ_ROW_ORDER", order)
     inp = W.make_tail(77, "nvfp4", "bf16", 45, hidden, norm_out=False, scale=None)
     G = float(oracle_global_scale(inp))
     sf = _poisoned_sf(45, hidden)

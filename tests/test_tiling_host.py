@@ -24,7 +24,8 @@ import nvfp4_quantization_place_amd as A  # noqa: E402
 OK, CONFIG, LAUNCH = 0, 9, 7
 BASE = 1 << 40
 MB = 1 << 20
-ENV = ("ANQ_TAIL_TILING", "ANQ_ROWS_PER_GROUP", "ANQ_STREAM", "ANQ_STREAM_CODES", "ANQ_GATE_LUT",
+ENV = ("ANQ_TAIL_TILING", "ANQ_ROWS_PER_GROUP", "ANQ_ROW_ORDER", "ANQ_STREAM", "ANQ_STREAM_CODES",
+       "ANQ_GATE_LUT",
        "ANQ_GATE_BLOCK", "ANQ_QK_WAVES", "ANQ_QK_GROUPS", "ANQ_QK_BLOCK")
 
 
@@ -99,9 +100,10 @@ def test_workload_tilings(L, tokens, hidden, want):
 def test_every_accepted_tiling_covers_the_rows(L, hidden, tokens, monkeypatch):
     vec = hidden // 8
     for g, k in [(16, 1), (32, 1), (64, 1), (64, 2), (0, 1), (0, 2), (0, 4), (0, 8)]:
-        for rows in ("", "1", "3"):
+        for rows, order in (("", ""), ("1", "0"), ("3", "1")):
             monkeypatch.setenv("ANQ_TAIL_TILING", f"{g}:{k}")
             monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
+            monkeypatch.setenv("ANQ_ROW_ORDER", order)
             exists = (g == 0 and (vec + k - 1) // k <= 1024) or (g in (16, 32) and k == 1 and g >= vec) \
                 or (g == 64 and g * k >= vec)
             for op in ("fp8", "nvfp4", "swizzled", "none"):
@@ -113,7 +115,9 @@ def test_every_accepted_tiling_covers_the_rows(L, hidden, tokens, monkeypatch):
                 got = last(L)
                 assert got["group"] == str(g) and got["vec_per_lane"] == str(k), got
                 if rows:
-                    assert got["rows"] == rows, got
+                    assert got["rows"] == rows and got["interleave"] == order, got
+                else:
+                    assert got["interleave"] == "0", got   # the tail tilings: consecutive rows
 
 
 @pytest.mark.parametrize("value", ["16:2", "32:2", "0:3", "8:1", "64:4", "0:1x", "abc", "0",
@@ -131,6 +135,7 @@ def test_bad_tiling_override_is_refused(L, value, monkeypatch):
 @pytest.mark.parametrize("name,value", [("ANQ_ROWS_PER_GROUP", "0"), ("ANQ_ROWS_PER_GROUP", "-2"),
                                         ("ANQ_ROWS_PER_GROUP", "two"), ("ANQ_STREAM", "2"),
                                         ("ANQ_STREAM", "yes"), ("ANQ_STREAM_CODES", "2"),
+                                        ("ANQ_ROW_ORDER", "2"), ("ANQ_ROW_ORDER", "-1"),
                                         ("ANQ_GATE_LUT", "2"),
                                         ("ANQ_GATE_BLOCK", "96"), ("ANQ_GATE_BLOCK", "2048"),
                                         ("ANQ_QK_WAVES", "0"), ("ANQ_QK_GROUPS", "5"),
@@ -187,6 +192,30 @@ def test_gated_table_choice(L, monkeypatch):
     assert g(16) == OK and last(L)["epi"] == "5"
     monkeypatch.setenv("ANQ_GATE_BLOCK", "256")
     assert g(8192) == OK and last(L)["block"] == "256"
+
+
+@pytest.mark.parametrize("tokens,hidden,group,rows,grid", [
+    (8192, 8192, 1024, 8, 1024),     # 16 rows per group at 512 workgroups: halved
+    (4096, 8192, 1024, 8, 512),
+    (2048, 8192, 1024, 4, 512),
+    (2048, 1024, 1024, 1, 256),      # fewer rows than lane groups at 512 workgroups
+    (8192, 4096, 128, 8, 1024),      # 16-lane groups, 32 per workgroup
+    (4096, 4096, 256, 8, 512),       # 32-lane groups
+])
+def test_gated_table_tiling_interleaves(L, tokens, hidden, group, rows, grid, monkeypatch):
+    """The table tiling: 512-lane workgroups, rows interleaved across lane
+    groups, about 512 workgroups (1024 once that leaves 8 rows per group);
+    ANQ_ROW_ORDER=0 restores consecutive rows with the same grid."""
+    monkeypatch.setenv("ANQ_GATE_LUT", "1")
+    call = lambda: L.gated_rmsnorm_quant_nvfp4(  # noqa: E731
+        addr(0), addr(1), addr(2), addr(3), 1e-5, tokens, hidden, group, 1, addr(4), addr(6), None)
+    assert call() == OK
+    got = last(L)
+    assert got["ok"] == "1" and got["epi"] == "5" and got["block"] == "512"
+    assert (got["rows"], got["grid"], got["interleave"]) == (str(rows), str(grid), "1"), got
+    monkeypatch.setenv("ANQ_ROW_ORDER", "0")
+    assert call() == OK
+    assert (last(L)["grid"], last(L)["interleave"]) == (str(grid), "0")
 
 
 def qk(L, tokens, nq, nk, nv, D, rot=None, store=False):
