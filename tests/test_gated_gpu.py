@@ -191,6 +191,24 @@ def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, block, ord
     np.testing.assert_array_equal(q, ref["q"])
 
 
+@pytest.mark.parametrize("tokens,hidden,group", [(2048, 8192, 1024), (4096, 4096, 128),
+                                                 (1500, 3072, 256), (8192, 2048, 64)])
+def test_gated_table_interleaved_large(tokens, hidden, group):
+    """Calls large enough that the gate-table tiling gives each lane group
+    several interleaved rows (2 to 8; at [8192, 2048] in groups of 64 the
+    grid doubles to 1024 workgroups, and [1500, 3072] ends in a ragged last
+    sweep): whole tokens sampled against the oracle."""
+    inp = W.make_gated(tokens + hidden + group, "bf16", tokens, hidden, group,
+                       z=("normal", 2.0), eps=1e-5)
+    rows = np.unique(np.concatenate([[0, tokens - 1],
+                                     np.random.default_rng(tokens).choice(tokens, 40)]))
+    G = float(O.nvfp4_global_scale(_oracle(inp, 1.0, rows)["n"]))
+    q, sf = _run(inp, G)
+    ref = _oracle(inp, G, rows)
+    np.testing.assert_array_equal(sf[rows], ref["sf"])
+    np.testing.assert_array_equal(q[rows], ref["q"])
+
+
 def test_gated_table_path_edge_rows(monkeypatch):
     """Gates outside the table (|z| < 2^-25, |z| >= 128, z = 0) next to table
     entries in one vector, and every bf16 z in the table's range once."""
