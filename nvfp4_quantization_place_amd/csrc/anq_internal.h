@@ -49,13 +49,14 @@ struct TailParams {
 // (16, 32 or 64; the workgroup holds block / group lane groups), or group == 0
 // for one row at a time per workgroup of `block` lanes. Each lane owns vectors
 // lane + k*lanes, k < vec_per_lane. Each lane group walks `rows` consecutive
-// rows, loading the next while it finishes the current one.
+// rows, or with `interleave` every (grid lane groups)-th row, loading the next
+// while it finishes the current one.
 struct Tiling {
   int group;
   int vec_per_lane;
   int block;
   int rows;
-  bool interleave;    // rows in grid-stride order (rows_per_group unused)
+  bool interleave;    // rows in grid-stride order (rows then only sizes the grid)
   bool stream;        // non-temporal loads and stores of the row streams
   bool stream_codes;  // the same hint on the code and linear block-scale stores
                       // (plain FP8 and NVFP4 epilogues)

@@ -126,11 +126,12 @@ __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int 
   return ss;
 }
 
-// Each lane group (G lanes, or the whole workgroup when G == 0) walks
-// rows_per_group consecutive rows and loads the next row's x and residual
-// before it reduces and stores the current one, so load latency overlaps the
-// previous row's work while the rows in flight across the GPU stay a compact
-// window of the tensor. Loads use clamped indices and are never predicated,
+// Each lane group (G lanes, or the whole workgroup when G == 0) walks its
+// rows, rows_per_group consecutive ones or (interleaved) every groups-th one,
+// and loads the next row's x and residual before it reduces and stores the
+// current one, so load latency overlaps the previous row's work. With one row
+// per lane group, or interleaved rows, the rows in flight across the GPU form
+// one window of the tensor. Loads use clamped indices and are never predicated,
 // so every load of a row is in flight at once; only the stores of vectors past
 // the row end (hidden not a multiple of 8 * lanes) are skipped.
 //
