@@ -34,7 +34,7 @@ def _guard_intact(buf, n_bytes):
     return bool(np.all(tail == SENT))
 
 
-@pytest.mark.parametrize("tokens,hidden", [(1, 16), (5, 64), (3, 1040), (2, 7168)])
+@pytest.mark.parametrize("tokens,hidden", [(1, 16), (5, 64), (3, 1040), (2, 7168), (40, 1024)])
 def test_row_ops_write_inside_their_buffers(tokens, hidden):
     import nvfp4_quantization_place_amd as A
     inp = W.make_tail(3, "nvfp4", "bf16", tokens, hidden)

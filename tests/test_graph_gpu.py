@@ -28,6 +28,9 @@ def _calls(A, b):
                                        sf=b["sfs"])
     A.gated_rmsnorm_quant_nvfp4(b["x"], b["z"], b["g"], b["G"], 1e-5, group=256, q=b["qg"],
                                 sf=b["sfg"])
+    # groups of 64: 4800 group-rows, the gate-table tiling with interleaved rows
+    A.gated_rmsnorm_quant_nvfp4(b["x"], b["z"], b["g"], b["G"], 1e-5, group=64, q=b["qg2"],
+                                sf=b["sfg2"])
     A.qk_norm_rope_fp8(b["qkv"], b["gq"], b["gk"], b["pos"], b["cs"], b["s"], 1e-6, 4, 2, 2, 128,
                        out=b["qko"])
     A.qk_norm_rope_fp8_kv_store(b["qkv"], b["gq"], b["gk"], b["pos"], b["cs"], b["s"], 1e-6, 4, 2,
@@ -37,7 +40,7 @@ def _calls(A, b):
                                   4, 2, 2, 128, 64, slot_mapping=b["slots"], kv_cache=b["kvm"],
                                   q_out=b["qqm"])
     return [b[k] for k in ("res", "q4", "sf4", "n4", "res2", "q8", "n8", "res3", "qs", "sfs", "qg",
-                           "sfg", "qko", "qq", "kv", "qq4", "qsf4", "qqm", "kvm")]
+                           "sfg", "qg2", "sfg2", "qko", "qq", "kv", "qq4", "qsf4", "qqm", "kvm")]
 
 
 def test_graph_replays_match_eager():
@@ -60,6 +63,8 @@ def test_graph_replays_match_eager():
              sfs=torch.empty(*A.nvfp4_swizzled_sf_shape(M, H), dtype=torch.uint8, device=dev),
              qg=torch.empty(M, H // 2, dtype=torch.uint8, device=dev),
              sfg=torch.empty(M, H // 16, dtype=torch.uint8, device=dev),
+             qg2=torch.empty(M, H // 2, dtype=torch.uint8, device=dev),
+             sfg2=torch.empty(M, H // 16, dtype=torch.uint8, device=dev),
              qkv=qk.qkv.to(dev), gq=qk.gamma_q.to(dev), gk=qk.gamma_k.to(dev),
              pos=qk.positions.to(dev), cs=torch.from_numpy(qk.cos_sin).to(dev),
              qko=torch.empty(77, 8 * 128, dtype=torch.uint8, device=dev),
