@@ -81,7 +81,8 @@ bool finish_grid(int64_t rows, int64_t groups_per_block, Tiling* t) {
 //   larger            : a workgroup of up to 1024 lanes, 2, 4 or 8 vectors each
 // and rows per lane group chosen so that a small grid still fills the GPU.
 // ANQ_TAIL_TILING="G:K" (G lanes per row, 0 = a workgroup; K vectors per lane),
-// ANQ_ROWS_PER_GROUP (>= 1) and ANQ_STREAM (0 / 1) override the choice.
+// ANQ_ROWS_PER_GROUP (>= 1), ANQ_ROW_ORDER (0 consecutive / 1 interleaved),
+// ANQ_STREAM and ANQ_STREAM_CODES (0 / 1) override the choice.
 int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
   Tiling t{};
   if (vec <= 64) {
@@ -121,6 +122,13 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
   // vector per lane; with two, one row per workgroup measured faster above)
   t.rows = (t.group == 0 && t.block >= 512 && tokens >= 4096 && t.vec_per_lane == 1) ? 2 : 1;
   if (!env_int("ANQ_ROWS_PER_GROUP", 1, 1 << 20, &t.rows)) return ANQ_ERR_CONFIG;
+  // several rows per lane group: interleaved across the grid, so the rows in
+  // flight stay one window of the tensor. bf16 with norm output, inputs from
+  // HBM, one GPU, two rows per workgroup, consecutive -> interleaved: NVFP4
+  // [8192, 8192] 93.1 -> 90.6-91.6 us, [16384, 4096] 92.4-92.8 -> 91.3,
+  // [32768, 4096] 181.5 -> 178.2; FP8 [8192, 4096] 49.4-49.5 -> 49.0,
+  // [4096, 8192] 48.8-49.0 -> 48.6-48.9
+  t.interleave = t.rows > 1;
   // streaming hints from 1 MiB of x. With inputs coming from HBM they measured
   // 10-15% faster from 1 to 32 MiB of x on MI355X (fp16 [256, 8192] NVFP4 5.25
   // -> 4.65 us, [64, 8192] 4.08 -> 3.88) and 3% slower at 256 KiB; with inputs

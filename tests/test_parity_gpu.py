@@ -121,6 +121,20 @@ def test_tail_published_grid_nvfp4_with_norm(hidden, tokens, dtype):
     run_and_compare(inp)
 
 
+@pytest.mark.parametrize("tokens,hidden,op", [(4099, 4000, "fp8"), (4099, 4000, "nvfp4"),
+                                               (4100, 8192, "nvfp4")])
+def test_tail_default_interleaved_rows(tokens, hidden, op):
+    """Calls whose default tiling gives each workgroup two rows (one vector
+    per lane, 512 or more lanes, 4096 or more tokens), taken interleaved
+    across the grid; an odd token count leaves the last sweep ragged. Sampled
+    rows against the oracle, every output."""
+    inp = W.make_tail(tokens + hidden, op, "bf16", tokens, hidden, norm_out=True,
+                      scale=0.02 if op == "fp8" else None, outliers=0.002)
+    rows = np.unique(np.concatenate([[0, 1, tokens // 2, tokens - 2, tokens - 1],
+                                     np.random.default_rng(hidden).choice(tokens, 200)]))
+    run_and_compare(inp, rows)
+
+
 # ------------------------------------------------------------ edge rows ----
 
 def _tail_from_arrays(op, dtype, x, res, gamma, eps=1e-6, scale=0.02, norm=True):

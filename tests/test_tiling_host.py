@@ -82,8 +82,9 @@ def tail(L, op, tokens, hidden, dtype=1, norm=True):
                       stream_codes="0")),
     (1024, 7168, dict(group="0", vec_per_lane="1", block="896", rows="1", stream="1",
                       stream_codes="1")),
-    (8192, 8192, dict(group="0", vec_per_lane="1", block="1024", rows="2", stream="1",
-                      stream_codes="0")),
+    (8192, 8192, dict(group="0", vec_per_lane="1", block="1024", rows="2", interleave="1",
+                      stream="1", stream_codes="0")),
+    (65536, 1024, dict(interleave="0")),
     (3, 65536, dict(group="0", vec_per_lane="8", block="1024")),
 ])
 def test_workload_tilings(L, tokens, hidden, want):
@@ -116,8 +117,8 @@ def test_every_accepted_tiling_covers_the_rows(L, hidden, tokens, monkeypatch):
                 assert got["group"] == str(g) and got["vec_per_lane"] == str(k), got
                 if rows:
                     assert got["rows"] == rows and got["interleave"] == order, got
-                else:
-                    assert got["interleave"] == "0", got   # the tail tilings: consecutive rows
+                else:   # default: interleaved exactly when a lane group takes several rows
+                    assert got["interleave"] == ("1" if int(got["rows"]) > 1 else "0"), got
 
 
 @pytest.mark.parametrize("value", ["16:2", "32:2", "0:3", "8:1", "64:4", "0:1x", "abc", "0",
