@@ -47,7 +47,8 @@ int launch_tail(int dtype, int epi, bool norm_out, const TailParams& p, const Ti
                   (t.group == 0 || (t.block == (epi == kEpiGatedNvfp4Lut ? t.block : 256) &&
                                     t.block % t.group == 0)) &&
                   lanes_per_row * t.vec_per_lane >= p.vec &&
-                  (t.group > 0 || (int64_t)t.block - 64 < (p.vec + t.vec_per_lane - 1) / t.vec_per_lane) &&
+                  (t.group > 0 || (int64_t)t.block - 64 < (p.vec + t.vec_per_lane - 1) / t.vec_per_lane ||
+                   (t.block == 1024 && t.vec_per_lane == 1 && p.vec > 12 * 64)) &&
                   t.rows == p.rows_per_group && t.rows >= 1 && t.grid >= 1 &&
                   p.interleave == (t.interleave ? 1 : 0) &&
                   t.grid <= 0x7FFFFFFF && t.grid * groups_per_block * t.rows >= p.tokens &&

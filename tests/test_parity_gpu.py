@@ -135,6 +135,20 @@ def test_tail_default_interleaved_rows(tokens, hidden, op):
     run_and_compare(inp, rows)
 
 
+@pytest.mark.parametrize("tokens,hidden,op,dtype", [(1031, 7168, "nvfp4", "bf16"),
+                                                     (1100, 6656, "fp8", "f16"),
+                                                     (1024, 7680, "nvfp4", "f16")])
+def test_tail_padded_workgroups(tokens, hidden, op, dtype):
+    """One vector per lane in 13 to 15 wavefronts, which the default tiling
+    pads to 16 at 1024 rows or more: the padding lanes own no vector, add
+    nothing to the sum and store nothing. Sampled rows, every output."""
+    inp = W.make_tail(tokens + hidden, op, dtype, tokens, hidden, norm_out=True,
+                      scale=0.02 if op == "fp8" else None, outliers=0.002)
+    rows = np.unique(np.concatenate([[0, tokens - 1],
+                                     np.random.default_rng(hidden).choice(tokens, 150)]))
+    run_and_compare(inp, rows)
+
+
 # ------------------------------------------------------------ edge rows ----
 
 def _tail_from_arrays(op, dtype, x, res, gamma, eps=1e-6, scale=0.02, norm=True):

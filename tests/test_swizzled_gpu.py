@@ -32,7 +32,8 @@ def _poisoned_sf(tokens, hidden):
 
 
 SHAPES = [(1, 16), (5, 48), (7, 400), (9, 512), (37, 1040), (128, 7168), (129, 1024), (300, 2048),
-          (64, 8192), (3, 16400), (2, 40976), (3, 65520)]
+          (64, 8192), (3, 16400), (2, 40976), (3, 65520),
+          (1030, 7168)]  # 14 wavefronts padded to 16: lanes past the row gather zero codes
 
 
 @pytest.mark.parametrize("tokens,hidden", SHAPES)

@@ -80,8 +80,11 @@ def tail(L, op, tokens, hidden, dtype=1, norm=True):
                        stream_codes="0")),
     (8192, 7168, dict(group="0", vec_per_lane="2", block="448", rows="1", stream="1",
                       stream_codes="0")),
-    (1024, 7168, dict(group="0", vec_per_lane="1", block="896", rows="1", stream="1",
-                      stream_codes="1")),
+    (1024, 7168, dict(group="0", vec_per_lane="1", block="1024", rows="1", stream="1",
+                      stream_codes="1")),     # 14 wavefronts padded to 16
+    (512, 7168, dict(group="0", vec_per_lane="1", block="896")),   # too few rows to pad
+    (1024, 6144, dict(group="0", vec_per_lane="1", block="768")),  # 12 wavefronts: not padded
+    (1024, 7680, dict(group="0", vec_per_lane="1", block="1024")),
     (8192, 8192, dict(group="0", vec_per_lane="1", block="1024", rows="2", interleave="1",
                       stream="1", stream_codes="0")),
     (65536, 1024, dict(interleave="0")),
