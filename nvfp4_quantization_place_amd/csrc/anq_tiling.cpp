@@ -173,17 +173,40 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
 // groups of 128 36.1 -> 34.0; then 1024 workgroups at [8192, 8192] groups of
 // 1024 66.1 -> 63.9, of 512 63.2 -> 59.9, [8192, 4096] groups of 128 34.3 ->
 // 32.3. 256 and 1024 lanes per workgroup measured no better (320, 384, 768:
-// 74-85 us). ANQ_GATE_BLOCK (a multiple of 64, 64 to 1024),
+// 74-85 us).
+// Wider rows (1040 to 8192 elements) take one workgroup of one vector per lane
+// each, as the tail tiling does, in about two waves of resident workgroups:
+// 512 times the workgroups a CU holds (4 wavefronts per SIMD, four tables of
+// LDS).
+// bf16, one GPU, grid halved / as chosen / doubled: [8192, 8192] in one group
+// 62.8 (as chosen) against 66.9 (doubled); in groups of 4096 63.9 / 62.9 /
+// 63.5 us; [4096, 5120] in one group 24.3 (as chosen) against 31.6 (doubled).
+// ANQ_GATE_BLOCK (a multiple of 64, 64 to 1024; lane-group tilings only),
 // ANQ_ROWS_PER_GROUP, ANQ_ROW_ORDER and ANQ_STREAM override.
 int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* out) {
   Tiling t{};
-  t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
-  t.vec_per_lane = vec <= 64 ? 1 : 2;
-  t.block = 512;
-  if (!env_int("ANQ_GATE_BLOCK", 64, 1024, &t.block) || t.block % 64 != 0) return ANQ_ERR_CONFIG;
-  const int64_t groups_per_block = t.block / t.group;
-  int64_t r = rows / (groups_per_block * 512);
-  if (r >= 16) r /= 2;
+  int block = 512;
+  if (!env_int("ANQ_GATE_BLOCK", 64, 1024, &block) || block % 64 != 0) return ANQ_ERR_CONFIG;
+  int64_t groups_per_block;
+  int64_t r;
+  if (vec <= 128) {
+    t.group = vec <= 16 ? 16 : (vec <= 32 ? 32 : 64);
+    t.vec_per_lane = vec <= 64 ? 1 : 2;
+    t.block = block;
+    groups_per_block = t.block / t.group;
+    r = rows / (groups_per_block * 512);
+    if (r >= 16) r /= 2;
+  } else if (vec <= 1024) {
+    t.group = 0;
+    t.vec_per_lane = 1;
+    t.block = (vec + 63) / 64 * 64;
+    groups_per_block = 1;
+    const int waves = t.block / 64;
+    const int per_cu = 16 / waves < 4 ? 16 / waves : 4;
+    r = rows / (512 * (int64_t)per_cu);
+  } else {
+    return ANQ_ERR_UNSUPPORTED;  // the caller keeps wider groups on the computed gate
+  }
   t.rows = (int)(r < 1 ? 1 : (r > 64 ? 64 : r));
   t.interleave = true;
   if (!env_int("ANQ_ROWS_PER_GROUP", 1, 1 << 20, &t.rows)) return ANQ_ERR_CONFIG;

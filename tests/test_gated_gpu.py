@@ -170,14 +170,18 @@ def test_gated_workload_size():
 
 
 @pytest.mark.parametrize("tokens,hidden,group", [(5, 64, 16), (37, 1024, 1024), (37, 1024, 128),
-                                                 (64, 8192, 1024), (9, 2048, 64), (130, 4096, 512)])
+                                                 (64, 8192, 1024), (9, 2048, 64), (130, 4096, 512),
+                                                 (5, 2048, 2048), (7, 8192, 8192), (9, 5120, 5120),
+                                                 (4, 3072, 1536)])
 @pytest.mark.parametrize("rows", ["", "1", "3"])
 @pytest.mark.parametrize("block", ["", "256"])
 @pytest.mark.parametrize("order", ["", "0"])
 def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, block, order, monkeypatch):
     """The bf16 gate read from the workgroup's LDS table (forced on small
     calls), with several rows per lane group, interleaved (the default) or
-    consecutive, and both workgroup sizes, gives the oracle's codes."""
+    consecutive, and both workgroup sizes of the lane-group tiling (groups of
+    1040 and more take a workgroup per row whatever the size asked), gives the
+    oracle's codes."""
     monkeypatch.setenv("ANQ_GATE_LUT", "1")
     monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
     monkeypatch.setenv("ANQ_ROW_ORDER", order)
@@ -192,12 +196,15 @@ def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, block, ord
 
 
 @pytest.mark.parametrize("tokens,hidden,group", [(2048, 8192, 1024), (4096, 4096, 128),
-                                                 (1500, 3072, 256), (8192, 2048, 64)])
+                                                 (1500, 3072, 256), (8192, 2048, 64),
+                                                 (512, 8192, 8192), (2048, 8192, 4096),
+                                                 (4096, 5120, 5120), (1501, 4096, 2048)])
 def test_gated_table_interleaved_large(tokens, hidden, group):
     """Calls large enough that the gate-table tiling gives each lane group
     several interleaved rows (2 to 8; at [8192, 2048] in groups of 64 the
     grid doubles to 1024 workgroups, and [1500, 3072] ends in a ragged last
-    sweep): whole tokens sampled against the oracle."""
+    sweep), and wide groups with a workgroup per row (one to eight rows each,
+    640-lane workgroups at 5120): whole tokens sampled against the oracle."""
     inp = W.make_gated(tokens + hidden + group, "bf16", tokens, hidden, group,
                        z=("normal", 2.0), eps=1e-5)
     rows = np.unique(np.concatenate([[0, tokens - 1],

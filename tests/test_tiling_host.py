@@ -222,6 +222,42 @@ def test_gated_table_tiling_interleaves(L, tokens, hidden, group, rows, grid, mo
     assert (last(L)["grid"], last(L)["interleave"]) == (str(grid), "0")
 
 
+@pytest.mark.parametrize("tokens,hidden,group,block,rows,grid", [
+    (8192, 8192, 8192, 1024, 16, 512),   # one workgroup per CU: two waves of 256
+    (8192, 8192, 4096, 512, 16, 1024),   # two per CU
+    (8192, 8192, 2048, 256, 16, 2048),   # four per CU (four tables of LDS)
+    (4096, 5120, 5120, 640, 8, 512),
+    (300, 8192, 8192, 1024, 1, 300),     # fewer rows than resident workgroups
+])
+def test_gated_table_wide_groups(L, tokens, hidden, group, block, rows, grid):
+    """Groups of 1040 to 8192 elements use the gate table with one workgroup
+    of one vector per lane per row, interleaved rows, about two waves of the
+    workgroups the GPU holds at once."""
+    assert L.gated_rmsnorm_quant_nvfp4(addr(0), addr(1), addr(2), addr(3), 1e-5, tokens, hidden,
+                                       group, 1, addr(4), addr(6), None) == OK
+    got = last(L)
+    assert got["ok"] == "1" and got["epi"] == "5" and got["group"] == "0", got
+    assert (got["vec_per_lane"], got["block"], got["rows"], got["grid"], got["interleave"]) == \
+        ("1", str(block), str(rows), str(grid), "1"), got
+
+
+def test_gated_table_choice_by_size(L, monkeypatch):
+    """The table is used for bf16 z in groups of at most 8192 once a call has
+    2048 group rows or 2^21 elements; wider groups always compute the gate."""
+    g = lambda tokens, hidden, group: L.gated_rmsnorm_quant_nvfp4(  # noqa: E731
+        addr(0), addr(1), addr(2), addr(3), 1e-5, tokens, hidden, group, 1, addr(4), addr(6), None)
+    assert g(256, 8192, 8192) == OK and last(L)["epi"] == "5"    # 2^21 elements
+    assert g(255, 8192, 8192) == OK and last(L)["epi"] == "4"
+    assert g(1024, 2048, 2048) == OK and last(L)["epi"] == "5"
+    assert g(512, 3072, 1536) == OK and last(L)["epi"] == "4"    # 1.5 M elements
+    assert g(4096, 16384, 16384) == OK and last(L)["epi"] == "4"  # wider than the table tiling
+    monkeypatch.setenv("ANQ_GATE_LUT", "1")
+    assert g(2, 8192, 8192) == OK and last(L)["epi"] == "5"
+    assert g(2, 16384, 16384) == OK and last(L)["epi"] == "4"
+    monkeypatch.setenv("ANQ_GATE_LUT", "0")
+    assert g(8192, 8192, 8192) == OK and last(L)["epi"] == "4"
+
+
 def qk(L, tokens, nq, nk, nv, D, rot=None, store=False):
     rot = D if rot is None else rot
     if store:
