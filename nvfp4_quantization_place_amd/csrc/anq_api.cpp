@@ -200,12 +200,12 @@ extern "C" int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const voi
   // groups of 8192, 4096, 2048 115 / 105 / 107 -> 63 / 63 / 66-68 us, [4096,
   // 5120] in one group 48 -> 24; [256, 8192] one group 6.8 -> 6.2; at 1.5 M
   // elements ([512, 3072], groups of 1536) the table lost, 6.3 -> 7.1.
-  const auto lut_fits = [&] { return dtype == ANQ_BF16 && group <= 8192; };
-  bool lut = lut_fits() && (p.tokens >= 2048 || p.tokens * group >= ((int64_t)1 << 21));
+  const bool lut_fits = dtype == ANQ_BF16 && group <= 8192;
+  bool lut = lut_fits && (p.tokens >= 2048 || p.tokens * group >= ((int64_t)1 << 21));
   if (const char* e = getenv("ANQ_GATE_LUT")) {
     if (*e) {
       if (strcmp(e, "0") != 0 && strcmp(e, "1") != 0) return ANQ_ERR_CONFIG;
-      lut = e[0] == '1' && lut_fits();  // the table covers bf16 z only
+      lut = e[0] == '1' && lut_fits;  // the table covers bf16 z only
     }
   }
   anq::Tiling t;
