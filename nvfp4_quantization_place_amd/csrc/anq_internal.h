@@ -59,7 +59,7 @@ struct Tiling {
   bool interleave;    // rows in grid-stride order (rows then only sizes the grid)
   bool stream;        // non-temporal loads and stores of the row streams
   bool stream_codes;  // the same hint on the code and linear block-scale stores
-                      // (plain FP8 and NVFP4 epilogues)
+                      // (plain FP8 and NVFP4 epilogues, gate-table epilogue)
   int64_t grid;
 };
 

@@ -266,9 +266,10 @@ tail_kernel(TailParams p) {
 
   // The epilogue of the lane's vector k of `row`: the norm output and the codes.
   // Codes and linear block scales carry the streaming hint only with NT == 2
-  // (the host's choice for calls below 32 MiB of x): at large calls their 8-,
-  // 4- and 1-byte stores fill whole lines only once merged in the L2, and the
-  // hint measured 3-7% slower there. The swizzled scale words never take it.
+  // (the host's choice: plain epilogues below 32 MiB of x, where at large
+  // calls their 8-, 4- and 1-byte stores fill whole lines only once merged in
+  // the L2 and the hint measured 3-7% slower; the gate-table epilogue
+  // wherever its rows are hinted). The swizzled scale words never take it.
   // (A run-time flag choosing between a hinted and a plain store compiled to
   // the plain store alone: the two stores were merged and the hint dropped.)
   auto emit = [&](int64_t row_, int k, const float (&n)[8]) {
@@ -476,8 +477,9 @@ static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
 template <int DT, int EPI, bool NORM>
 static hipError_t launch3(const TailParams& p, const Tiling& t, hipStream_t s) {
   if (!t.stream) return launch4<DT, EPI, NORM, 0>(p, t, s);
-  // the code-store hint exists for the plain FP8 and NVFP4 epilogues only
-  if constexpr (EPI == kEpiFp8 || EPI == kEpiNvfp4) {
+  // the code-store hint exists for the plain FP8 and NVFP4 epilogues and the
+  // gate-table one
+  if constexpr (EPI == kEpiFp8 || EPI == kEpiNvfp4 || EPI == kEpiGatedNvfp4Lut) {
     if (t.stream_codes) return launch4<DT, EPI, NORM, 2>(p, t, s);
   }
   return launch4<DT, EPI, NORM, 1>(p, t, s);

@@ -215,7 +215,10 @@ int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* out) {
   // 24.1, [1024, 8192] 16.4 -> 16.9)
   t.stream = (int64_t)vec * 16 * rows >= ((int64_t)1 << 20);
   if (!env_stream(&t.stream)) return ANQ_ERR_CONFIG;
-  t.stream_codes = false;  // the gated calls are large: unhinted, as above
+  // the hint on the code and linear scale stores too, wherever the rows take
+  // it: bf16, one GPU, [4096, 5120] in one group 24.2 -> 22.8 us; no change
+  // at [8192, 8192] and [2048, 8192] in groups of 1024 (63.0-63.7, 19.0 us)
+  t.stream_codes = t.stream;
   if (!env_stream_codes(&t.stream_codes)) return ANQ_ERR_CONFIG;
   if (!env_interleave(&t.interleave)) return ANQ_ERR_CONFIG;
   finish_grid(rows, groups_per_block, &t);

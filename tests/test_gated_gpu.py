@@ -195,6 +195,25 @@ def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, block, ord
     np.testing.assert_array_equal(q, ref["q"])
 
 
+@pytest.mark.parametrize("tokens,hidden,group", [(37, 1024, 128), (9, 2048, 64), (7, 8192, 8192),
+                                                 (9, 5120, 5120)])
+@pytest.mark.parametrize("stream,codes", [("1", "1"), ("1", "0"), ("0", "1")])
+def test_gated_table_path_streaming_hints(tokens, hidden, group, stream, codes, monkeypatch):
+    """The streaming hints on the rows and on the code and scale stores of
+    the gate-table kernel (forced on small calls, both tilings) change no
+    bit."""
+    monkeypatch.setenv("ANQ_GATE_LUT", "1")
+    monkeypatch.setenv("ANQ_STREAM", stream)
+    monkeypatch.setenv("ANQ_STREAM_CODES", codes)
+    inp = W.make_gated(hidden + group + 3 * tokens, "bf16", tokens, hidden, group,
+                       z=("normal", 3.0), eps=1e-5)
+    G = float(O.nvfp4_global_scale(_oracle(inp, 1.0)["n"]))
+    q, sf = _run(inp, G)
+    ref = _oracle(inp, G)
+    np.testing.assert_array_equal(sf, ref["sf"])
+    np.testing.assert_array_equal(q, ref["q"])
+
+
 @pytest.mark.parametrize("tokens,hidden,group", [(2048, 8192, 1024), (4096, 4096, 128),
                                                  (1500, 3072, 256), (8192, 2048, 64),
                                                  (512, 8192, 8192), (2048, 8192, 4096),
