@@ -172,7 +172,8 @@ def test_gated_workload_size():
 @pytest.mark.parametrize("tokens,hidden,group", [(5, 64, 16), (37, 1024, 1024), (37, 1024, 128),
                                                  (64, 8192, 1024), (9, 2048, 64), (130, 4096, 512),
                                                  (5, 2048, 2048), (7, 8192, 8192), (9, 5120, 5120),
-                                                 (4, 3072, 1536)])
+                                                 (4, 3072, 1536), (5, 16384, 16384),
+                                                 (3, 12288, 12288)])
 @pytest.mark.parametrize("rows", ["", "1", "3"])
 @pytest.mark.parametrize("block", ["", "256"])
 @pytest.mark.parametrize("order", ["", "0"])
@@ -217,7 +218,8 @@ def test_gated_table_path_streaming_hints(tokens, hidden, group, stream, codes, 
 @pytest.mark.parametrize("tokens,hidden,group", [(2048, 8192, 1024), (4096, 4096, 128),
                                                  (1500, 3072, 256), (8192, 2048, 64),
                                                  (512, 8192, 8192), (2048, 8192, 4096),
-                                                 (4096, 5120, 5120), (1501, 4096, 2048)])
+                                                 (4096, 5120, 5120), (1501, 4096, 2048),
+                                                 (2048, 16384, 16384)])
 def test_gated_table_interleaved_large(tokens, hidden, group):
     """Calls large enough that the gate-table tiling gives each lane group
     several interleaved rows (2 to 8; at [8192, 2048] in groups of 64 the

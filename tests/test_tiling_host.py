@@ -228,21 +228,23 @@ def test_gated_table_tiling_interleaves(L, tokens, hidden, group, rows, grid, mo
     (8192, 8192, 2048, 256, 16, 2048),   # four per CU (four tables of LDS)
     (4096, 5120, 5120, 640, 8, 512),
     (300, 8192, 8192, 1024, 1, 300),     # fewer rows than resident workgroups
+    (2048, 16384, 16384, 1024, 4, 512),  # two vectors per lane
+    (4096, 12288, 12288, 768, 8, 512),
 ])
 def test_gated_table_wide_groups(L, tokens, hidden, group, block, rows, grid):
-    """Groups of 1040 to 8192 elements use the gate table with one workgroup
-    of one vector per lane per row, interleaved rows, about two waves of the
-    workgroups the GPU holds at once."""
+    """Groups of 1040 to 16384 elements use the gate table with one workgroup
+    per row (one vector per lane, two past 8192 elements), interleaved rows,
+    about two waves of the workgroups the GPU holds at once."""
     assert L.gated_rmsnorm_quant_nvfp4(addr(0), addr(1), addr(2), addr(3), 1e-5, tokens, hidden,
                                        group, 1, addr(4), addr(6), None) == OK
     got = last(L)
     assert got["ok"] == "1" and got["epi"] == "5" and got["group"] == "0", got
     assert (got["vec_per_lane"], got["block"], got["rows"], got["grid"], got["interleave"]) == \
-        ("1", str(block), str(rows), str(grid), "1"), got
+        ("1" if group <= 8192 else "2", str(block), str(rows), str(grid), "1"), got
 
 
 def test_gated_table_choice_by_size(L, monkeypatch):
-    """The table is used for bf16 z in groups of at most 8192 once a call has
+    """The table is used for bf16 z in groups of at most 16384 once a call has
     2048 group rows or 2^21 elements; wider groups always compute the gate."""
     g = lambda tokens, hidden, group: L.gated_rmsnorm_quant_nvfp4(  # noqa: E731
         addr(0), addr(1), addr(2), addr(3), 1e-5, tokens, hidden, group, 1, addr(4), addr(6), None)
@@ -250,10 +252,11 @@ def test_gated_table_choice_by_size(L, monkeypatch):
     assert g(255, 8192, 8192) == OK and last(L)["epi"] == "4"
     assert g(1024, 2048, 2048) == OK and last(L)["epi"] == "5"
     assert g(512, 3072, 1536) == OK and last(L)["epi"] == "4"    # 1.5 M elements
-    assert g(4096, 16384, 16384) == OK and last(L)["epi"] == "4"  # wider than the table tiling
+    assert g(4096, 16384, 16384) == OK and last(L)["epi"] == "5"
+    assert g(4096, 32768, 32768) == OK and last(L)["epi"] == "4"  # wider than the table tiling
     monkeypatch.setenv("ANQ_GATE_LUT", "1")
-    assert g(2, 8192, 8192) == OK and last(L)["epi"] == "5"
-    assert g(2, 16384, 16384) == OK and last(L)["epi"] == "4"
+    assert g(2, 16384, 16384) == OK and last(L)["epi"] == "5"
+    assert g(2, 32768, 32768) == OK and last(L)["epi"] == "4"
     monkeypatch.setenv("ANQ_GATE_LUT", "0")
     assert g(8192, 8192, 8192) == OK and last(L)["epi"] == "4"
 
