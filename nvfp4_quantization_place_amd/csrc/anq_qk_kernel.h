@@ -217,13 +217,19 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
       // the partner of each rotated element is element i of b in lane ^ RL,
       // of the same head; the whole wavefront takes part in the exchange.
       // The first element of a pair takes x c - y s as x c + (-y) s (the
-      // same binary32 result), the second x c + y s.
+      // same binary32 result), the second x c + y s. Every lane computes the
+      // rotation and selects it: a conditional assignment let the compiler
+      // sink each product into a branch of its own, eight exec-mask branches
+      // per group (same box, 4096 tokens, rotary 64: plain op 11.93 -> 11.66
+      // us, mixed pool 12.53 -> 12.47).
       const int src = (lane ^ RL) << 2;
+      const bool take = qk && rope_b;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float y = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(ob[i])));
-        const float rot = (ob[i] * c[i]) + ((upper ? y : -y) * s[i]);
-        if (qk && rope_b) ob[i] = rot;
+        float rot = (ob[i] * c[i]) + ((upper ? y : -y) * s[i]);
+        asm volatile("" : "+v"(rot));
+        ob[i] = take ? rot : ob[i];
       }
     }
     // the mixed pool keeps a K head's rotated part in bf16, before the division
