@@ -12,10 +12,12 @@
 //    load/store instruction of a wavefront touches 1 KiB of contiguous bytes.
 //  * The row stays in registers between the add and the epilogue: x and
 //    residual are read once, residual / norm_out / codes written once.
-//  * Small rows (<= 1024 elements) use 16, 32 or 64 lanes of one wavefront per
-//    row and reduce with cross-lane shuffles; larger rows use one workgroup of
-//    up to 1024 lanes per row and combine wavefront partials through LDS in a
-//    fixed order.
+//  * Small rows (up to 512 elements, and the gate-table variant's groups up to
+//    1024) use 16, 32 or 64 lanes of one wavefront per row and reduce with
+//    cross-lane shuffles; larger rows use one workgroup of up to 1024 lanes
+//    per row and combine wavefront partials through LDS in a fixed order.
+//  * A lane group that takes several rows takes them consecutively or, where
+//    the host asks, interleaved across the grid (rows i, i + groups, ...).
 //  * The sum of squares is accumulated in float64 (squares of fp16/bf16 values
 //    are exact there) and rounded once to binary32. When that float64 total is
 //    within its error bound of a binary32 rounding midpoint, the row is summed
