@@ -137,15 +137,26 @@ __device__ __forceinline__ float row_sum_squares(double acc, int32_t width, int 
 // so every load of a row is in flight at once; only the stores of vectors past
 // the row end (hidden not a multiple of 8 * lanes) are skipped.
 //
-// Register budget: 7 wavefronts per SIMD (<= 72 VGPRs) for one vector per
-// lane, which then needs no spills; 4 (<= 128) for rows wider than 8192 and
-// for the gated variant (its binary64 exp needs the registers).
+// Register budget, in wavefronts per SIMD: 7 (<= 72 VGPRs) for one vector per
+// lane; 6 (<= 80) for the swizzled NVFP4 epilogue on 32-lane groups, which
+// at 72 spilled three 64-bit values, one of them reloaded inside the row loop
+// behind a wait for every load in flight (the next row's prefetch included);
+// 4 (<= 128) for two or more vectors per lane and for the gated variants
+// (their binary64 exp needs the registers). Of the instantiations the host
+// can choose, only the gated one at eight vectors per lane spills (five
+// values, reloaded on the rare paths only: the double-double sum, the
+// division fallbacks).
+template <int EPI, int K, int G>
+constexpr int tail_waves_per_simd() {
+  if (K != 1 || EPI == kEpiGatedNvfp4 || EPI == kEpiGatedNvfp4Lut) return 4;
+  return EPI == kEpiNvfp4Swz && G == 32 ? 6 : 7;
+}
+
 // NT: 0 no streaming hints; 1 on the row loads and stores (x, residual, norm
 // output); 2 also on the code and linear block-scale stores
 template <int DT, int EPI, bool NORM, int K, int G, int NT, bool SL = (K >= 4)>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, G > 0 && EPI != kEpiGatedNvfp4Lut ? 256 : 1024),
-                               amdgpu_waves_per_eu(K == 1 && EPI != kEpiGatedNvfp4 &&
-                                                           EPI != kEpiGatedNvfp4Lut ? 7 : 4)))
+                               amdgpu_waves_per_eu(tail_waves_per_simd<EPI, K, G>())))
 tail_kernel(TailParams p) {
   __shared__ double lds[64];
   __shared__ float mult_tab[128];  // NVFP4: G / value(sf) for every block-scale code
@@ -208,12 +219,16 @@ tail_kernel(TailParams p) {
   // the residual is held packed in T (it is the stored value, so unpacking it
   // again is exact), and gamma is loaded after the sum of squares. Holding all
   // of it at once spilled: at bf16 [2048, 32768] and [1024, 65536] the kernel
-  // streamed at 4.0 and 1.1 TB/s.
+  // streamed at 4.0 and 1.1 TB/s. The gated variants (groups wider than 16384)
+  // take a row of the same shape: u is binary32 (no stored value), held across
+  // the reduction at four vectors per lane and recomputed at eight. With the
+  // prefetch they spilled 34 and 571 VGPRs.
   constexpr bool kWide = SL && !kGated;
+  constexpr bool kWideGated = SL && kGated;
   constexpr bool kReload = kWide && K >= 8;
 
   U4 gv[K], xv[K], rv[K];
-  if constexpr (!kWide) {
+  if constexpr (!kWide && !kWideGated) {
     const size_t rb = (size_t)(row < last ? row : last) * row_bytes;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -266,7 +281,8 @@ tail_kernel(TailParams p) {
     return recip_rn_ext(sqrtf(mean + p.eps));
   };
 
-  // The epilogue of the lane's vector k of `row`: the norm output and the codes.
+  // The epilogue of one of the lane's vectors of `row` (in the row, `ok`; at
+  // byte offset `off`): the norm output and the codes.
   // Codes and linear block scales carry the streaming hint only with NT == 2
   // (the host's choice: plain epilogues below 32 MiB of x, where at large
   // calls their 8-, 4- and 1-byte stores fill whole lines only once merged in
@@ -274,14 +290,14 @@ tail_kernel(TailParams p) {
   // wherever its rows are hinted). The swizzled scale words never take it.
   // (A run-time flag choosing between a hinted and a plain store compiled to
   // the plain store alone: the two stores were merged and the hint dropped.)
-  auto emit = [&](int64_t row_, int k, const float (&n)[8]) {
+  auto emit = [&](int64_t row_, bool ok, uint32_t off, const float (&n)[8]) {
     if constexpr (NORM) {
-      if (vok[k]) st16s<(NT != 0)>(row_ptr<G>(nout, (size_t)row_ * row_bytes) + voff[k], pack8<DT>(n));
+      if (ok) st16s<(NT != 0)>(row_ptr<G>(nout, (size_t)row_ * row_bytes) + off, pack8<DT>(n));
     }
     if constexpr (EPI == kEpiFp8) {
       uint32_t lo, hi;
       fp8_codes8(n, sc, inv_sc, lo, hi);
-      if (vok[k]) st8s<NT == 2>(row_ptr<G>(p.q, (size_t)row_ * p.hidden) + voff[k] / 2, lo, hi);
+      if (ok) st8s<NT == 2>(row_ptr<G>(p.q, (size_t)row_ * p.hidden) + off / 2, lo, hi);
     } else if constexpr (kNvfp4) {
       uint32_t w, sfc;
       nvfp4_half_block(n, sc, mult_tab, w, sfc);
@@ -291,18 +307,18 @@ tail_kernel(TailParams p) {
         // block, lane groups a multiple of 8 wide), so lane 8j gathers them
         // and stores the word; codes of vectors past the row end count as 0,
         // which also writes the padded columns of the last word.
-        const uint32_t c8 = vok[k] ? (sfc & 0xffu) : 0u;
+        const uint32_t c8 = ok ? (sfc & 0xffu) : 0u;
         const uint32_t word = c8 | ((uint32_t)__shfl_down((int)c8, 2) << 8) |
                               ((uint32_t)__shfl_down((int)c8, 4) << 16) |
                               ((uint32_t)__shfl_down((int)c8, 6) << 24);
-        if (vok[k] && (lane & 7) == 0)
-          st4s<false>(p.sf + sf_swizzled_offset(row_, (int32_t)(voff[k] / 32), p.sf_tiles), word);
+        if (ok && (lane & 7) == 0)
+          st4s<false>(p.sf + sf_swizzled_offset(row_, (int32_t)(off / 32), p.sf_tiles), word);
       }
-      if (vok[k]) {
-        st4s<NT == 2>(row_ptr<G>(p.q, (size_t)row_ * (p.hidden / 2)) + voff[k] / 4, w);
+      if (ok) {
+        st4s<NT == 2>(row_ptr<G>(p.q, (size_t)row_ * (p.hidden / 2)) + off / 4, w);
         if constexpr (EPI != kEpiNvfp4Swz) {
           if ((lane & 1) == 0)  // linear [rows, width/16] (the plain and the gated variants)
-            st1s<NT == 2>(row_ptr<G>(p.sf, (size_t)row_ * (p.hidden / 16)) + voff[k] / 32,
+            st1s<NT == 2>(row_ptr<G>(p.sf, (size_t)row_ * (p.hidden / 16)) + off / 32,
                           (uint8_t)sfc);
         }
       }
@@ -324,7 +340,92 @@ tail_kernel(TailParams p) {
       unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + vec_off(k) + 2 * i), f, unused);
       return f;
     };
-    if constexpr (kWide) {
+    // gated: the same pass recomputes u from x and z
+    auto gated_u = [&](int k, int i) {
+      const uint8_t* xrow = row_ptr<G>(x, (size_t)row * row_bytes);
+      float xf, zf, unused;
+      unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(xrow + vec_off(k) + 2 * i), xf, unused);
+      unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + vec_off(k) + 2 * i), zf, unused);
+      return silu_gate(xf, zf, exp2_tab);
+    };
+    if constexpr (kWideGated) {
+      static_assert(K == 4 || K == 8, "wide gated rows: four or eight vectors per lane");
+      constexpr bool kHold = K == 4;
+      constexpr int kRunUnroll = kHold ? 4 : 1;  // the run loops: unrolled for one run, kept for two
+      if constexpr (kHold) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) asm volatile("" : "+v"(voff[k]));  // as in the wide row below
+      }
+      const uint8_t* xrow = row_ptr<G>(x, (size_t)row * row_bytes);
+      const uint8_t* grow = p.gamma_period > 1 ? gam + (size_t)gslice * row_bytes : gam;
+      // Four vectors per lane hold u (32 VGPRs) across the reduction. Eight
+      // would not fit beside the gate's arithmetic: they take the row in two
+      // runs of four, in a loop the compiler keeps (unrolled, it overlapped
+      // the runs and spilled), and recompute u after the reduction from x and
+      // z read again (the lane's own lines, from the cache).
+      // vector k's offset and whether it lies in the row: from the unrolled
+      // arrays for one run, computed in the kept loop
+      auto off_of = [&](int k) -> uint32_t {
+        if constexpr (kHold) return voff[k];
+        else return vec_off(k);
+      };
+      auto ok_of = [&](int k) -> bool {
+        if constexpr (kHold) return vok[k];
+        else return lane + k * L < V;
+      };
+      // u of the four vectors k0 .. k0 + 3, from x and z loaded together
+      auto run_u = [&](int k0, float (&ur)[4][8], bool hint) {
+        U4 xw[4], zw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t off = off_of(k0 + j);
+          xw[j] = hint ? ld16s<(NT != 0)>(xrow + off) : ld16(xrow + off);
+          zw[j] = hint ? ld16s<(NT != 0)>(rrow + off) : ld16(rrow + off);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float xf[8], zf[8];
+          unpack8<DT>(xw[j], xf);
+          unpack8<DT>(zw[j], zf);
+          silu_gate8(xf, zf, exp2_tab, ur[j]);  // binary32 u
+        }
+      };
+      float u[4][8];
+      double acc = 0.0;
+#pragma unroll kRunUnroll
+      for (int k0 = 0; k0 < K; k0 += 4) {
+        run_u(k0, u, true);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          double a = 0.0;  // vectors past the row end hold a clamped copy: not counted
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = __builtin_fma((double)u[j][i], (double)u[j][i], a);
+          acc += ok_of(k0 + j) ? a : 0.0;
+        }
+      }
+      U4 gw[4];
+      if constexpr (kHold) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gw[j] = ld16(grow + voff[j]);  // lands during the reduction
+      }
+      const float r = row_r(row_sum_squares<K>(acc, p.hidden, parity, lane, L, V, red, gated_u));
+#pragma unroll kRunUnroll
+      for (int k0 = 0; k0 < K; k0 += 4) {
+        if constexpr (!kHold) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) gw[j] = ld16(grow + off_of(k0 + j));
+          run_u(k0, u, false);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float g[8], n[8];
+          unpack8<DT>(gw[j], g);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) n[i] = (u[j][i] * r) * g[i];
+          emit(row, ok_of(k0 + j), off_of(k0 + j), n);
+        }
+      }
+    } else if constexpr (kWide) {
       // Opaque per row (4 and 8 vectors per lane): otherwise the compiler
       // hoists a 64-bit address per vector and output stream (base + offset)
       // out of the row loop, which at 8 vectors per lane costs more registers
@@ -372,7 +473,7 @@ tail_kernel(TailParams p) {
         unpack8<DT>(gw[k], g);
 #pragma unroll
         for (int i = 0; i < 8; ++i) n[i] = (h[i] * r) * g[i];
-        emit(row, k, n);
+        emit(row, vok[k], voff[k], n);
       }
     } else {
     if constexpr (kGated) {  // each group of a token has its own gamma slice
@@ -419,14 +520,8 @@ tail_kernel(TailParams p) {
     }
 
     float ss;
-    if constexpr (kGated) {  // the fallback recomputes u from x and z
-      const uint8_t* xrow = row_ptr<G>(x, (size_t)row * row_bytes);
-      ss = row_sum_squares<K>(acc, p.hidden, parity, lane, L, V, red, [&](int k, int i) {
-        float xf, zf, unused;
-        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(xrow + vec_off(k) + 2 * i), xf, unused);
-        unpack2<DT>((uint32_t)*reinterpret_cast<const volatile uint16_t*>(rrow + vec_off(k) + 2 * i), zf, unused);
-        return silu_gate(xf, zf, exp2_tab);
-      });
+    if constexpr (kGated) {
+      ss = row_sum_squares<K>(acc, p.hidden, parity, lane, L, V, red, gated_u);
     } else {
       ss = row_sum_squares<K>(acc, p.hidden, parity, lane, L, V, red, stored_h);
     }
@@ -437,7 +532,7 @@ tail_kernel(TailParams p) {
       unpack8<DT>(gv[k], g);
 #pragma unroll
       for (int i = 0; i < 8; ++i) n[i] = (h[k][i] * r) * g[i];
-      emit(row, k, n);
+      emit(row, vok[k], voff[k], n);
     }
     }
   }
@@ -470,8 +565,10 @@ static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
     }
     if (!fn) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 0, NT>;
   }
-  else if (t.group == 0 && t.vec_per_lane == 4) fn = (const void*)&tail_kernel<DT, EPI, NORM, 4, 0, NT>;
-  else if (t.group == 0 && t.vec_per_lane == 8) fn = (const void*)&tail_kernel<DT, EPI, NORM, 8, 0, NT>;
+  else if constexpr (EPI != kEpiGatedNvfp4Lut) {  // the table tiling stops at two
+    if (t.group == 0 && t.vec_per_lane == 4) fn = (const void*)&tail_kernel<DT, EPI, NORM, 4, 0, NT>;
+    else if (t.group == 0 && t.vec_per_lane == 8) fn = (const void*)&tail_kernel<DT, EPI, NORM, 8, 0, NT>;
+  }
   if (!fn) return hipErrorInvalidConfiguration;
   return hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3((unsigned)t.block), args, 0, s);
 }

@@ -73,7 +73,10 @@ def _oracle(inp, G, rows=None):
 
 
 GRID = [(5, 64, 16), (37, 1024, 1024), (37, 1024, 128), (64, 8192, 1024), (16, 8192, 8192),
-        (9, 2048, 64), (3, 16384, 16384), (130, 4096, 512), (1, 16, 16)]
+        (9, 2048, 64), (3, 16384, 16384), (130, 4096, 512), (1, 16, 16),
+        # groups past 16384: four and eight vectors per lane (the computed gate
+        # for both dtypes; 40976: the last vectors of a lane past the group end)
+        (5, 65536, 32768), (3, 32768, 32768), (2, 65536, 65536), (3, 40976, 40976)]
 
 
 @pytest.mark.parametrize("tokens,hidden,group", GRID)
@@ -91,7 +94,7 @@ def test_gated_matches_oracle(tokens, hidden, group, dtype):
 @pytest.mark.parametrize("group,tiling,rows,stream", [
     (128, "16:1", "1", "0"), (256, "32:1", "2", "1"), (256, "64:1", "3", "0"),
     (256, "64:2", "2", "1"), (256, "0:1", "1", "1"), (256, "0:2", "4", "0"),
-    (128, "32:1", "5", "1")])
+    (128, "32:1", "5", "1"), (256, "0:4", "3", "1"), (512, "0:8", "2", "0")])
 @pytest.mark.parametrize("order", ["0", "1"])
 def test_gated_every_tiling(group, tiling, rows, stream, order, monkeypatch):
     """Groups over rows of 1024: the per-group gamma slice (also when a lane
