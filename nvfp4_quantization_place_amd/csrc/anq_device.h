@@ -21,11 +21,17 @@ struct alignas(16) U4 {
   uint32_t w[4];
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ U4 ld16(const void* p) {
   return *reinterpret_cast<const U4*>(p);
 }
+// stored as a vector, not as a struct copy: the copy kept arrays of U4 that
+// only some lanes fill in scratch memory
 __device__ __forceinline__ void st16(void* p, const U4& v) {
-  *reinterpret_cast<U4*>(p) = v;
+  const u32x4 x = {v.w[0], v.w[1], v.w[2], v.w[3]};
+  *reinterpret_cast<u32x4*>(p) = x;
 }
 
 // Row streams are read once and written once: with NT they carry the
@@ -34,8 +40,6 @@ __device__ __forceinline__ void st16(void* p, const U4& v) {
 // hinted together cut the kernel time by ~10% (either alone does little); from
 // 1 to 32 MiB of input, with inputs coming from HBM, the hinted loads alone cut
 // it by 5-15%. The launchers choose NT by call size.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <bool NT>
 __device__ __forceinline__ U4 ld16s(const void* p) {

@@ -161,8 +161,9 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
 
   // one group of heads: the slot's head h = pass * HPP + slot, from its two
   // unpacked vectors, to the lane's 16 codes v and (K heads of the mixed
-  // pool) its rotated values in bf16
-  auto group = [&](int pass, float (&a)[8], float (&b)[8], U4& v, U4& bfa, U4& bfb) {
+  // pool) its rotated values in bf16: b's in bfb, and with R = D a's in v
+  // (such a head stores no codes), so a group holds 8 registers, not 12
+  auto group = [&](int pass, float (&a)[8], float (&b)[8], U4& v, U4& bfb) {
     const int h = pass * HPP + slot;
     const bool qk = h < qk_heads;  // uniform over the head's lanes
     float oa[8], ob[8];
@@ -234,6 +235,7 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
     }
     // the mixed pool keeps a K head's rotated part in bf16, before the division
     const bool k_mixed = STORE == kStoreMixed && h >= p.nq && qk;  // uniform per head
+    U4 bfa;
     if constexpr (STORE == kStoreMixed) {
       if (k_mixed) {
         if (!PART) bfa = pack8<kBF16>(oa);
@@ -256,10 +258,13 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
     v.w[1] = odd ? r1 : a1;
     v.w[2] = odd ? b0 : r0;
     v.w[3] = odd ? b1 : r1;
+    if constexpr (STORE == kStoreMixed && !PART) {
+      if (k_mixed) v = bfa;
+    }
   };
 
   // the stores of one group
-  auto store = [&](int pass, const U4& v, const U4& bfa, const U4& bfb) {
+  auto store = [&](int pass, const U4& v, const U4& bfb) {
     const int h = pass * HPP + slot;
     if (h >= heads) return;
     const bool k_mixed = STORE == kStoreMixed && h >= p.nq && h < qk_heads;
@@ -283,8 +288,8 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
             // boundary, so a pair of lanes is rotated or not together)
             if (rope_b) st16s<NT>(kh + (uint32_t)R + 16u * (uint32_t)j, bfb);
             if (!odd || !rope_b) st16s<NT>(kh + st_off, v);
-          } else {  // R = D: the whole head in bf16
-            st16s<NT>(kh + 16u * (uint32_t)j, bfa);
+          } else {  // R = D: the whole head in bf16 (a's half in v)
+            st16s<NT>(kh + 16u * (uint32_t)j, v);
             st16s<NT>(kh + kHalf * 2 + 16u * (uint32_t)j, bfb);
           }
         } else {  // V heads (and K heads of the uniform pool): codes
@@ -298,21 +303,21 @@ __global__ void __launch_bounds__(1024) qk_kernel(QKParams p) {
   };
 
   const int mine = (passes - w + W - 1) / W;  // groups of this wavefront, <= PF (w < W <= passes)
-  U4 v[PF], bfa[PF], bfb[PF];
+  U4 v[PF], bfb[PF];
 #pragma unroll
   for (int u = 0; u < PF; ++u) {
     if (u < mine) {  // uniform over the wavefront
       float a[8], b[8];
       unpack8<DT>(ra[u], a);
       unpack8<DT>(rb[u], b);
-      group(w + u * W, a, b, v[u], bfa[u], bfb[u]);
+      group(w + u * W, a, b, v[u], bfb[u]);
     }
   }
   // every store after every group: the wait for a group's loads then never
   // also waits for an earlier group's stores (one counter covers both)
 #pragma unroll
   for (int u = 0; u < PF; ++u)
-    if (u < mine) store(w + u * W, v[u], bfa[u], bfb[u]);
+    if (u < mine) store(w + u * W, v[u], bfb[u]);
 }
 
 template <int DT, bool NT, int STORE, int PF, bool PART>

@@ -127,6 +127,33 @@ def test_mixed_pool_waves_and_blocks(waves, block, monkeypatch):
     np.testing.assert_array_equal(_np(pool), ref["kv"])
 
 
+@pytest.mark.parametrize("groups", ["4", "3", "2"])
+@pytest.mark.parametrize("D,R,heads", [(128, 128, (16, 8, 8)), (128, 64, (16, 8, 8)),
+                                       (64, 64, (32, 16, 16)), (256, 256, (7, 5, 4)),
+                                       (256, 64, (8, 4, 4))])
+@pytest.mark.parametrize("stream", ["", "0"])
+def test_mixed_pool_several_groups_per_wavefront(D, R, heads, groups, stream, monkeypatch):
+    """One wavefront per token taking up to four head groups, all computed
+    before any is stored (the layout of large calls): every group's codes and
+    bf16 halves reach their own heads, with the whole head rotated too."""
+    monkeypatch.setenv("ANQ_QK_WAVES", "1")
+    monkeypatch.setenv("ANQ_QK_GROUPS", groups)
+    monkeypatch.setenv("ANQ_STREAM", stream)
+    inp = _inp(D, R, heads, "bf16", tokens=19, seed=4)
+    A = _A()
+    nq, nk, nv = heads
+    num_slots = 32
+    slots = _slots(np.random.default_rng(D + R + 4), inp.tokens, num_slots)
+    width = A.mixed_kv_row_bytes(nk, nv, D, R)
+    pool = torch.full((num_slots, width), SENTINEL, dtype=torch.uint8, device="cuda")
+    q = A.qk_norm_rope_kv_store_mixed(*_dev_args(inp), R, torch.from_numpy(slots).cuda(), pool)
+    torch.cuda.synchronize()
+    ref = O.qk_norm_rope_kv_store_mixed(*_ora_args(inp), R, "bf16", slots,
+                                        np.full((num_slots, width), SENTINEL, np.uint8))
+    np.testing.assert_array_equal(_np(q), ref["q"])
+    np.testing.assert_array_equal(_np(pool), ref["kv"])
+
+
 def test_mixed_pool_writes_nothing_outside_its_outputs():
     """q_out and the pool sit inside larger buffers filled with a canary; every
     byte outside them keeps it."""
