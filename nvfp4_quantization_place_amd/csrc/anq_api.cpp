@@ -192,16 +192,18 @@ extern "C" int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const voi
   p.hidden = (int32_t)group;
   p.vec = (int32_t)(group / 8);
   p.gamma_period = (int32_t)(hidden / group);
-  // bf16 z, groups of at most 16384 and enough work to share a workgroup's
-  // table: the gate from the lookup table (ANQ_GATE_LUT=0/1 overrides, for A/B
+  // bf16 z and enough work to share a workgroup's table: the gate from the
+  // lookup table (ANQ_GATE_LUT=0/1 overrides, for A/B
   // runs). Measured, one GPU: groups of at most 1024 gain 5-14% from 2048 group
   // rows up and lose below 1024 (the 32 KiB copy per workgroup is then not
   // amortised). Wider groups gain from 2^21 elements: bf16 [8192, 8192] in
   // groups of 8192, 4096, 2048 115 / 105 / 107 -> 63 / 63 / 66-68 us, [4096,
   // 5120] in one group 48 -> 24; [256, 8192] one group 6.8 -> 6.2; at 1.5 M
   // elements ([512, 3072], groups of 1536) the table lost, 6.3 -> 7.1. Groups
-  // of 12288 and 16384: [4096, 12288] 93 -> 56 us, [2048, 16384] 58.7 -> 35.8.
-  const bool lut_fits = dtype == ANQ_BF16 && group <= 16384;
+  // of 12288 and 16384: [4096, 12288] 93 -> 56 us, [2048, 16384] 58.7 -> 35.8;
+  // of 32768 and 65536 (four and eight vectors per lane), from [32, 65536]:
+  // 1.3-1.7x faster, e.g. [1024, 32768] 55.8 -> 40.0 us.
+  const bool lut_fits = dtype == ANQ_BF16;
   bool lut = lut_fits && (p.tokens >= 2048 || p.tokens * group >= ((int64_t)1 << 21));
   if (const char* e = getenv("ANQ_GATE_LUT")) {
     if (*e) {

@@ -350,6 +350,12 @@ tail_kernel(TailParams p) {
     };
     if constexpr (kWideGated) {
       static_assert(K == 4 || K == 8, "wide gated rows: four or eight vectors per lane");
+      // Four vectors per lane hold u (32 VGPRs) across the reduction. Eight
+      // would not fit beside the gate's arithmetic (nor, with the table gate,
+      // beside their gamma and the loads in flight): they take the row in two
+      // runs of four, in a loop the compiler keeps (unrolled, it overlapped
+      // the runs and spilled), and recompute u after the reduction from x and
+      // z read again (the lane's own lines, from the cache).
       constexpr bool kHold = K == 4;
       constexpr int kRunUnroll = kHold ? 4 : 1;  // the run loops: unrolled for one run, kept for two
       if constexpr (kHold) {
@@ -358,11 +364,6 @@ tail_kernel(TailParams p) {
       }
       const uint8_t* xrow = row_ptr<G>(x, (size_t)row * row_bytes);
       const uint8_t* grow = p.gamma_period > 1 ? gam + (size_t)gslice * row_bytes : gam;
-      // Four vectors per lane hold u (32 VGPRs) across the reduction. Eight
-      // would not fit beside the gate's arithmetic: they take the row in two
-      // runs of four, in a loop the compiler keeps (unrolled, it overlapped
-      // the runs and spilled), and recompute u after the reduction from x and
-      // z read again (the lane's own lines, from the cache).
       // vector k's offset and whether it lies in the row: from the unrolled
       // arrays for one run, computed in the kept loop
       auto off_of = [&](int k) -> uint32_t {
@@ -384,10 +385,15 @@ tail_kernel(TailParams p) {
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float xf[8], zf[8];
+          float xf[8];
           unpack8<DT>(xw[j], xf);
-          unpack8<DT>(zw[j], zf);
-          silu_gate8(xf, zf, exp2_tab, ur[j]);  // binary32 u
+          if constexpr (kLut) {
+            gate_lut8(xf, zw[j], gate_tab, exp2_tab, ur[j]);  // binary32 u, looked up
+          } else {
+            float zf[8];
+            unpack8<DT>(zw[j], zf);
+            silu_gate8(xf, zf, exp2_tab, ur[j]);  // binary32 u
+          }
         }
       };
       float u[4][8];
@@ -565,10 +571,8 @@ static hipError_t launch4(const TailParams& p, const Tiling& t, hipStream_t s) {
     }
     if (!fn) fn = (const void*)&tail_kernel<DT, EPI, NORM, 2, 0, NT>;
   }
-  else if constexpr (EPI != kEpiGatedNvfp4Lut) {  // the table tiling stops at two
-    if (t.group == 0 && t.vec_per_lane == 4) fn = (const void*)&tail_kernel<DT, EPI, NORM, 4, 0, NT>;
-    else if (t.group == 0 && t.vec_per_lane == 8) fn = (const void*)&tail_kernel<DT, EPI, NORM, 8, 0, NT>;
-  }
+  else if (t.group == 0 && t.vec_per_lane == 4) fn = (const void*)&tail_kernel<DT, EPI, NORM, 4, 0, NT>;
+  else if (t.group == 0 && t.vec_per_lane == 8) fn = (const void*)&tail_kernel<DT, EPI, NORM, 8, 0, NT>;
   if (!fn) return hipErrorInvalidConfiguration;
   return hipLaunchKernel(fn, dim3((unsigned)t.grid), dim3((unsigned)t.block), args, 0, s);
 }

@@ -174,15 +174,18 @@ int pick_tail_tiling(int32_t vec, int64_t tokens, bool swizzled, Tiling* out) {
 // 1024 66.1 -> 63.9, of 512 63.2 -> 59.9, [8192, 4096] groups of 128 34.3 ->
 // 32.3. 256 and 1024 lanes per workgroup measured no better (320, 384, 768:
 // 74-85 us).
-// Wider rows (1040 to 16384 elements) take one workgroup per row, one vector
-// per lane (two past 8192), in about two waves of resident workgroups:
+// Wider rows (1040 to 65536 elements) take one workgroup per row, one vector
+// per lane (two past 8192, four past 16384, eight past 32768), in about two
+// waves of resident workgroups:
 // 512 times the workgroups a CU holds (4 wavefronts per SIMD, four tables of
 // LDS).
 // bf16, one GPU, grid halved / as chosen / doubled: [8192, 8192] in one group
 // 62.8 (as chosen) against 66.9 (doubled); in groups of 4096 63.9 / 62.9 /
 // 63.5 us; [4096, 5120] in one group 24.3 (as chosen) against 31.6 (doubled).
 // Two vectors per lane against the computed gate, one group per row: [2048,
-// 16384] 58.7 -> 35.8 us, [4096, 12288] 93 -> 56.
+// 16384] 58.7 -> 35.8 us, [4096, 12288] 93 -> 56. Four and eight: [256,
+// 32768] 16.1 -> 12.3 us, [1024, 32768] 55.8 -> 40.0, [256, 65536] 43.3 ->
+// 32.5, [1024, 65536] 159 -> 111, [32, 65536] 34.5 -> 19.8.
 // ANQ_GATE_BLOCK (a multiple of 64, 64 to 1024; lane-group tilings only),
 // ANQ_ROWS_PER_GROUP, ANQ_ROW_ORDER and ANQ_STREAM override.
 int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* out) {
@@ -198,16 +201,16 @@ int pick_gate_lut_tiling(int32_t vec, int64_t rows, Tiling* out) {
     groups_per_block = t.block / t.group;
     r = rows / (groups_per_block * 512);
     if (r >= 16) r /= 2;
-  } else if (vec <= 2048) {
+  } else if (vec <= 8192) {
     t.group = 0;
-    t.vec_per_lane = vec <= 1024 ? 1 : 2;
+    t.vec_per_lane = vec <= 1024 ? 1 : (vec <= 2048 ? 2 : (vec <= 4096 ? 4 : 8));
     t.block = ((vec + t.vec_per_lane - 1) / t.vec_per_lane + 63) / 64 * 64;
     groups_per_block = 1;
     const int waves = t.block / 64;
     const int per_cu = 16 / waves < 4 ? 16 / waves : 4;
     r = rows / (512 * (int64_t)per_cu);
   } else {
-    return ANQ_ERR_UNSUPPORTED;  // wider groups stay on the computed gate
+    return ANQ_ERR_UNSUPPORTED;  // past the widest row
   }
   t.rows = (int)(r < 1 ? 1 : (r > 64 ? 64 : r));
   t.interleave = true;

@@ -176,7 +176,8 @@ def test_gated_workload_size():
                                                  (64, 8192, 1024), (9, 2048, 64), (130, 4096, 512),
                                                  (5, 2048, 2048), (7, 8192, 8192), (9, 5120, 5120),
                                                  (4, 3072, 1536), (5, 16384, 16384),
-                                                 (3, 12288, 12288)])
+                                                 (3, 12288, 12288), (5, 65536, 32768),
+                                                 (3, 40976, 40976), (2, 65536, 65536)])
 @pytest.mark.parametrize("rows", ["", "1", "3"])
 @pytest.mark.parametrize("block", ["", "256"])
 @pytest.mark.parametrize("order", ["", "0"])
@@ -184,8 +185,8 @@ def test_gated_table_path_matches_oracle(tokens, hidden, group, rows, block, ord
     """The bf16 gate read from the workgroup's LDS table (forced on small
     calls), with several rows per lane group, interleaved (the default) or
     consecutive, and both workgroup sizes of the lane-group tiling (groups of
-    1040 and more take a workgroup per row whatever the size asked), gives the
-    oracle's codes."""
+    1040 and more take a workgroup per row whatever the size asked; past
+    16384, four or eight vectors per lane), gives the oracle's codes."""
     monkeypatch.setenv("ANQ_GATE_LUT", "1")
     monkeypatch.setenv("ANQ_ROWS_PER_GROUP", rows)
     monkeypatch.setenv("ANQ_ROW_ORDER", order)
@@ -222,7 +223,8 @@ def test_gated_table_path_streaming_hints(tokens, hidden, group, stream, codes, 
                                                  (1500, 3072, 256), (8192, 2048, 64),
                                                  (512, 8192, 8192), (2048, 8192, 4096),
                                                  (4096, 5120, 5120), (1501, 4096, 2048),
-                                                 (2048, 16384, 16384)])
+                                                 (2048, 16384, 16384), (512, 32768, 32768),
+                                                 (130, 65536, 65536)])
 def test_gated_table_interleaved_large(tokens, hidden, group):
     """Calls large enough that the gate-table tiling gives each lane group
     several interleaved rows (2 to 8; at [8192, 2048] in groups of 64 the

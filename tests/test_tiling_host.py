@@ -230,22 +230,27 @@ def test_gated_table_tiling_interleaves(L, tokens, hidden, group, rows, grid, mo
     (300, 8192, 8192, 1024, 1, 300),     # fewer rows than resident workgroups
     (2048, 16384, 16384, 1024, 4, 512),  # two vectors per lane
     (4096, 12288, 12288, 768, 8, 512),
+    (512, 32768, 32768, 1024, 1, 512),   # four vectors per lane
+    (4096, 65536, 65536, 1024, 8, 512),  # eight
+    (300, 40976, 40976, 704, 1, 300),    # eight, the last ones past the group end
 ])
 def test_gated_table_wide_groups(L, tokens, hidden, group, block, rows, grid):
-    """Groups of 1040 to 16384 elements use the gate table with one workgroup
-    per row (one vector per lane, two past 8192 elements), interleaved rows,
-    about two waves of the workgroups the GPU holds at once."""
+    """Groups of 1040 to 65536 elements use the gate table with one workgroup
+    per row (one vector per lane, two past 8192 elements, four past 16384,
+    eight past 32768), interleaved rows, about two waves of the workgroups the
+    GPU holds at once."""
     assert L.gated_rmsnorm_quant_nvfp4(addr(0), addr(1), addr(2), addr(3), 1e-5, tokens, hidden,
                                        group, 1, addr(4), addr(6), None) == OK
     got = last(L)
     assert got["ok"] == "1" and got["epi"] == "5" and got["group"] == "0", got
     assert (got["vec_per_lane"], got["block"], got["rows"], got["grid"], got["interleave"]) == \
-        ("1" if group <= 8192 else "2", str(block), str(rows), str(grid), "1"), got
+        (str(1 if group <= 8192 else 2 if group <= 16384 else 4 if group <= 32768 else 8),
+         str(block), str(rows), str(grid), "1"), got
 
 
 def test_gated_table_choice_by_size(L, monkeypatch):
-    """The table is used for bf16 z in groups of at most 16384 once a call has
-    2048 group rows or 2^21 elements; wider groups always compute the gate."""
+    """The table is used for bf16 z once a call has 2048 group rows or 2^21
+    elements, whatever the group width."""
     g = lambda tokens, hidden, group: L.gated_rmsnorm_quant_nvfp4(  # noqa: E731
         addr(0), addr(1), addr(2), addr(3), 1e-5, tokens, hidden, group, 1, addr(4), addr(6), None)
     assert g(256, 8192, 8192) == OK and last(L)["epi"] == "5"    # 2^21 elements
@@ -253,10 +258,13 @@ def test_gated_table_choice_by_size(L, monkeypatch):
     assert g(1024, 2048, 2048) == OK and last(L)["epi"] == "5"
     assert g(512, 3072, 1536) == OK and last(L)["epi"] == "4"    # 1.5 M elements
     assert g(4096, 16384, 16384) == OK and last(L)["epi"] == "5"
-    assert g(4096, 32768, 32768) == OK and last(L)["epi"] == "4"  # wider than the table tiling
+    assert g(4096, 32768, 32768) == OK and last(L)["epi"] == "5"
+    assert g(64, 32768, 32768) == OK and last(L)["epi"] == "5"    # 2^21 elements
+    assert g(63, 32768, 32768) == OK and last(L)["epi"] == "4"
+    assert g(32, 65536, 65536) == OK and last(L)["epi"] == "5"
     monkeypatch.setenv("ANQ_GATE_LUT", "1")
     assert g(2, 16384, 16384) == OK and last(L)["epi"] == "5"
-    assert g(2, 32768, 32768) == OK and last(L)["epi"] == "4"
+    assert g(2, 65536, 65536) == OK and last(L)["epi"] == "5"
     monkeypatch.setenv("ANQ_GATE_LUT", "0")
     assert g(8192, 8192, 8192) == OK and last(L)["epi"] == "4"
 
