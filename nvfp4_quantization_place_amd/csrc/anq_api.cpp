@@ -202,9 +202,13 @@ extern "C" int gated_rmsnorm_quant_nvfp4(const void* x, const void* z, const voi
   // elements ([512, 3072], groups of 1536) the table lost, 6.3 -> 7.1. Groups
   // of 12288 and 16384: [4096, 12288] 93 -> 56 us, [2048, 16384] 58.7 -> 35.8;
   // of 32768 and 65536 (four and eight vectors per lane), from [32, 65536]:
-  // 1.3-1.7x faster, e.g. [1024, 32768] 55.8 -> 40.0 us.
+  // 1.3-1.7x faster, e.g. [1024, 32768] 55.8 -> 40.0 us. Groups of 8192 and
+  // more gain at any size, their rows being long beside the copy: [1, 65536]
+  // 30.9 -> 15.0 us, [8, 32768] 11.1 -> 7.5, [4, 16384] 6.9 -> 5.5, [16, 8192]
+  // 4.8 -> 4.1, [128, 8192] 6.1 -> 5.4.
   const bool lut_fits = dtype == ANQ_BF16;
-  bool lut = lut_fits && (p.tokens >= 2048 || p.tokens * group >= ((int64_t)1 << 21));
+  bool lut = lut_fits && (group >= 8192 || p.tokens >= 2048 ||
+                          p.tokens * group >= ((int64_t)1 << 21));
   if (const char* e = getenv("ANQ_GATE_LUT")) {
     if (*e) {
       if (strcmp(e, "0") != 0 && strcmp(e, "1") != 0) return ANQ_ERR_CONFIG;

@@ -249,19 +249,19 @@ def test_gated_table_wide_groups(L, tokens, hidden, group, block, rows, grid):
 
 
 def test_gated_table_choice_by_size(L, monkeypatch):
-    """The table is used for bf16 z once a call has 2048 group rows or 2^21
-    elements, whatever the group width."""
+    """The table is used for bf16 z in groups of 8192 or more, and in
+    narrower groups once a call has 2048 group rows or 2^21 elements."""
     g = lambda tokens, hidden, group: L.gated_rmsnorm_quant_nvfp4(  # noqa: E731
         addr(0), addr(1), addr(2), addr(3), 1e-5, tokens, hidden, group, 1, addr(4), addr(6), None)
-    assert g(256, 8192, 8192) == OK and last(L)["epi"] == "5"    # 2^21 elements
-    assert g(255, 8192, 8192) == OK and last(L)["epi"] == "4"
+    assert g(256, 4096, 4096) == OK and last(L)["epi"] == "4"
+    assert g(512, 4096, 4096) == OK and last(L)["epi"] == "5"    # 2^21 elements
+    assert g(1, 8192, 8192) == OK and last(L)["epi"] == "5"      # groups of 8192 and more
+    assert g(1, 16384, 8192) == OK and last(L)["epi"] == "5"
     assert g(1024, 2048, 2048) == OK and last(L)["epi"] == "5"
     assert g(512, 3072, 1536) == OK and last(L)["epi"] == "4"    # 1.5 M elements
     assert g(4096, 16384, 16384) == OK and last(L)["epi"] == "5"
     assert g(4096, 32768, 32768) == OK and last(L)["epi"] == "5"
-    assert g(64, 32768, 32768) == OK and last(L)["epi"] == "5"    # 2^21 elements
-    assert g(63, 32768, 32768) == OK and last(L)["epi"] == "4"
-    assert g(32, 65536, 65536) == OK and last(L)["epi"] == "5"
+    assert g(1, 65536, 65536) == OK and last(L)["epi"] == "5"
     monkeypatch.setenv("ANQ_GATE_LUT", "1")
     assert g(2, 16384, 16384) == OK and last(L)["epi"] == "5"
     assert g(2, 65536, 65536) == OK and last(L)["epi"] == "5"
